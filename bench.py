@@ -1,0 +1,159 @@
+"""Throughput of the small_fc_lopt optimizer step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload vit_b16]
+
+A step is one lopt_step over the whole parameter list (row/column sums,
+moving averages, statistics, finalize, apply).  Inputs (parameters, state,
+gradients) are resident in HBM before the timed region; the same gradients
+are reused for every timed step.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+FLOP_PER_ELEM = 2 * (28 * 32 + 32 * 32 + 32 * 2)   # MLP with step features folded into the bias
+PEAK_FP32_MFMA_TFLOPS = 157.3                      # MI355X dense fp32 matrix
+PEAK_FP32_VALU_TFLOPS = 78.6                       # 256 CU x 4 SIMD x 16 lanes x 2 x 2.4 GHz (no packed fp32)
+PEAK_HBM_GBS = 8000.0
+# ViT-B/16 step of small_fc_lopt with the fused CUDA kernels on the PyLO page
+# ("Benchmark results" > step-time table): 99.59 ms for 86,563,584 parameters.
+PAGE_VIT_GPARAMS_PER_S = 86_563_584 / 99.59e-3 / 1e9
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(seconds_hint: float):
+    """The oracle on one ViT-B/16 block (12 tensors), one step, on host cores."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    import oracle
+    from learned_optimizer_step_amd import workloads as W
+
+    cores = len(os.sched_getaffinity(0))
+    threads = min(cores, 16)
+    w = W.get_workload("vit_b16")
+    idx = [i for i, t in enumerate(w.tensors) if t.name.startswith("blocks.0.")]
+    ps = [W.param_init(w, i) for i in idx]
+    gs = [W.grad_at(w, i, 1) for i in idx]
+    sts = [W.state_init(w, i) for i in idx]
+    n = sum(w.tensors[i].n for i in idx)
+    mlp = W.mlp_weights()
+    with threadpool_limits(limits=threads):
+        t0 = time.perf_counter()
+        oracle.step(ps, gs, sts, 1, mlp, oracle.Hyper())
+        dt = time.perf_counter() - t0
+    return {"value": n / dt / 1e9, "unit": "G params/s", "cores": threads, "kind": "oracle",
+            "sample": f"one ViT-B/16 block (blocks.0.*: {len(idx)} tensors, {n} params), 1 step, "
+                      f"fp64 NumPy, {threads} BLAS threads, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="vit_b16")
+    ap.add_argument("--impl", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
+              f"multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from learned_optimizer_step_amd import lopt as L
+    from learned_optimizer_step_amd import workloads as W
+
+    impl = {"auto": L.LOPT_MLP_AUTO, "valu": L.LOPT_MLP_VALU, "mfma": L.LOPT_MLP_MFMA}[args.impl]
+    w = W.get_workload(args.workload)
+    log(f"[bench] {w.key}: {len(w.tensors)} tensors, {w.n_params} params; generating inputs")
+    dev = torch.device("cuda:0")
+    params, grads = [], []
+    for i, t in enumerate(w.tensors):
+        params.append(torch.from_numpy(W.param_init(w, i).reshape(t.shape)).to(dev))
+        grads.append(torch.from_numpy(W.grad_at(w, i, 1).reshape(t.shape)).to(dev))
+    cfg = L.config_from(mlp_impl=impl)
+    opt = L.LOpt(params, W.mlp_weights(), cfg)
+    if w.prewarm_std is not None:
+        for i in range(len(w.tensors)):
+            st = W.state_init(w, i)
+            v = opt.state_views(i)
+            for k in ("m", "v", "r", "c"):
+                v[k].copy_(torch.from_numpy(st[k]))
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        opt.step(grads)
+    torch.cuda.synchronize()
+
+    nk = L.LOPT_N_KERNELS
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(args.steps)]
+    stream = torch.cuda.current_stream(dev)
+    for evs in events:          # torch creates the HIP event on first record
+        for e in evs:
+            e.record(stream)
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        L.lopt_set_timing_events(opt.handle, [e.cuda_event for e in events[k]])
+        opt.step(grads)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    L.lopt_set_timing_events(opt.handle, [])
+    ms = (t1 - t0) * 1e3 / args.steps
+    kern = np.array([[events[k][j].elapsed_time(events[k][j + 1]) for j in range(nk)]
+                     for k in range(args.steps)])
+    kern_ms = kern.mean(axis=0)
+    opt.close()
+
+    n = w.n_params
+    value = n / (ms * 1e-3) / 1e9
+    apply_ms = float(kern_ms[4])
+    achieved = FLOP_PER_ELEM * n / (apply_ms * 1e-3) / 1e12
+    use_mfma = impl != L.LOPT_MLP_VALU
+    peak = PEAK_FP32_MFMA_TFLOPS if use_mfma else PEAK_FP32_VALU_TFLOPS
+    out = {
+        "metric": "G params updated/sec per optimizer step; % of HBM / FP32 roofline",
+        "value": round(value, 4),
+        "unit": "G params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(value / PAGE_VIT_GPARAMS_PER_S, 3) if w.key == "vit_b16" else None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.key}: {w.description}", "n_params": n, "n_tensors": len(w.tensors),
+                   "mlp_impl": "mfma" if use_mfma else "valu", "state": "zero-init, gradients fixed"},
+        "roofline": {"bound": "mfma" if use_mfma else "alu", "kernel": "k_apply",
+                     "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "flop_per_elem": FLOP_PER_ELEM, "elems_per_launch": n},
+        "step_frac_fp32_peak": round(FLOP_PER_ELEM * n / (ms * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4),
+        "kernels_ms": {name: round(float(t), 4) for name, t in zip(L.KERNEL_NAMES, kern_ms)},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle on host cores)")
+        out["cpu_baseline"] = cpu_baseline(20.0)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,177 @@
+/*
+ * lopt.h - C ABI of the small_fc_lopt learned-optimizer step on MI355X (gfx950).
+ *
+ * The operation (PyLO page, "PyLO: Towards Accessible Learned Optimizers in
+ * PyTorch", sections "Library design" and "CUDA kernel design: two-pass
+ * fusion"): an optimizer keeps per-parameter accumulators, and each step
+ * builds a feature vector for every parameter element, normalises each
+ * feature with a statistic of its squares over the whole tensor (kernel 1),
+ * then rebuilds the features, runs a small MLP per element and applies the
+ * resulting update (kernel 2).
+ *
+ * Per element (i, j) of a tensor viewed as rows x cols (a 1-D tensor of length
+ * n is 1 x n), at step t = 1, 2, ...:
+ *   m_a <- b_a m_a + (1-b_a) g   (a = 1..3),   v <- b_v v + (1-b_v) g^2
+ *   r_k <- f_k r_k + (1-f_k)(mean_j g^2 + eps_f),  c_k likewise over i (k = 1..3)
+ *   28 features: g, p, m_a, v, m_a/sqrt(v+eps_v), 1/sqrt(v+eps_v), g rho_k,
+ *     1/sqrt(r_k[i]), 1/sqrt(c_k[j]), m_a rho_k with
+ *     rho_k = (r_k[i] c_k[j] / mean_i r_k)^(-1/2)
+ *   each feature divided by sqrt(mean over the tensor of its square + eps_norm)
+ *   x = [28 normalised features, tanh(t / tau_q) for q < n_time]
+ *   (dir, mag) = W3 relu(W2 relu(W1 x + b1) + b2) + b3
+ *   u = dir exp(mag exp_mult) step_mult;  p <- p - lr u - lr wd p
+ *
+ * All arithmetic on the device is fp32.  Every call returns an lopt_status;
+ * no C++ exception crosses this boundary.  lopt_last_error() gives a
+ * thread-local message for the last failing call on the calling thread.
+ */
+#ifndef LOPT_H
+#define LOPT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LOPT_N_FEATURES 28 /* per-element features, each normalised per tensor */
+#define LOPT_HIDDEN 32     /* width of both hidden layers */
+#define LOPT_MAX_TIME 11   /* maximum number of step (time) features */
+
+typedef enum lopt_status {
+  LOPT_OK = 0,
+  LOPT_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad shape, aliasing, bad config */
+  LOPT_ERR_UNSUPPORTED = 2,      /* a tensor with 2^31 or more elements, misalignment */
+  LOPT_ERR_WORKSPACE = 3,        /* workspace too small or not 256-byte aligned */
+  LOPT_ERR_HIP = 4,              /* a HIP runtime call or kernel launch failed */
+  LOPT_ERR_STATE = 5             /* tensor list differs from the one given to init_state */
+} lopt_status;
+
+/* Implementation of the per-element MLP in the apply kernel. */
+typedef enum lopt_mlp_impl {
+  LOPT_MLP_AUTO = 0, /* currently the matrix-core path */
+  LOPT_MLP_VALU = 1, /* vector FMA, weights broadcast from scalar registers */
+  LOPT_MLP_MFMA = 2  /* fp32 matrix-core (v_mfma_f32_32x32x2_f32) path */
+} lopt_mlp_impl;
+
+/* Hyperparameters.  lopt_default_config() fills the defaults shown. */
+typedef struct lopt_config {
+  float beta_m[3];    /* momentum decays, default 0.1, 0.5, 0.9 */
+  float beta_v;       /* second-moment decay, default 0.999 */
+  float beta_f[3];    /* row/column second-moment decays, default 0.9, 0.99, 0.999 */
+  float eps_v;        /* inside 1/sqrt(v + eps_v), default 1e-8 */
+  float eps_f;        /* added to the row/column means of g^2, default 1e-20 */
+  float eps_norm;     /* inside the feature normaliser's root, default 1e-30 */
+  float exp_mult;     /* default 1e-3 */
+  float step_mult;    /* default 1e-3 */
+  float lr;           /* multiplies the whole update, default 1 */
+  float weight_decay; /* decoupled: p <- p - lr u - lr wd p, default 0 */
+  int32_t n_time;     /* number of tanh(t/tau) step features, 0..11, default 11 */
+  float timescales[LOPT_MAX_TIME]; /* tau_q, default 1,3,10,30,100,300,1e3,3e3,1e4,3e4,1e5 */
+  int32_t mlp_impl;   /* lopt_mlp_impl */
+} lopt_config;
+
+/* One parameter tensor.  All pointers are device pointers (hipMalloc / torch),
+ * fp32, contiguous, 4-byte aligned.
+ *   param: rows*cols values, row-major; updated in place by lopt_step.
+ *   grad:  rows*cols values; read only.  Its address may change between steps.
+ *          May be NULL in lopt_workspace_bytes and lopt_init_state.
+ *   state: lopt_state_floats(rows, cols) values, owned by the caller and
+ *          updated in place.  Layout (each block contiguous):
+ *            m1 | m2 | m3 | v      (rows*cols each, row-major)
+ *            r1 | r2 | r3          (rows each)
+ *            c1 | c2 | c3          (cols each)
+ *   rows, cols: >= 1 and rows*cols < 2^31.  A 1-D tensor of length n is
+ *          passed as rows = 1, cols = n; then c_k is per element and r_k is a
+ *          single value.
+ * grad must not overlap param or state; no two tensors may overlap. */
+typedef struct lopt_tensor {
+  float* param;
+  const float* grad;
+  float* state;
+  int64_t rows;
+  int64_t cols;
+} lopt_tensor;
+
+typedef struct lopt_handle lopt_handle;
+
+/* Fills *out with the default hyperparameters.  Errors: out == NULL. */
+lopt_status lopt_default_config(lopt_config* out);
+
+/* Number of floats in the packed MLP weights for n_time step features:
+ * W1[32][28+n_time], b1[32], W2[32][32], b2[32], W3[2][32], b3[2]
+ * (row-major, out x in).  2402 for n_time = 11.  Returns 0 if n_time is out
+ * of range. */
+size_t lopt_mlp_floats(int32_t n_time);
+
+/* Creates a handle on the current HIP device.  cfg: hyperparameters (copied);
+ * mlp_host: host pointer to lopt_mlp_floats(cfg->n_time) floats (copied to
+ * device memory that the handle owns).  The call is synchronous.
+ * Errors: null pointers or out-of-range config -> INVALID_ARGUMENT;
+ * allocation/copy failure -> HIP.  *out is set only on success. */
+lopt_status lopt_create(const lopt_config* cfg, const float* mlp_host, lopt_handle** out);
+
+/* Frees the handle and its device memory (not the caller's buffers).  The
+ * caller must make sure no step using the handle is still running. */
+void lopt_destroy(lopt_handle* h);
+
+/* Floats in one tensor's state buffer: 4*rows*cols + 3*(rows + cols);
+ * 0 for an invalid shape. */
+size_t lopt_state_floats(int64_t rows, int64_t cols);
+
+/* Bytes of device workspace that lopt_init_state/lopt_step need for this
+ * tensor list (n tensors).  h may be NULL (the size depends only on the list);
+ * no device call is made.  Errors: as lopt_init_state's validation. */
+lopt_status lopt_workspace_bytes(const lopt_handle* h, const lopt_tensor* ts, int32_t n,
+                                 size_t* bytes);
+
+/* Binds the tensor list to the handle: validates it, lays out the plan (per-
+ * tensor descriptors, work lists and reduction buffers) inside `workspace`,
+ * zero-fills every state buffer and sets the step counter to 0.  workspace:
+ * device pointer, 256-byte aligned, >= lopt_workspace_bytes(); owned by the
+ * caller, which must keep it alive and untouched until the last lopt_step.
+ * stream: a hipStream_t (NULL = default stream); the call returns after the
+ * plan upload and the zero fill have been queued and the upload has finished.
+ * To start from pre-warmed accumulators, write the state buffers after this
+ * call.  Errors: validation -> INVALID_ARGUMENT / UNSUPPORTED / WORKSPACE
+ * (nothing is modified); HIP failure -> HIP. */
+lopt_status lopt_init_state(lopt_handle* h, const lopt_tensor* ts, int32_t n, void* workspace,
+                            size_t ws_bytes, void* stream);
+
+/* One optimizer step over the bound tensor list: t <- t + 1, then queues the
+ * five kernels of the step on `stream` and returns (asynchronous).  ts must
+ * list the same tensors (param, state, rows, cols) in the same order as
+ * lopt_init_state; grad pointers may differ (the plan's copy is refreshed,
+ * which synchronises the stream).  Errors: a different list -> STATE; bad
+ * pointers -> INVALID_ARGUMENT; launch failure -> HIP.  On error nothing is
+ * queued and t is unchanged.  NaN/Inf in the inputs propagate. */
+lopt_status lopt_step(lopt_handle* h, const lopt_tensor* ts, int32_t n, void* stream);
+
+/* Step counter: the number of steps taken (t of the last step). */
+lopt_status lopt_get_step(const lopt_handle* h, int64_t* t);
+
+/* Sets the step counter (to resume from saved state); t >= 0. */
+lopt_status lopt_set_step(lopt_handle* h, int64_t t);
+
+/* Kernels of one step, in launch order. */
+#define LOPT_N_KERNELS 5 /* row/col sums, moving averages, statistics, finalize, apply */
+
+/* Measurement hook (the PyLO page reports step times, "Benchmark results" >
+ * "Step-time reduction"; this lets a caller time each kernel of the step on
+ * the step's own stream).  events: n caller-owned hipEvent_t handles; with
+ * n == LOPT_N_KERNELS + 1 every following lopt_step records events[k] on its
+ * stream just before kernel k and events[LOPT_N_KERNELS] after the last one;
+ * n == 0 switches recording off.  The array is copied; the events must stay
+ * valid while steps that record them are queued.  Errors: NULL handle, NULL
+ * events with n > 0, other n -> INVALID_ARGUMENT. */
+lopt_status lopt_set_timing_events(lopt_handle* h, void* const* events, int32_t n);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* lopt_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOPT_H */

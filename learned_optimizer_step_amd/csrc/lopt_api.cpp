@@ -1,0 +1,521 @@
+// C ABI of the small_fc_lopt optimizer step: validation, planning of the
+// per-step work lists inside the caller's workspace, and the launch sequence.
+//
+// The interface follows the PyLO page's "Library design" section: an
+// optimizer object holds the learned-optimizer weights and the per-parameter
+// accumulators and exposes a step over the parameter list.  Here the caller
+// owns all tensors (allocated by PyTorch); the library owns a device copy of
+// the MLP weights and nothing else.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <stdexcept>
+#include <string>
+#include <vector>
+
+#include "../../include/lopt.h"
+#include "lopt_internal.h"
+
+using namespace lopt;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+struct ApiError {
+  lopt_status code;
+  std::string msg;
+};
+
+[[noreturn]] void fail(lopt_status code, const std::string& msg) { throw ApiError{code, msg}; }
+
+void hip_check(hipError_t e, const char* what) {
+  if (e != hipSuccess) fail(LOPT_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+template <class F>
+lopt_status guarded(F&& f) {
+  try {
+    f();
+    g_last_error.clear();
+    return LOPT_OK;
+  } catch (const ApiError& e) {
+    g_last_error = e.msg;
+    return e.code;
+  } catch (const std::bad_alloc&) {
+    g_last_error = "host allocation failed";
+    return LOPT_ERR_HIP;
+  } catch (const std::exception& e) {
+    g_last_error = e.what();
+    return LOPT_ERR_HIP;
+  } catch (...) {
+    g_last_error = "unknown error";
+    return LOPT_ERR_HIP;
+  }
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int pow2_log2_ceil(int x) {
+  int l = 0;
+  while ((1 << l) < x) ++l;
+  return l;
+}
+
+// Work lists and workspace layout for one tensor list.
+struct Plan {
+  std::vector<TensorDesc> desc;
+  std::vector<const float*> grads;
+  std::vector<Tile0> tiles0;
+  std::vector<Seg1> segs1;
+  std::vector<Chunk> chunks;
+  int32_t n_rseg = 0;
+  // byte offsets inside the workspace
+  size_t off_desc = 0, off_grads = 0, off_tiles0 = 0, off_segs1 = 0, off_chunks = 0;
+  size_t off_rbar = 0, off_stats = 0, off_scales = 0, off_packed = 0, off_floats = 0;
+  size_t floats = 0;  // per-tensor float arrays (row/col partials, rq, cq)
+  size_t total = 0;
+  std::vector<lopt_tensor> bound;
+};
+
+void validate_config(const lopt_config* c) {
+  if (!c) fail(LOPT_ERR_INVALID_ARGUMENT, "config is NULL");
+  auto finite = [](float x) { return std::isfinite(x); };
+  for (int a = 0; a < 3; ++a)
+    if (!(c->beta_m[a] >= 0.f && c->beta_m[a] <= 1.f) || !(c->beta_f[a] >= 0.f && c->beta_f[a] <= 1.f))
+      fail(LOPT_ERR_INVALID_ARGUMENT, "decays must lie in [0, 1]");
+  if (!(c->beta_v >= 0.f && c->beta_v <= 1.f)) fail(LOPT_ERR_INVALID_ARGUMENT, "beta_v must lie in [0, 1]");
+  if (!(c->eps_v >= 0.f) || !(c->eps_f >= 0.f) || !(c->eps_norm >= 0.f) || !finite(c->eps_v) ||
+      !finite(c->eps_f) || !finite(c->eps_norm))
+    fail(LOPT_ERR_INVALID_ARGUMENT, "epsilons must be finite and >= 0");
+  if (!finite(c->exp_mult) || !finite(c->step_mult) || !finite(c->lr) || !finite(c->weight_decay))
+    fail(LOPT_ERR_INVALID_ARGUMENT, "exp_mult, step_mult, lr and weight_decay must be finite");
+  if (c->n_time < 0 || c->n_time > LOPT_MAX_TIME) fail(LOPT_ERR_INVALID_ARGUMENT, "n_time must be in 0..11");
+  for (int q = 0; q < c->n_time; ++q)
+    if (!(c->timescales[q] > 0.f) || !finite(c->timescales[q]))
+      fail(LOPT_ERR_INVALID_ARGUMENT, "timescales must be finite and > 0");
+  if (c->mlp_impl < LOPT_MLP_AUTO || c->mlp_impl > LOPT_MLP_MFMA)
+    fail(LOPT_ERR_INVALID_ARGUMENT, "unknown mlp_impl");
+}
+
+struct Range {
+  uintptr_t a, b;  // [a, b)
+  int tensor;
+};
+
+// require_grads: gradients are first needed by lopt_step; lopt_init_state and
+// lopt_workspace_bytes accept NULL gradient pointers.
+void validate_tensors(const lopt_tensor* ts, int32_t n, bool require_grads) {
+  if (n < 0) fail(LOPT_ERR_INVALID_ARGUMENT, "negative tensor count");
+  if (n > 0 && !ts) fail(LOPT_ERR_INVALID_ARGUMENT, "tensor list is NULL");
+  std::vector<Range> written;
+  written.reserve(2 * size_t(n));
+  for (int32_t i = 0; i < n; ++i) {
+    const lopt_tensor& t = ts[i];
+    const std::string at = "tensor " + std::to_string(i) + ": ";
+    if (!t.param || !t.state) fail(LOPT_ERR_INVALID_ARGUMENT, at + "NULL param or state");
+    if (require_grads && !t.grad) fail(LOPT_ERR_INVALID_ARGUMENT, at + "NULL grad");
+    if (t.rows < 1 || t.cols < 1) fail(LOPT_ERR_INVALID_ARGUMENT, at + "rows and cols must be >= 1");
+    if (t.rows > INT32_MAX || t.cols > INT32_MAX || t.rows * t.cols >= (int64_t(1) << 31))
+      fail(LOPT_ERR_UNSUPPORTED, at + "tensors must have fewer than 2^31 elements");
+    if ((reinterpret_cast<uintptr_t>(t.param) | reinterpret_cast<uintptr_t>(t.grad) |
+         reinterpret_cast<uintptr_t>(t.state)) & 3u)
+      fail(LOPT_ERR_UNSUPPORTED, at + "pointers must be 4-byte aligned");
+    const size_t ne = size_t(t.rows * t.cols);
+    const size_t ns = lopt_state_floats(t.rows, t.cols);
+    const uintptr_t p = reinterpret_cast<uintptr_t>(t.param);
+    const uintptr_t s = reinterpret_cast<uintptr_t>(t.state);
+    written.push_back({p, p + 4 * ne, i});
+    written.push_back({s, s + 4 * ns, i});
+  }
+  std::sort(written.begin(), written.end(), [](const Range& x, const Range& y) { return x.a < y.a; });
+  for (size_t k = 1; k < written.size(); ++k)
+    if (written[k].a < written[k - 1].b)
+      fail(LOPT_ERR_INVALID_ARGUMENT, "param/state buffers of tensors " + std::to_string(written[k - 1].tensor) +
+                                          " and " + std::to_string(written[k].tensor) + " overlap");
+  for (int32_t i = 0; i < n; ++i) {
+    if (!ts[i].grad) continue;
+    const uintptr_t g = reinterpret_cast<uintptr_t>(ts[i].grad);
+    const uintptr_t ge = g + 4 * size_t(ts[i].rows * ts[i].cols);
+    // first written range that ends after g
+    auto it = std::upper_bound(written.begin(), written.end(), g,
+                               [](uintptr_t v, const Range& r) { return v < r.a; });
+    if (it != written.begin()) {
+      auto prev = std::prev(it);
+      if (prev->b > g) fail(LOPT_ERR_INVALID_ARGUMENT, "grad of tensor " + std::to_string(i) + " overlaps a written buffer");
+    }
+    if (it != written.end() && it->a < ge)
+      fail(LOPT_ERR_INVALID_ARGUMENT, "grad of tensor " + std::to_string(i) + " overlaps a written buffer");
+  }
+}
+
+Plan build_plan(const lopt_tensor* ts, int32_t n) {
+  validate_tensors(ts, n, false);
+  Plan pl;
+  pl.bound.assign(ts, ts + n);
+  pl.desc.resize(n);
+  pl.grads.resize(n);
+  size_t fl = 0;  // floats of per-tensor arrays
+  int32_t rseg = 0;
+  for (int32_t ti = 0; ti < n; ++ti) {
+    const lopt_tensor& t = ts[ti];
+    TensorDesc& d = pl.desc[ti];
+    std::memset(&d, 0, sizeof(d));
+    d.p = t.param;
+    d.st = t.state;
+    d.R = int32_t(t.rows);
+    d.C = int32_t(t.cols);
+    d.n = uint32_t(t.rows * t.cols);
+    d.vec = t.rows == 1;
+    fastdiv_magic(uint32_t(d.C), &d.cmagic, &d.cshift);
+    // host check of the divisor constants at the edges of the index range
+    for (uint64_t e : {uint64_t(0), uint64_t(d.C) - 1, uint64_t(d.C), uint64_t(d.n) - 1,
+                       uint64_t(d.n) - uint64_t(d.C), uint64_t(d.n) / 2}) {
+      if (e >= d.n) continue;
+      const uint32_t q = uint32_t(((uint64_t(e) * d.cmagic >> 32) + e) >> d.cshift);
+      if (q != e / uint64_t(d.C)) fail(LOPT_ERR_UNSUPPORTED, "internal: division constants failed check");
+    }
+    pl.grads[ti] = t.grad;
+
+    // row/column sum tiles
+    if (d.vec) {
+      const int32_t nt = int32_t((int64_t(d.n) + kTile0Elems - 1) / kTile0Elems);
+      d.ncw = nt;
+      d.nrb = 0;
+      for (int32_t q = 0; q < nt; ++q) {
+        Tile0 tl{};
+        tl.tensor = ti;
+        tl.flat = 1;
+        tl.c0 = q * kTile0Elems;
+        tl.c1 = int32_t(std::min<int64_t>(int64_t(q + 1) * kTile0Elems, d.n));
+        tl.win = q;
+        pl.tiles0.push_back(tl);
+      }
+    } else {
+      const int cwl = std::min(8, pow2_log2_ceil(d.C));
+      const int CW = 1 << cwl;
+      const int RS = kBlock / CW;
+      const int ncw = (d.C + CW - 1) / CW;
+      int TR = RS * kTile0Iters;  // rows per tile
+      while (TR > RS && int64_t(TR / 2) * CW >= kTile0Elems) TR /= 2;
+      const int nrb = (d.R + TR - 1) / TR;
+      d.ncw = ncw;
+      d.nrb = nrb;
+      for (int b = 0; b < nrb; ++b)
+        for (int w = 0; w < ncw; ++w) {
+          Tile0 tl{};
+          tl.tensor = ti;
+          tl.flat = 0;
+          tl.r0 = b * TR;
+          tl.r1 = std::min(d.R, (b + 1) * TR);
+          tl.c0 = w * CW;
+          tl.c1 = std::min(d.C, (w + 1) * CW);
+          tl.cw_log2 = cwl;
+          tl.rb = b;
+          tl.win = w;
+          pl.tiles0.push_back(tl);
+        }
+    }
+    // per-tensor float arrays
+    d.off_rowpart = int64_t(fl);
+    fl += size_t(d.ncw) * d.R;
+    d.off_colpart = int64_t(fl);
+    fl += size_t(d.nrb) * d.C;
+    fl = align_up(fl, 4);
+    d.off_rq = int64_t(fl);
+    fl += align_up(3 * size_t(d.R), 4);
+    d.off_cq = int64_t(fl);
+    fl += d.vec ? 0 : align_up(3 * size_t(d.C), 4);
+
+    // moving-average segments
+    d.rseg0 = rseg;
+    if (d.vec) {
+      pl.segs1.push_back(Seg1{ti, kSegVec, 0, 1, rseg, {0, 0, 0}});
+      d.nrseg = 1;
+      ++rseg;
+    } else {
+      d.nrseg = (d.R + kSeg1 - 1) / kSeg1;
+      for (int a = 0; a < d.R; a += kSeg1)
+        pl.segs1.push_back(Seg1{ti, kSegRows, a, std::min(d.R, a + kSeg1), rseg++, {0, 0, 0}});
+      for (int a = 0; a < d.C; a += kSeg1)
+        pl.segs1.push_back(Seg1{ti, kSegCols, a, std::min(d.C, a + kSeg1), -1, {0, 0, 0}});
+    }
+
+    // statistics / apply chunks
+    d.chunk0 = int32_t(pl.chunks.size());
+    for (uint64_t e = 0; e < d.n; e += kChunkElems)
+      pl.chunks.push_back(Chunk{ti, uint32_t(e), uint32_t(std::min<uint64_t>(e + kChunkElems, d.n)), 0});
+    d.nchunk = int32_t(pl.chunks.size()) - d.chunk0;
+  }
+  pl.n_rseg = rseg;
+  pl.floats = fl;
+
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  pl.off_desc = take(sizeof(TensorDesc) * pl.desc.size());
+  pl.off_grads = take(sizeof(const float*) * pl.grads.size());
+  pl.off_tiles0 = take(sizeof(Tile0) * pl.tiles0.size());
+  pl.off_segs1 = take(sizeof(Seg1) * pl.segs1.size());
+  pl.off_chunks = take(sizeof(Chunk) * pl.chunks.size());
+  pl.off_rbar = take(sizeof(float) * 4 * size_t(pl.n_rseg));
+  pl.off_stats = take(sizeof(float) * kStatStride * pl.chunks.size());
+  pl.off_scales = take(sizeof(float) * kStatStride * pl.desc.size());
+  pl.off_packed = take(sizeof(float) * kPkFloats);
+  pl.off_floats = take(sizeof(float) * pl.floats);
+  pl.total = off;
+  // per-tensor float offsets are relative to the workspace base
+  const int64_t base = int64_t(pl.off_floats / sizeof(float));
+  for (auto& d : pl.desc) {
+    d.off_rowpart += base;
+    d.off_colpart += base;
+    d.off_rq += base;
+    d.off_cq += base;
+  }
+  return pl;
+}
+
+}  // namespace
+
+struct lopt_handle {
+  lopt_config cfg{};
+  int device = 0;
+  float* d_mlp = nullptr;
+  bool bound = false;
+  Plan plan;
+  char* ws = nullptr;
+  size_t ws_bytes = 0;
+  int64_t t = 0;
+  std::vector<hipEvent_t> events;  // optional timing events (kNumKernels + 1)
+};
+
+namespace {
+
+StepCtx make_ctx(const lopt_handle* h) {
+  const Plan& pl = h->plan;
+  StepCtx c{};
+  c.ws = reinterpret_cast<float*>(h->ws);
+  c.desc = reinterpret_cast<const TensorDesc*>(h->ws + pl.off_desc);
+  c.grads = reinterpret_cast<const float* const*>(h->ws + pl.off_grads);
+  c.tiles0 = reinterpret_cast<const Tile0*>(h->ws + pl.off_tiles0);
+  c.segs1 = reinterpret_cast<const Seg1*>(h->ws + pl.off_segs1);
+  c.chunks = reinterpret_cast<const Chunk*>(h->ws + pl.off_chunks);
+  c.rbar_part = reinterpret_cast<float*>(h->ws + pl.off_rbar);
+  c.stats_part = reinterpret_cast<float*>(h->ws + pl.off_stats);
+  c.scales = reinterpret_cast<float*>(h->ws + pl.off_scales);
+  c.packed = reinterpret_cast<float*>(h->ws + pl.off_packed);
+  c.mlp = h->d_mlp;
+  c.n_tensors = int32_t(pl.desc.size());
+  c.n_tiles0 = int32_t(pl.tiles0.size());
+  c.n_segs1 = int32_t(pl.segs1.size());
+  c.n_chunks = int32_t(pl.chunks.size());
+  c.mlp_impl = h->cfg.mlp_impl == LOPT_MLP_VALU ? LOPT_MLP_VALU : LOPT_MLP_MFMA;
+  return c;
+}
+
+StepParams make_params(const lopt_handle* h, int64_t t) {
+  const lopt_config& c = h->cfg;
+  StepParams p{};
+  for (int a = 0; a < 3; ++a) {
+    p.beta_m[a] = c.beta_m[a];
+    p.beta_f[a] = c.beta_f[a];
+  }
+  p.beta_v = c.beta_v;
+  p.eps_v = c.eps_v;
+  p.eps_f = c.eps_f;
+  p.eps_norm = c.eps_norm;
+  p.exp_mult = c.exp_mult;
+  p.step_mult = c.step_mult;
+  p.lr = c.lr;
+  p.weight_decay = c.weight_decay;
+  p.t = float(t);
+  p.n_time = c.n_time;
+  for (int q = 0; q < kMaxTime; ++q) p.timescales[q] = q < c.n_time ? c.timescales[q] : 1.f;
+  return p;
+}
+
+template <class T>
+void upload(char* ws, size_t off, const std::vector<T>& v, hipStream_t s) {
+  if (v.empty()) return;
+  hip_check(hipMemcpyAsync(ws + off, v.data(), sizeof(T) * v.size(), hipMemcpyHostToDevice, s),
+            "hipMemcpyAsync(plan)");
+}
+
+void check_same_list(const lopt_handle* h, const lopt_tensor* ts, int32_t n, bool* grads_changed) {
+  if (!h->bound) fail(LOPT_ERR_STATE, "lopt_init_state has not been called");
+  const auto& b = h->plan.bound;
+  if (n != int32_t(b.size())) fail(LOPT_ERR_STATE, "tensor count differs from lopt_init_state");
+  if (n > 0 && !ts) fail(LOPT_ERR_INVALID_ARGUMENT, "tensor list is NULL");
+  *grads_changed = false;
+  for (int32_t i = 0; i < n; ++i) {
+    if (ts[i].param != b[i].param || ts[i].state != b[i].state || ts[i].rows != b[i].rows ||
+        ts[i].cols != b[i].cols)
+      fail(LOPT_ERR_STATE, "tensor " + std::to_string(i) + " differs from lopt_init_state");
+    if (ts[i].grad != b[i].grad) *grads_changed = true;
+  }
+  if (*grads_changed) validate_tensors(ts, n, true);
+}
+
+}  // namespace
+
+extern "C" {
+
+lopt_status lopt_default_config(lopt_config* out) {
+  return guarded([&] {
+    if (!out) fail(LOPT_ERR_INVALID_ARGUMENT, "out is NULL");
+    lopt_config c{};
+    c.beta_m[0] = 0.1f; c.beta_m[1] = 0.5f; c.beta_m[2] = 0.9f;
+    c.beta_v = 0.999f;
+    c.beta_f[0] = 0.9f; c.beta_f[1] = 0.99f; c.beta_f[2] = 0.999f;
+    c.eps_v = 1e-8f;
+    c.eps_f = 1e-20f;
+    c.eps_norm = 1e-30f;
+    c.exp_mult = 1e-3f;
+    c.step_mult = 1e-3f;
+    c.lr = 1.f;
+    c.weight_decay = 0.f;
+    c.n_time = 11;
+    const float ts[LOPT_MAX_TIME] = {1.f, 3.f, 10.f, 30.f, 100.f, 300.f, 1e3f, 3e3f, 1e4f, 3e4f, 1e5f};
+    std::memcpy(c.timescales, ts, sizeof(ts));
+    c.mlp_impl = LOPT_MLP_AUTO;
+    *out = c;
+  });
+}
+
+size_t lopt_mlp_floats(int32_t n_time) {
+  if (n_time < 0 || n_time > LOPT_MAX_TIME) return 0;
+  const size_t din = size_t(kNF + n_time);
+  return size_t(kH) * din + kH + size_t(kH) * kH + kH + 2 * kH + 2;
+}
+
+size_t lopt_state_floats(int64_t rows, int64_t cols) {
+  if (rows < 1 || cols < 1 || rows > INT32_MAX || cols > INT32_MAX) return 0;
+  return size_t(4 * rows * cols + 3 * (rows + cols));
+}
+
+lopt_status lopt_create(const lopt_config* cfg, const float* mlp_host, lopt_handle** out) {
+  return guarded([&] {
+    if (!out) fail(LOPT_ERR_INVALID_ARGUMENT, "out is NULL");
+    if (!mlp_host) fail(LOPT_ERR_INVALID_ARGUMENT, "mlp_host is NULL");
+    validate_config(cfg);
+    const size_t nw = lopt_mlp_floats(cfg->n_time);
+    for (size_t i = 0; i < nw; ++i)
+      if (!std::isfinite(mlp_host[i])) fail(LOPT_ERR_INVALID_ARGUMENT, "MLP weights must be finite");
+    auto* h = new lopt_handle();
+    h->cfg = *cfg;
+    try {
+      hip_check(hipGetDevice(&h->device), "hipGetDevice");
+      hip_check(hipMalloc(reinterpret_cast<void**>(&h->d_mlp), nw * sizeof(float)), "hipMalloc(weights)");
+      hip_check(hipMemcpy(h->d_mlp, mlp_host, nw * sizeof(float), hipMemcpyHostToDevice), "hipMemcpy(weights)");
+    } catch (...) {
+      if (h->d_mlp) (void)hipFree(h->d_mlp);
+      delete h;
+      throw;
+    }
+    *out = h;
+  });
+}
+
+void lopt_destroy(lopt_handle* h) {
+  if (!h) return;
+  if (h->d_mlp) (void)hipFree(h->d_mlp);
+  delete h;
+}
+
+lopt_status lopt_workspace_bytes(const lopt_handle* h, const lopt_tensor* ts, int32_t n, size_t* bytes) {
+  return guarded([&] {
+    (void)h;  // the plan depends only on the tensor list
+    if (!bytes) fail(LOPT_ERR_INVALID_ARGUMENT, "NULL output");
+    Plan pl = build_plan(ts, n);
+    *bytes = pl.total;
+  });
+}
+
+lopt_status lopt_init_state(lopt_handle* h, const lopt_tensor* ts, int32_t n, void* workspace, size_t ws_bytes,
+                            void* stream) {
+  return guarded([&] {
+    if (!h) fail(LOPT_ERR_INVALID_ARGUMENT, "handle is NULL");
+    Plan pl = build_plan(ts, n);
+    if (pl.total > 0 && !workspace) fail(LOPT_ERR_WORKSPACE, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) fail(LOPT_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (ws_bytes < pl.total)
+      fail(LOPT_ERR_WORKSPACE, "workspace too small: need " + std::to_string(pl.total) + " bytes");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    upload(ws, pl.off_desc, pl.desc, s);
+    upload(ws, pl.off_grads, pl.grads, s);
+    upload(ws, pl.off_tiles0, pl.tiles0, s);
+    upload(ws, pl.off_segs1, pl.segs1, s);
+    upload(ws, pl.off_chunks, pl.chunks, s);
+    hip_check(hipStreamSynchronize(s), "hipStreamSynchronize(plan upload)");
+    h->plan = std::move(pl);
+    h->ws = ws;
+    h->ws_bytes = ws_bytes;
+    h->bound = true;
+    h->t = 0;
+    hip_check(launch_zero_state(make_ctx(h), s), "launch(zero state)");
+  });
+}
+
+lopt_status lopt_step(lopt_handle* h, const lopt_tensor* ts, int32_t n, void* stream) {
+  return guarded([&] {
+    if (!h) fail(LOPT_ERR_INVALID_ARGUMENT, "handle is NULL");
+    bool grads_changed = false;
+    check_same_list(h, ts, n, &grads_changed);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (grads_changed) {
+      for (int32_t i = 0; i < n; ++i) {
+        h->plan.grads[i] = ts[i].grad;
+        h->plan.bound[i].grad = ts[i].grad;
+      }
+      upload(h->ws, h->plan.off_grads, h->plan.grads, s);
+      hip_check(hipStreamSynchronize(s), "hipStreamSynchronize(grad pointer upload)");
+    }
+    const StepParams p = make_params(h, h->t + 1);
+    hip_check(launch_step(make_ctx(h), p, s, h->events.empty() ? nullptr : h->events.data()), "launch(step)");
+    h->t += 1;
+  });
+}
+
+lopt_status lopt_get_step(const lopt_handle* h, int64_t* t) {
+  return guarded([&] {
+    if (!h || !t) fail(LOPT_ERR_INVALID_ARGUMENT, "NULL handle or output");
+    *t = h->t;
+  });
+}
+
+lopt_status lopt_set_step(lopt_handle* h, int64_t t) {
+  return guarded([&] {
+    if (!h) fail(LOPT_ERR_INVALID_ARGUMENT, "handle is NULL");
+    if (t < 0) fail(LOPT_ERR_INVALID_ARGUMENT, "step must be >= 0");
+    h->t = t;
+  });
+}
+
+lopt_status lopt_set_timing_events(lopt_handle* h, void* const* events, int32_t n) {
+  return guarded([&] {
+    if (!h) fail(LOPT_ERR_INVALID_ARGUMENT, "handle is NULL");
+    if (n == 0) {
+      h->events.clear();
+      return;
+    }
+    if (n != kNumKernels + 1 || !events) fail(LOPT_ERR_INVALID_ARGUMENT, "expected LOPT_N_KERNELS + 1 events");
+    std::vector<hipEvent_t> ev(n);
+    for (int32_t k = 0; k < n; ++k) {
+      if (!events[k]) fail(LOPT_ERR_INVALID_ARGUMENT, "NULL event");
+      ev[k] = static_cast<hipEvent_t>(events[k]);
+    }
+    h->events = std::move(ev);
+  });
+}
+
+const char* lopt_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

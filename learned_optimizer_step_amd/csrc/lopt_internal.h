@@ -1,0 +1,127 @@
+// Internal definitions shared by the host planner (lopt_api.cpp) and the
+// gfx950 kernels (lopt_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace lopt {
+
+constexpr int kBlock = 256;        // threads per workgroup in every kernel (4 wave64s)
+constexpr int kNF = 28;            // per-element features
+constexpr int kH = 32;             // hidden width
+constexpr int kMaxTime = 11;
+constexpr int kStatStride = 32;    // floats per stats partial / per-tensor scale record
+
+// Work sizes.
+constexpr int kTile0Elems = 16384;   // elements per row/column-sum tile
+constexpr int kTile0Iters = 64;      // row iterations per 2-D tile (bounds the LDS buffer)
+constexpr int kSeg1 = 256;           // rows or columns per moving-average segment
+constexpr int kChunkElems = 16384;   // elements per statistics / apply chunk
+
+// Packed MLP in the workspace, written once per step by the finalize kernel:
+// W1 feature columns [32][28], b1 with the step features folded in [32],
+// W2 [32][32], b2 [32], W3 [2][32], b3 [2].
+constexpr int kPkW1 = 0;
+constexpr int kPkB1 = kPkW1 + kH * kNF;
+constexpr int kPkW2 = kPkB1 + kH;
+constexpr int kPkB2 = kPkW2 + kH * kH;
+constexpr int kPkW3 = kPkB2 + kH;
+constexpr int kPkB3 = kPkW3 + 2 * kH;
+constexpr int kPkFloats = kPkB3 + 2;
+
+// Per-tensor descriptor (device resident, in the workspace).
+struct TensorDesc {
+  float* p;
+  float* st;                 // state: m1 m2 m3 v (n each) | r1 r2 r3 (R) | c1 c2 c3 (C)
+  int32_t R, C;
+  uint32_t n;
+  uint32_t cmagic;           // e / C == (umulhi(e, cmagic) + e) >> cshift for e < 2^31
+  uint32_t cshift;
+  int32_t vec;               // R == 1: c_k per element, r_k a single value
+  int32_t ncw;               // row partials per row (column windows; flat tiles for vec)
+  int32_t nrb;               // column partials per column (row blocks)
+  int32_t rseg0, nrseg;      // moving-average row segments (sum of r_k partials)
+  int32_t chunk0, nchunk;    // statistics / apply chunks
+  int64_t off_rowpart;       // floats: [ncw][R]
+  int64_t off_colpart;       // floats: [nrb][C]       (2-D only)
+  int64_t off_rq;            // floats: [3][R]  r_k^(-1/2)
+  int64_t off_cq;            // floats: [3][C]  c_k^(-1/2) (2-D only)
+};
+
+// Row/column sum-of-squares tile.
+struct Tile0 {
+  int32_t tensor;
+  int32_t flat;              // 1: flat element range of a 1-D tensor
+  int32_t r0, r1;            // 2-D rows [r0, r1)
+  int32_t c0, c1;            // 2-D columns [c0, c1); flat: elements [c0, c1)
+  int32_t cw_log2;           // 2-D: log2(threads per row slot)
+  int32_t rb;                // 2-D: row-block index (column partial slot)
+  int32_t win;               // row partial slot (column window, or flat tile index)
+  int32_t pad[3];
+};
+
+// Moving-average segment.
+enum : int32_t { kSegRows = 0, kSegCols = 1, kSegVec = 2 };
+struct Seg1 {
+  int32_t tensor;
+  int32_t kind;
+  int32_t a, b;              // rows or columns [a, b)
+  int32_t slot;              // rows / vec: index of the r_k partial-sum record
+  int32_t pad[3];
+};
+
+// Statistics / apply chunk: elements [e0, e1) of one tensor.
+struct Chunk {
+  int32_t tensor;
+  uint32_t e0, e1;
+  int32_t pad;
+};
+
+// Hyperparameters as the kernels see them.
+struct StepParams {
+  float beta_m[3];
+  float beta_v;
+  float beta_f[3];
+  float eps_v, eps_f, eps_norm;
+  float exp_mult, step_mult, lr, weight_decay;
+  float t;                   // 1-based step index of this step
+  int32_t n_time;
+  float timescales[kMaxTime];
+};
+
+// Where everything lives: the workspace base and the per-step buffers.
+struct StepCtx {
+  float* ws;                         // workspace base (floats)
+  const TensorDesc* desc;
+  const float* const* grads;         // per-tensor gradient pointers
+  const Tile0* tiles0;
+  const Seg1* segs1;
+  const Chunk* chunks;
+  float* rbar_part;                  // [n_rows_segs][4]
+  float* stats_part;                 // [n_chunks][32]
+  float* scales;                     // [n_tensors][32]: s_0..s_27, sqrt(rbar_k) at 28..30
+  float* packed;                     // kPkFloats
+  const float* mlp;                  // raw weights (handle-owned)
+  int32_t n_tensors, n_tiles0, n_segs1, n_chunks;
+  int32_t mlp_impl;                  // 1 = VALU, 2 = MFMA
+};
+
+hipError_t launch_zero_state(const StepCtx& c, hipStream_t s);
+constexpr int kNumKernels = 5;
+// events: nullptr, or kNumKernels + 1 events recorded around the launches.
+hipError_t launch_step(const StepCtx& c, const StepParams& p, hipStream_t s, const hipEvent_t* events);
+
+// Fast division by a 32-bit divisor for numerators below 2^31
+// (round-up multiplier method, Granlund & Montgomery 1994).
+inline void fastdiv_magic(uint32_t d, uint32_t* magic, uint32_t* shift) {
+  uint32_t l = 0;
+  while ((uint64_t(1) << l) < d) ++l;
+  uint64_t m = ((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1;
+  *magic = uint32_t(m);
+  *shift = l;
+}
+
+}  // namespace lopt

@@ -1,0 +1,266 @@
+"""ctypes binding of liblopt (include/lopt.h).  Argument marshalling only.
+
+Every function has the C name and raises ``LoptError`` on a non-OK status.
+The library must be built (``python -m learned_optimizer_step_amd.build``);
+loading fails loudly when it is missing -- there is no fallback path.
+
+``LOpt`` is a small convenience around the C calls for PyTorch tensors: it
+allocates the state buffers and the workspace with torch (device memory is
+all torch is used for) and passes raw pointers and the current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblopt.so")
+
+LOPT_OK = 0
+LOPT_ERR_INVALID_ARGUMENT = 1
+LOPT_ERR_UNSUPPORTED = 2
+LOPT_ERR_WORKSPACE = 3
+LOPT_ERR_HIP = 4
+LOPT_ERR_STATE = 5
+STATUS_NAMES = {0: "OK", 1: "INVALID_ARGUMENT", 2: "UNSUPPORTED", 3: "WORKSPACE", 4: "HIP", 5: "STATE"}
+
+LOPT_MLP_AUTO = 0
+LOPT_MLP_VALU = 1
+LOPT_MLP_MFMA = 2
+LOPT_MAX_TIME = 11
+
+
+class LoptError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+class lopt_config(ctypes.Structure):
+    _fields_ = [("beta_m", ctypes.c_float * 3), ("beta_v", ctypes.c_float),
+                ("beta_f", ctypes.c_float * 3), ("eps_v", ctypes.c_float),
+                ("eps_f", ctypes.c_float), ("eps_norm", ctypes.c_float),
+                ("exp_mult", ctypes.c_float), ("step_mult", ctypes.c_float),
+                ("lr", ctypes.c_float), ("weight_decay", ctypes.c_float),
+                ("n_time", ctypes.c_int32), ("timescales", ctypes.c_float * LOPT_MAX_TIME),
+                ("mlp_impl", ctypes.c_int32)]
+
+
+class lopt_tensor(ctypes.Structure):
+    _fields_ = [("param", ctypes.c_void_p), ("grad", ctypes.c_void_p), ("state", ctypes.c_void_p),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Loads liblopt.so (after torch, so both share torch's HIP runtime)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with `python -m learned_optimizer_step_amd.build`")
+    try:
+        import torch  # noqa: F401  (binds libamdhip64 to torch's copy first)
+    except ImportError:
+        pass
+    lib = ctypes.CDLL(p)
+    st = ctypes.c_int
+    sig = {
+        "lopt_default_config": (st, [ctypes.POINTER(lopt_config)]),
+        "lopt_mlp_floats": (ctypes.c_size_t, [ctypes.c_int32]),
+        "lopt_create": (st, [ctypes.POINTER(lopt_config), ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)]),
+        "lopt_destroy": (None, [ctypes.c_void_p]),
+        "lopt_state_floats": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64]),
+        "lopt_workspace_bytes": (st, [ctypes.c_void_p, ctypes.POINTER(lopt_tensor), ctypes.c_int32,
+                                      ctypes.POINTER(ctypes.c_size_t)]),
+        "lopt_init_state": (st, [ctypes.c_void_p, ctypes.POINTER(lopt_tensor), ctypes.c_int32,
+                                 ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+        "lopt_step": (st, [ctypes.c_void_p, ctypes.POINTER(lopt_tensor), ctypes.c_int32, ctypes.c_void_p]),
+        "lopt_get_step": (st, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64)]),
+        "lopt_set_step": (st, [ctypes.c_void_p, ctypes.c_int64]),
+        "lopt_set_timing_events": (st, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32]),
+        "lopt_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != LOPT_OK:
+        raise LoptError(status, lopt_last_error())
+
+
+def lopt_last_error() -> str:
+    return load_library().lopt_last_error().decode()
+
+
+def lopt_default_config() -> lopt_config:
+    c = lopt_config()
+    _check(load_library().lopt_default_config(ctypes.byref(c)))
+    return c
+
+
+def lopt_mlp_floats(n_time: int) -> int:
+    return int(load_library().lopt_mlp_floats(n_time))
+
+
+def lopt_state_floats(rows: int, cols: int) -> int:
+    return int(load_library().lopt_state_floats(rows, cols))
+
+
+def lopt_create(cfg: lopt_config, mlp_host: np.ndarray) -> ctypes.c_void_p:
+    w = np.ascontiguousarray(mlp_host, dtype=np.float32)
+    if w.size != lopt_mlp_floats(cfg.n_time):
+        raise ValueError(f"expected {lopt_mlp_floats(cfg.n_time)} MLP floats, got {w.size}")
+    h = ctypes.c_void_p()
+    _check(load_library().lopt_create(ctypes.byref(cfg), w.ctypes.data_as(ctypes.c_void_p), ctypes.byref(h)))
+    return h
+
+
+def lopt_destroy(h) -> None:
+    load_library().lopt_destroy(h)
+
+
+def tensor_array(ts: Sequence[lopt_tensor]):
+    arr = (lopt_tensor * max(1, len(ts)))()
+    for i, t in enumerate(ts):
+        arr[i] = t
+    return arr
+
+
+def lopt_workspace_bytes(h, ts: Sequence[lopt_tensor]) -> int:
+    out = ctypes.c_size_t()
+    _check(load_library().lopt_workspace_bytes(h, tensor_array(ts), len(ts), ctypes.byref(out)))
+    return int(out.value)
+
+
+def lopt_init_state(h, ts: Sequence[lopt_tensor], workspace: int, ws_bytes: int, stream: int) -> None:
+    _check(load_library().lopt_init_state(h, tensor_array(ts), len(ts), ctypes.c_void_p(workspace),
+                                          ws_bytes, ctypes.c_void_p(stream)))
+
+
+def lopt_step(h, ts: Sequence[lopt_tensor], stream: int) -> None:
+    _check(load_library().lopt_step(h, tensor_array(ts), len(ts), ctypes.c_void_p(stream)))
+
+
+def lopt_get_step(h) -> int:
+    t = ctypes.c_int64()
+    _check(load_library().lopt_get_step(h, ctypes.byref(t)))
+    return int(t.value)
+
+
+def lopt_set_step(h, t: int) -> None:
+    _check(load_library().lopt_set_step(h, t))
+
+
+LOPT_N_KERNELS = 5
+KERNEL_NAMES = ("k_rowcol_sumsq", "k_moving_avg", "k_stats", "k_finalize", "k_apply")
+
+
+def lopt_set_timing_events(h, events: Sequence[int]) -> None:
+    """events: LOPT_N_KERNELS + 1 raw hipEvent_t handles (ints), or [] to stop."""
+    arr = (ctypes.c_void_p * max(1, len(events)))(*events)
+    _check(load_library().lopt_set_timing_events(h, arr, len(events)))
+
+
+def config_from(**overrides) -> lopt_config:
+    """Default config with fields replaced (lists for the array fields)."""
+    c = lopt_default_config()
+    for k, v in overrides.items():
+        if k in ("beta_m", "beta_f", "timescales"):
+            arr = getattr(c, k)
+            for i, x in enumerate(v):
+                arr[i] = x
+        else:
+            setattr(c, k, v)
+    return c
+
+
+def matrix_shape(shape) -> tuple:
+    """(rows, cols) view of a 1-D or 2-D tensor: length n -> (1, n)."""
+    if len(shape) == 1:
+        return 1, int(shape[0])
+    if len(shape) == 2:
+        return int(shape[0]), int(shape[1])
+    raise ValueError("parameters must be 1-D or 2-D")
+
+
+class LOpt:
+    """The optimizer over a list of fp32 CUDA (HIP) tensors.
+
+    params: torch tensors (1-D or 2-D, contiguous, float32, on one device).
+    mlp: packed fp32 MLP weights (numpy).  cfg: lopt_config.
+    """
+
+    def __init__(self, params, mlp: np.ndarray, cfg: Optional[lopt_config] = None):
+        import torch
+        self.torch = torch
+        self.params = list(params)
+        for p in self.params:
+            if p.dtype != torch.float32 or not p.is_cuda or not p.is_contiguous():
+                raise ValueError("parameters must be contiguous float32 device tensors")
+        self.cfg = cfg if cfg is not None else lopt_default_config()
+        self.shapes = [matrix_shape(p.shape) for p in self.params]
+        dev = self.params[0].device if self.params else torch.device("cuda")
+        self.states = [torch.empty(lopt_state_floats(r, c), dtype=torch.float32, device=dev)
+                       for r, c in self.shapes]
+        self.handle = lopt_create(self.cfg, mlp)
+        ts = self._tensors(None)  # gradients are first needed by lopt_step
+        self.ws_bytes = lopt_workspace_bytes(self.handle, ts)
+        self.workspace = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)
+        lopt_init_state(self.handle, ts, self.workspace.data_ptr(), self.ws_bytes,
+                        torch.cuda.current_stream(dev).cuda_stream)
+
+    def _tensors(self, grads) -> List[lopt_tensor]:
+        out = []
+        for i, (p, s, (r, c)) in enumerate(zip(self.params, self.states, self.shapes)):
+            g = grads[i].data_ptr() if grads is not None else None
+            out.append(lopt_tensor(p.data_ptr(), g, s.data_ptr(), r, c))
+        return out
+
+    def step(self, grads) -> None:
+        for g, p in zip(grads, self.params):
+            if g.dtype != self.torch.float32 or not g.is_contiguous() or g.numel() != p.numel():
+                raise ValueError("gradients must be contiguous float32 tensors shaped like the parameters")
+        dev = self.params[0].device if self.params else None
+        lopt_step(self.handle, self._tensors(list(grads)),
+                  self.torch.cuda.current_stream(dev).cuda_stream)
+
+    @property
+    def t(self) -> int:
+        return lopt_get_step(self.handle)
+
+    @t.setter
+    def t(self, value: int) -> None:
+        lopt_set_step(self.handle, value)
+
+    def state_views(self, i: int) -> dict:
+        """Views of tensor i's state: m (3,R,C), v (R,C), r (3,R), c (3,C)."""
+        R, C = self.shapes[i]
+        s = self.states[i]
+        n = R * C
+        return {"m": s[:3 * n].view(3, R, C), "v": s[3 * n:4 * n].view(R, C),
+                "r": s[4 * n:4 * n + 3 * R].view(3, R), "c": s[4 * n + 3 * R:].view(3, C)}
+
+    def close(self) -> None:
+        if getattr(self, "handle", None) is not None:
+            self.torch.cuda.synchronize()
+            lopt_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -225,10 +225,12 @@ def feature_scales(sum_sq: np.ndarray, n: int, hp: Hyper) -> np.ndarray:
 
 
 def mlp_forward(x: np.ndarray, w: Mlp) -> Tuple[np.ndarray, np.ndarray]:
-    h1 = np.maximum(x @ w.W1.T + w.b1, 0.0)
+    lead = x.shape[:-1]
+    x2 = x.reshape(-1, x.shape[-1])
+    h1 = np.maximum(x2 @ w.W1.T + w.b1, 0.0)
     h2 = np.maximum(h1 @ w.W2.T + w.b2, 0.0)
     out = h2 @ w.W3.T + w.b3
-    return out[..., 0], out[..., 1]
+    return out[:, 0].reshape(lead), out[:, 1].reshape(lead)
 
 
 def update_from_output(direction, magnitude, hp: Hyper):
@@ -265,7 +267,7 @@ def step_tensor(p, g, state: dict, t: int, mlp: Mlp, hp: Hyper,
     n = R * C
     acc = accumulate(G, state, hp)
     if block_rows is None:
-        block_rows = max(1, (1 << 20) // max(C, 1)) if not keep else R
+        block_rows = max(1, (1 << 14) // max(C, 1)) if not keep else R
     blocks = [slice(i, min(i + block_rows, R)) for i in range(0, R, block_rows)]
 
     # pass 1: sum of squares of each feature over the tensor
@@ -298,6 +300,42 @@ def step_tensor(p, g, state: dict, t: int, mlp: Mlp, hp: Hyper,
                  "r": acc.r.astype(sd), "c": acc.c.astype(sd)}
     info = StepInfo(sum_sq, scales, u_all, F_all, x_all, acc if keep else None)
     return p_new.astype(sd).reshape(shape), new_state, info
+
+
+def step_tensor_rows(p, g, state: dict, t: int, mlp: Mlp, hp: Hyper, rows: Sequence[int],
+                     block_rows: Optional[int] = None):
+    """One step of one tensor, with the update evaluated only on ``rows``.
+
+    The per-tensor quantities (row/column moving averages and every feature's
+    sum of squares) are computed over the whole tensor exactly as in
+    ``step_tensor``; the MLP and the update are evaluated for the listed rows
+    only.  Returns (p_new[rows], {"m": m[:, rows], "v": v[rows], "r", "c"}),
+    rounded to fp32.
+    """
+    P = as_matrix(p)
+    G = as_matrix(g)
+    R, C = G.shape
+    n = R * C
+    rows = np.asarray(rows, dtype=np.int64)
+    acc = accumulate(G, state, hp)
+    if block_rows is None:
+        block_rows = max(1, (1 << 14) // max(C, 1))
+    sum_sq = np.zeros(N_FEATURES)
+    for r0 in range(0, R, block_rows):
+        F = features(P, G, acc, hp, slice(r0, min(r0 + block_rows, R)))
+        sum_sq += (F * F).reshape(-1, N_FEATURES).sum(axis=0)
+    scales = feature_scales(sum_sq, n, hp)
+    T = time_features(t, hp)
+    sub = Accumulators(acc.m[:, rows], acc.v[rows], acc.r[:, rows], acc.c, acc.rbar)
+    F = features(P[rows], G[rows], sub, hp)
+    x = np.concatenate([F * scales, np.broadcast_to(T, (len(rows), C, hp.n_time))], axis=-1)
+    d, mg = mlp_forward(x, mlp)
+    u = update_from_output(d, mg, hp)
+    p_old = P[rows].astype(np.float64)
+    p_new = p_old - hp.lr * u - hp.lr * hp.weight_decay * p_old
+    st = {"m": sub.m.astype(np.float32), "v": sub.v.astype(np.float32),
+          "r": acc.r.astype(np.float32), "c": acc.c.astype(np.float32)}
+    return p_new.astype(np.float32), st
 
 
 def step(params: Sequence[np.ndarray], grads: Sequence[np.ndarray], states: Sequence[dict],

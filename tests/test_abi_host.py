@@ -1,0 +1,155 @@
+"""Host-side tests of the C ABI: the library loads, exports every function the
+header declares, and validates arguments before any device work.  No kernel is
+launched; pointers passed here are fake device addresses that are never
+dereferenced (validation and planning are host-only)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from learned_optimizer_step_amd import lopt as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lopt.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(lopt_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.skip("liblopt.so not built")
+    return L.load_library()
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_default_config_values(lib):
+    c = L.lopt_default_config()
+    assert list(c.beta_m) == pytest.approx([0.1, 0.5, 0.9])
+    assert c.beta_v == pytest.approx(0.999)
+    assert list(c.beta_f) == pytest.approx([0.9, 0.99, 0.999])
+    assert c.eps_v == pytest.approx(1e-8) and c.eps_f == pytest.approx(1e-20)
+    assert c.eps_norm == pytest.approx(1e-30)
+    assert c.exp_mult == pytest.approx(1e-3) and c.step_mult == pytest.approx(1e-3)
+    assert c.lr == 1.0 and c.weight_decay == 0.0 and c.n_time == 11
+    assert list(c.timescales) == pytest.approx([1, 3, 10, 30, 100, 300, 1e3, 3e3, 1e4, 3e4, 1e5])
+    assert lib.lopt_default_config(None) == L.LOPT_ERR_INVALID_ARGUMENT
+    assert "NULL" in L.lopt_last_error()
+
+
+def test_sizes(lib):
+    assert L.lopt_mlp_floats(11) == 2402
+    assert L.lopt_mlp_floats(0) == 32 * 28 + 32 + 1024 + 32 + 64 + 2
+    assert L.lopt_mlp_floats(12) == 0 and L.lopt_mlp_floats(-1) == 0
+    assert L.lopt_state_floats(4, 5) == 4 * 20 + 3 * 9
+    assert L.lopt_state_floats(1, 7) == 4 * 7 + 3 * 8
+    assert L.lopt_state_floats(0, 3) == 0
+
+
+BASE = 1 << 40  # fake, 256-byte aligned device addresses
+
+
+def fake_list(shapes, gap=1 << 30, with_grads=True):
+    ts, a = [], BASE
+    for r, c in shapes:
+        n = r * c
+        p, a = a, a + gap
+        g, a = a, a + gap
+        s, a = a, a + gap
+        ts.append(L.lopt_tensor(p, g if with_grads else None, s, r, c))
+    return ts
+
+
+def ws_status(ts):
+    out = ctypes.c_size_t()
+    st = L.load_library().lopt_workspace_bytes(None, L.tensor_array(ts), len(ts), ctypes.byref(out))
+    return st, out.value
+
+
+def test_workspace_bytes_grows_with_list(lib):
+    st1, b1 = ws_status(fake_list([(256, 256)]))
+    st2, b2 = ws_status(fake_list([(256, 256), (1, 1000), (3, 7)]))
+    assert st1 == L.LOPT_OK and st2 == L.LOPT_OK and b2 > b1 > 0 and b1 % 256 == 0
+    st0, b0 = ws_status([])
+    assert st0 == L.LOPT_OK
+
+
+def test_workspace_bytes_accepts_null_grads(lib):
+    st, b = ws_status(fake_list([(8, 8), (1, 5)], with_grads=False))
+    assert st == L.LOPT_OK and b > 0
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (lambda t: setattr(t, "rows", 0), L.LOPT_ERR_INVALID_ARGUMENT),
+    (lambda t: setattr(t, "cols", -3), L.LOPT_ERR_INVALID_ARGUMENT),
+    (lambda t: setattr(t, "param", None), L.LOPT_ERR_INVALID_ARGUMENT),
+    (lambda t: setattr(t, "state", None), L.LOPT_ERR_INVALID_ARGUMENT),
+    (lambda t: setattr(t, "param", t.param + 2), L.LOPT_ERR_UNSUPPORTED),
+    (lambda t: (setattr(t, "rows", 1 << 16), setattr(t, "cols", 1 << 15)), L.LOPT_ERR_UNSUPPORTED),
+    (lambda t: setattr(t, "grad", t.param), L.LOPT_ERR_INVALID_ARGUMENT),
+    (lambda t: setattr(t, "grad", t.state + 64), L.LOPT_ERR_INVALID_ARGUMENT),
+    (lambda t: setattr(t, "state", t.param + 4), L.LOPT_ERR_INVALID_ARGUMENT),
+])
+def test_validation_codes(lib, mutate, code):
+    ts = fake_list([(16, 16), (1, 9)])
+    mutate(ts[0])
+    st, _ = ws_status(ts)
+    assert st == code, L.lopt_last_error()
+    assert L.lopt_last_error() != ""
+
+
+def test_overlap_between_tensors_is_rejected(lib):
+    ts = fake_list([(16, 16), (16, 16)])
+    ts[1].param = ts[0].state + 8  # inside tensor 0's state
+    st, _ = ws_status(ts)
+    assert st == L.LOPT_ERR_INVALID_ARGUMENT and "overlap" in L.lopt_last_error()
+
+
+def test_shared_gradient_buffer_is_allowed(lib):
+    ts = fake_list([(16, 16), (16, 16)])
+    ts[1].grad = ts[0].grad  # read-only aliasing between gradients is harmless
+    st, _ = ws_status(ts)
+    assert st == L.LOPT_OK
+
+
+def test_create_rejects_bad_config_without_device(lib):
+    w = (ctypes.c_float * 2402)()
+    h = ctypes.c_void_p()
+    c = L.lopt_default_config()
+    c.n_time = 12
+    assert lib.lopt_create(ctypes.byref(c), w, ctypes.byref(h)) == L.LOPT_ERR_INVALID_ARGUMENT
+    c = L.config_from(beta_m=[0.1, 1.5, 0.9])
+    assert lib.lopt_create(ctypes.byref(c), w, ctypes.byref(h)) == L.LOPT_ERR_INVALID_ARGUMENT
+    c = L.config_from(eps_v=-1.0)
+    assert lib.lopt_create(ctypes.byref(c), w, ctypes.byref(h)) == L.LOPT_ERR_INVALID_ARGUMENT
+    c = L.config_from(timescales=[1.0, 0.0])
+    assert lib.lopt_create(ctypes.byref(c), w, ctypes.byref(h)) == L.LOPT_ERR_INVALID_ARGUMENT
+    c = L.lopt_default_config()
+    assert lib.lopt_create(ctypes.byref(c), None, ctypes.byref(h)) == L.LOPT_ERR_INVALID_ARGUMENT
+    assert lib.lopt_create(None, w, ctypes.byref(h)) == L.LOPT_ERR_INVALID_ARGUMENT
+    assert h.value is None
+
+
+def test_null_handle_calls(lib):
+    t = ctypes.c_int64()
+    assert lib.lopt_get_step(None, ctypes.byref(t)) == L.LOPT_ERR_INVALID_ARGUMENT
+    assert lib.lopt_set_step(None, 3) == L.LOPT_ERR_INVALID_ARGUMENT
+    assert lib.lopt_step(None, None, 0, None) == L.LOPT_ERR_INVALID_ARGUMENT
+    assert lib.lopt_init_state(None, None, 0, None, 0, None) == L.LOPT_ERR_INVALID_ARGUMENT
+    lib.lopt_destroy(None)  # no-op
+
+
+def test_binding_has_the_c_names():
+    for n in declared_functions():
+        assert hasattr(L, n), n

@@ -1,0 +1,183 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bar: |gpu - oracle| <= 1e-7 + 1e-5 |oracle| element-wise on p, m1..m3, v,
+r1..r3 and c1..c3 after each case's step count.  Integer/bitwise properties
+(determinism, resume, tensor independence) are checked bit for bit.
+"""
+import numpy as np
+import pytest
+
+from gpu_harness import GpuRun, compare, hyper_from_cfg, oracle_run, parity, parity_one_step_rows, say
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("no GPU", allow_module_level=True)
+
+from learned_optimizer_step_amd import lopt as L  # noqa: E402
+from learned_optimizer_step_amd import workloads as W  # noqa: E402
+
+IMPLS = [L.LOPT_MLP_VALU]
+
+EDGE_SHAPES = [(1,), (2,), (3,), (15,), (16,), (17,), (63,), (65,), (40000,),
+               (1, 1), (2, 3), (3, 1), (7, 1), (17, 33), (65, 3), (4, 513), (300, 2),
+               (129, 257), (600, 5), (5, 600), (1000, 1), (33, 64)]
+
+
+def mlp(n_time=11, bias_std=0.0):
+    return W.mlp_weights(n_time, bias_std=bias_std)
+
+
+def check(errs):
+    assert not errs, "\n".join(errs[:20])
+
+
+@pytest.mark.parametrize("impl", IMPLS)
+def test_single256_ten_steps(impl):
+    w = W.get_workload("single256")
+    check(parity(w, mlp(), L.config_from(mlp_impl=impl), torch))
+
+
+@pytest.mark.parametrize("impl", IMPLS)
+def test_edge_shapes_ten_steps(impl):
+    w = W.custom_workload("edges", EDGE_SHAPES, grad_std=1e-2, steps=10, wid=101)
+    check(parity(w, mlp(bias_std=0.1), L.config_from(mlp_impl=impl), torch))
+
+
+@pytest.mark.parametrize("impl", IMPLS)
+def test_no_time_features_lr_wd_prewarmed(impl):
+    w = W.custom_workload("nt0", [(37, 41), (1, 77), (9,)], grad_std=1e-3, steps=4,
+                          prewarm_std=1e-3, wid=102)
+    cfg = L.config_from(mlp_impl=impl, n_time=0, lr=0.5, weight_decay=0.01, exp_mult=0.05, step_mult=0.01)
+    check(parity(w, mlp(n_time=0, bias_std=0.2), cfg, torch))
+
+
+@pytest.mark.parametrize("impl", IMPLS)
+def test_zero_gradients_stay_finite(impl):
+    w = W.custom_workload("zeros", [(8, 8), (1, 5)], grad_std=0.0, steps=3, wid=103)
+    check(parity(w, mlp(bias_std=0.1), L.config_from(mlp_impl=impl), torch))
+
+
+@pytest.mark.parametrize("impl", IMPLS)
+def test_single4096_prewarmed(impl):
+    w = W.get_workload("single4096")
+    check(parity(w, mlp(), L.config_from(mlp_impl=impl), torch))
+
+
+@pytest.mark.parametrize("impl", IMPLS)
+def test_vit_b16_five_steps_subset(impl):
+    # full 147-tensor workload on the GPU for 5 steps; the oracle follows a
+    # subset covering every shape class (tensors are independent)
+    w = W.get_workload("vit_b16")
+    names = [t.name for t in w.tensors]
+    subset = [names.index(n) for n in ("pos_embed", "blocks.0.qkv.weight", "blocks.0.qkv.bias",
+                                       "blocks.5.norm2.weight", "blocks.11.fc2.weight",
+                                       "blocks.11.fc1.bias", "head")]
+    check(parity(w, mlp(), L.config_from(mlp_impl=impl), torch, subset=subset))
+
+
+def sample_rows(R, k, seed):
+    rng = np.random.default_rng(seed)
+    return sorted(set([0, R - 1] + rng.choice(R, min(R, k), replace=False).tolist()))
+
+
+@pytest.mark.parametrize("impl", IMPLS)
+def test_llama1b_one_step_sampled(impl):
+    w = W.get_workload("llama1b")
+    names = [t.name for t in w.tensors]
+    picks = {names.index("layers.0.q"): sample_rows(2048, 24, 1),
+             names.index("layers.21.down"): sample_rows(5632, 24, 2),
+             names.index("layers.3.attn_norm"): None,
+             names.index("unembed"): sample_rows(32000, 24, 3)}
+    check(parity_one_step_rows(w, mlp(), L.config_from(mlp_impl=impl), torch, picks))
+
+
+@pytest.mark.parametrize("impl", IMPLS)
+def test_ragged10k_one_step_sampled(impl):
+    w = W.get_workload("ragged10k")
+    sizes = np.array([t.n for t in w.tensors])
+    rng = np.random.default_rng(7)
+    idx = set(rng.choice(len(w.tensors), 120, replace=False).tolist())
+    picks = {i: None for i in idx if sizes[i] < 300_000}
+    big = int(sizes.argmax())
+    picks[int(sizes.argmin())] = None
+    picks[big] = sample_rows(w.tensors[big].rows, 16, 4) if w.tensors[big].rows > 1 else None
+    check(parity_one_step_rows(w, mlp(), L.config_from(mlp_impl=impl), torch, picks))
+
+
+def _run_states(w, cfg, steps, m):
+    run = GpuRun(w, m, cfg, torch)
+    for t in range(1, steps + 1):
+        run.step(t)
+    out = [run.fetch(i) for i in range(len(w.tensors))]
+    run.close()
+    return out
+
+
+def test_bitwise_deterministic():
+    w = W.custom_workload("det", [(300, 200), (1, 5000), (1000, 3)], steps=3, wid=104)
+    m = mlp(bias_std=0.1)
+    a = _run_states(w, L.config_from(), 3, m)
+    b = _run_states(w, L.config_from(), 3, m)
+    for x, y in zip(a, b):
+        for k in x:
+            assert np.array_equal(x[k], y[k]), k
+
+
+def test_list_equals_separate_calls():
+    shapes = [(70, 90), (1, 333), (5, 1)]
+    m = mlp(bias_std=0.1)
+    w = W.custom_workload("ind", shapes, steps=2, wid=105)
+    together = _run_states(w, L.config_from(), 2, m)
+    for i, tt in enumerate(w.tensors):
+        p = torch.from_numpy(W.param_init(w, i).reshape(tt.shape)).cuda()
+        opt = L.LOpt([p], m, L.config_from())
+        for t in (1, 2):
+            opt.step([torch.from_numpy(W.grad_at(w, i, t).reshape(tt.shape)).cuda()])
+        torch.cuda.synchronize()
+        v = opt.state_views(0)
+        assert np.array_equal(p.cpu().numpy().reshape(tt.rows, tt.cols), together[i]["p"]), i
+        for k in ("m", "v", "r", "c"):
+            assert np.array_equal(v[k].cpu().numpy(), together[i][k]), (i, k)
+        opt.close()
+
+
+def test_resume_equals_uninterrupted_and_grad_pointers_may_change():
+    shapes = [(40, 50), (1, 64)]
+    m = mlp(bias_std=0.1)
+    w = W.custom_workload("res", shapes, steps=10, wid=106)
+    full = _run_states(w, L.config_from(), 10, m)
+    run = GpuRun(w, m, L.config_from(), torch)
+    for t in range(1, 6):
+        run.step(t)          # fresh gradient tensors each step: pointers change
+    saved = [run.fetch(i) for i in range(len(shapes))]
+    run.close()
+    run2 = GpuRun(w, m, L.config_from(), torch)
+    for i in range(len(shapes)):
+        run2.params[i].copy_(torch.from_numpy(saved[i]["p"].reshape(w.tensors[i].shape)))
+        v = run2.opt.state_views(i)
+        for k in ("m", "v", "r", "c"):
+            v[k].copy_(torch.from_numpy(saved[i][k]))
+    run2.opt.t = 5
+    for t in range(6, 11):
+        run2.step(t)
+    assert run2.opt.t == 10
+    for i in range(len(shapes)):
+        got = run2.fetch(i)
+        for k in got:
+            assert np.array_equal(got[k], full[i][k]), (i, k)
+    run2.close()
+
+
+def test_step_rejects_a_different_list():
+    p = torch.zeros(4, 4, device="cuda")
+    q = torch.zeros(4, 4, device="cuda")
+    opt = L.LOpt([p], mlp(), L.config_from())
+    g = torch.zeros(4, 4, device="cuda")
+    with pytest.raises(L.LoptError) as e:
+        L.lopt_step(opt.handle, [L.lopt_tensor(q.data_ptr(), g.data_ptr(), opt.states[0].data_ptr(), 4, 4)],
+                    torch.cuda.current_stream().cuda_stream)
+    assert e.value.status == L.LOPT_ERR_STATE
+    assert opt.t == 0
+    opt.close()

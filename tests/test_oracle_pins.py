@@ -361,3 +361,16 @@ def test_block_rows_only_changes_summation_order():
     b = step_tensor(p, g, st, 2, w, Hyper(), block_rows=5, store_dtype=F64)
     np.testing.assert_allclose(a[0], b[0], rtol=1e-14)
     np.testing.assert_allclose(a[2].sum_sq, b[2].sum_sq, rtol=1e-13)
+
+
+def test_sampled_rows_equal_full_step():
+    p, g, st = random_case(23, 9, seed=18)
+    w = random_mlp(18)
+    pf, sf, _ = step_tensor(p, g, st, 3, w, Hyper())
+    rows = [0, 5, 22, 7]
+    from oracle import step_tensor_rows
+    pr, sr = step_tensor_rows(p, g, st, 3, w, Hyper(), rows, block_rows=4)
+    np.testing.assert_allclose(pr, pf[rows], rtol=1e-7, atol=1e-30)
+    np.testing.assert_array_equal(sr["r"], sf["r"])
+    np.testing.assert_array_equal(sr["c"], sf["c"])
+    np.testing.assert_array_equal(sr["m"], sf["m"][:, rows])
