@@ -462,6 +462,135 @@ __global__ __launch_bounds__(kBlock) void k_apply_valu(StepCtx c, StepParams hp)
 }
 
 // ---------------------------------------------------------------------------
+// k_apply_mfma: the page's kernel 2 with layers 1 and 2 of the MLP on the fp32
+// matrix cores.  A wave owns 64 elements per iteration, one per lane, for all
+// per-element work (loads, features, update, stores).  The MLP is a pair of
+// 32-element GEMM chains per wave, v_mfma_f32_32x32x2_f32 with the hidden
+// units as M (weights = A operand, register resident), the elements as N and
+// the features as K:
+//   layer 1: 14 K-steps of two features.  v_permlane32_swap of the feature
+//     pair (2s, 2s+1) gives, in one instruction, the B operands of both
+//     halves: [F_2s of elements 0..31 | F_2s+1 of elements 0..31] and
+//     [F_2s of elements 32..63 | F_2s+1 of elements 32..63].
+//   layer 2: the layer-1 accumulator register r of a lane holds hidden unit
+//     8(r/4) + 4(lane/32) + r%4 of element lane%32, which is exactly a K-step
+//     B operand if W2's columns are visited in that order (no data movement).
+//   layer 3 (32 -> 2) on the vector ALU: per-lane partial dot products over
+//     the lane's 16 hidden units, completed with one more swap.
+// Biases enter as the C operand of the first MFMA of each chain; the feature
+// scales s_d are folded into W1's columns once per chunk.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ int acc_row(int r, int half) { return 8 * (r >> 2) + 4 * half + (r & 3); }
+
+__device__ __forceinline__ void swap_halves(float x, float y, float& lo, float& hi) {
+  // lo = [x lanes 0..31 | y lanes 0..31], hi = [x lanes 32..63 | y lanes 32..63]
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+
+template <bool VEC>
+__device__ __forceinline__ void apply_mfma_body(const StepCtx& c, const StepParams& hp, const Chunk& ch,
+                                                const TensorDesc& d) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int half = lane >> 5;
+  const int row = lane & 31;
+  const float* __restrict__ g = c.grads[ch.tensor];
+  const float* __restrict__ pk = c.packed;
+  const float* __restrict__ sc = c.scales + size_t(ch.tensor) * kStatStride;
+
+  float a1[kNF / 2];   // W1[row][2s + half] * s_(2s + half)
+  float a2[kH / 2];    // W2[row][acc_row(s, half)]
+  f32x16 bias1, bias2;
+  float w3d[16], w3m[16];
+#pragma unroll
+  for (int q = 0; q < kNF / 2; ++q) a1[q] = pk[kPkW1 + row * kNF + 2 * q + half] * sc[2 * q + half];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int hr = acc_row(q, half);
+    a2[q] = pk[kPkW2 + row * kH + hr];
+    bias1[q] = pk[kPkB1 + hr];
+    bias2[q] = pk[kPkB2 + hr];
+    w3d[q] = pk[kPkW3 + hr];
+    w3m[q] = pk[kPkW3 + kH + hr];
+  }
+  const float b3d = pk[kPkB3], b3m = pk[kPkB3 + 1];
+  float sr[3];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) sr[k] = sc[kNF + k];
+  const size_t n = d.n;
+
+  for (uint32_t base = ch.e0 + wave * 64; base < ch.e1; base += kBlock) {
+    const uint32_t e = base + lane;
+    const bool valid = e < ch.e1;
+    Elem x;
+    load_elem<VEC>(d, g, c.ws, valid ? e : ch.e0, x);
+    const float p_old = x.p;
+    float F[kNF], cn[3];
+    build_features<VEC>(hp, x, sr, F, cn);
+
+    f32x16 accA = bias1, accB = bias1;
+#pragma unroll
+    for (int q = 0; q < kNF / 2; ++q) {
+      float bA, bB;
+      swap_halves(F[2 * q], F[2 * q + 1], bA, bB);
+      accA = __builtin_amdgcn_mfma_f32_32x32x2f32(a1[q], bA, accA, 0, 0, 0);
+      accB = __builtin_amdgcn_mfma_f32_32x32x2f32(a1[q], bB, accB, 0, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      accA[q] = fmaxf(accA[q], 0.f);
+      accB[q] = fmaxf(accB[q], 0.f);
+    }
+    f32x16 acc2A = bias2, acc2B = bias2;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      acc2A = __builtin_amdgcn_mfma_f32_32x32x2f32(a2[q], accA[q], acc2A, 0, 0, 0);
+      acc2B = __builtin_amdgcn_mfma_f32_32x32x2f32(a2[q], accB[q], acc2B, 0, 0, 0);
+    }
+    float dA = 0.f, mA = 0.f, dB = 0.f, mB = 0.f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const float hA = fmaxf(acc2A[q], 0.f), hB = fmaxf(acc2B[q], 0.f);
+      dA = fmaf(w3d[q], hA, dA);
+      mA = fmaf(w3m[q], hA, mA);
+      dB = fmaf(w3d[q], hB, dB);
+      mB = fmaf(w3m[q], hB, mB);
+    }
+    // lane l < 32 holds chain A's partials of element l (its half) and lane
+    // l + 32 the other half; chain B likewise for element 32 + l.
+    float d0, d1, m0, m1;
+    swap_halves(dA, dB, d0, d1);
+    swap_halves(mA, mB, m0, m1);
+    const float dir = (d0 + d1) + b3d;
+    const float mag = (m0 + m1) + b3m;
+    if (valid) {
+      const float u = dir * expf(mag * hp.exp_mult) * hp.step_mult;
+      d.p[e] = p_old - hp.lr * fmaf(hp.weight_decay, p_old, u);
+      float* st = d.st;
+      st[e] = x.m[0];
+      st[n + e] = x.m[1];
+      st[2 * n + e] = x.m[2];
+      st[3 * n + e] = x.v;
+      if (VEC) {
+        float* cs = st + 4 * n + 3;
+#pragma unroll
+        for (int k = 0; k < 3; ++k) cs[k * n + e] = cn[k];
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void k_apply_mfma(StepCtx c, StepParams hp) {
+  const Chunk ch = c.chunks[blockIdx.x];
+  const TensorDesc d = c.desc[ch.tensor];
+  if (d.vec) apply_mfma_body<true>(c, hp, ch, d);
+  else apply_mfma_body<false>(c, hp, ch, d);
+}
+
+// ---------------------------------------------------------------------------
 // k_zero_state: zero-fills the state over the chunk list (per-element blocks
 // of each chunk; the first chunk of a tensor also clears r_k and c_k).
 __global__ __launch_bounds__(kBlock) void k_zero_state(StepCtx c) {
@@ -501,7 +630,10 @@ hipError_t launch_step(const StepCtx& c, const StepParams& p, hipStream_t s, con
   if ((e = mark(3)) != hipSuccess) return e;
   hipLaunchKernelGGL(k_finalize, dim3(c.n_tensors), dim3(kBlock), 0, s, c, p);
   if ((e = mark(4)) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_apply_valu, dim3(c.n_chunks), dim3(kBlock), 0, s, c, p);
+  if (c.mlp_impl == 1)
+    hipLaunchKernelGGL(k_apply_valu, dim3(c.n_chunks), dim3(kBlock), 0, s, c, p);
+  else
+    hipLaunchKernelGGL(k_apply_mfma, dim3(c.n_chunks), dim3(kBlock), 0, s, c, p);
   if ((e = mark(5)) != hipSuccess) return e;
   return hipGetLastError();
 }

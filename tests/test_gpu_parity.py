@@ -18,7 +18,7 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU container
 from learned_optimizer_step_amd import lopt as L  # noqa: E402
 from learned_optimizer_step_amd import workloads as W  # noqa: E402
 
-IMPLS = [L.LOPT_MLP_VALU]
+IMPLS = [L.LOPT_MLP_VALU, L.LOPT_MLP_MFMA]
 
 EDGE_SHAPES = [(1,), (2,), (3,), (15,), (16,), (17,), (63,), (65,), (40000,),
                (1, 1), (2, 3), (3, 1), (7, 1), (17, 33), (65, 3), (4, 513), (300, 2),
