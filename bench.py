@@ -32,8 +32,8 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(seconds_hint: float):
-    """The oracle on one ViT-B/16 block (12 tensors), one step, on host cores."""
+def cpu_baseline(blocks: int = 5):
+    """The oracle on the first ``blocks`` ViT-B/16 transformer blocks, one step, on host cores."""
     import numpy as np
     from threadpoolctl import threadpool_info, threadpool_limits
 
@@ -43,7 +43,8 @@ def cpu_baseline(seconds_hint: float):
     cores = len(os.sched_getaffinity(0))
     threads = min(cores, 16)
     w = W.get_workload("vit_b16")
-    idx = [i for i, t in enumerate(w.tensors) if t.name.startswith("blocks.0.")]
+    prefixes = tuple(f"blocks.{b}." for b in range(blocks))
+    idx = [i for i, t in enumerate(w.tensors) if t.name.startswith(prefixes)]
     ps = [W.param_init(w, i) for i in idx]
     gs = [W.grad_at(w, i, 1) for i in idx]
     sts = [W.state_init(w, i) for i in idx]
@@ -54,7 +55,7 @@ def cpu_baseline(seconds_hint: float):
         oracle.step(ps, gs, sts, 1, mlp, oracle.Hyper())
         dt = time.perf_counter() - t0
     return {"value": n / dt / 1e9, "unit": "G params/s", "cores": threads, "kind": "oracle",
-            "sample": f"one ViT-B/16 block (blocks.0.*: {len(idx)} tensors, {n} params), 1 step, "
+            "sample": f"ViT-B/16 blocks 0-{blocks - 1} ({len(idx)} tensors, {n} params), 1 step, "
                       f"fp64 NumPy, {threads} BLAS threads, {dt:.1f} s"}
 
 
@@ -66,6 +67,8 @@ def main():
     ap.add_argument("--workload", default="vit_b16")
     ap.add_argument("--impl", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after the timed steps, run one plain 1 GiB device copy (reference for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
@@ -120,6 +123,13 @@ def main():
                      for k in range(args.steps)])
     kern_ms = kern.mean(axis=0)
     opt.close()
+    if args.calibrate_copy:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)   # reads and writes exactly 1 GiB
+        torch.cuda.synchronize()
+        del src, dst
 
     n = w.n_params
     value = n / (ms * 1e-3) / 1e9
@@ -151,7 +161,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle on host cores)")
-        out["cpu_baseline"] = cpu_baseline(20.0)
+        out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)
 
 

@@ -13,7 +13,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "liblopt.so")
-SOURCES = ["lopt_kernels.hip", "lopt_api.cpp"]
+# (source, extra flags).  The apply kernels assume finite values in their
+# ReLUs (-fno-honor-nans gives a single v_max_f32 per ReLU).
+SOURCES = [("lopt_kernels.hip", []), ("lopt_apply.hip", ["-fno-honor-nans"]), ("lopt_api.cpp", [])]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU instructions are disabled for all device code.
@@ -27,22 +29,33 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
-    out_tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include"), *DEVICE_FLAGS,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", out_tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "is not a recognized feature for this target"
-    msgs = [l for l in (res.stdout + res.stderr).splitlines() if noise not in l]
+    noise = ("is not a recognized feature for this target", "argument unused during compilation")
+    msgs = [l for l in (res.stdout + res.stderr).splitlines() if not any(x in l for x in noise)]
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(out_tmp, LIB)
-    return LIB
+
+
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = []
+    for src, extra in SOURCES:
+        obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+        _run([hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-c", "-Wall",
+              "-Wno-unused-function", "-I", os.path.join(ROOT, "include"), *DEVICE_FLAGS, *extra,
+              *[f"-D{d}" for d in defines],
+              os.path.join(CSRC, src), "-o", obj], verbose)
+        objs.append(obj)
+    out_tmp = out + ".tmp"
+    _run([hipcc(), "-shared", "-fPIC", *objs, "-o", out_tmp], verbose)
+    os.replace(out_tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -1,0 +1,242 @@
+// Apply kernels of the optimizer step (the PyLO page's kernel 2: features
+// rebuilt in registers, normalised, MLP evaluated inline, parameter written).
+//
+// This translation unit is compiled with -fno-honor-nans: the ReLUs then map
+// to one v_max_f32 each instead of a quieting v_max followed by the max.
+// Non-finite inputs are not checked by the library (they propagate into the
+// accumulators; a NaN pre-activation leaves the ReLU as 0 either way).
+#include <hip/hip_runtime.h>
+
+#include "lopt_device.h"
+
+namespace lopt {
+
+// ---------------------------------------------------------------------------
+// k_apply_valu: the page's kernel 2 with the MLP on the vector ALU.  Weights
+// are read through uniform (scalar) loads from the packed copy, so every FMA
+// takes its weight from a scalar register.
+template <bool VEC>
+__device__ __forceinline__ void apply_valu_body(const StepCtx& c, const StepParams& hp, const Chunk& ch,
+                                                const TensorDesc& d) {
+  const float* __restrict__ g = c.grads[ch.tensor];
+  const float* __restrict__ pk = c.packed;
+  const float* __restrict__ sc = c.scales + size_t(ch.tensor) * kStatStride;
+  const size_t n = d.n;
+  for (uint32_t e = ch.e0 + threadIdx.x; e < ch.e1; e += kBlock) {
+    Elem x;
+    load_elem<VEC>(d, g, c.ws, e, x);
+    const float p_old = x.p;
+    float F[kNF], cn[3];
+    build_features<VEC>(hp, x, F, cn);
+#pragma unroll
+    for (int f = 0; f < kNF; ++f) F[f] *= sc[f];
+    float h1[kH];
+#pragma unroll
+    for (int o = 0; o < kH; ++o) {
+      float a = pk[kPkB1 + o];
+#pragma unroll
+      for (int f = 0; f < kNF; ++f) a = fmaf(pk[kPkW1 + o * kNF + f], F[f], a);
+      h1[o] = fmaxf(a, 0.f);
+    }
+    float dir = pk[kPkB3], mag = pk[kPkB3 + 1];
+#pragma unroll
+    for (int o = 0; o < kH; ++o) {
+      float a = pk[kPkB2 + o];
+#pragma unroll
+      for (int f = 0; f < kH; ++f) a = fmaf(pk[kPkW2 + o * kH + f], h1[f], a);
+      a = fmaxf(a, 0.f);
+      dir = fmaf(pk[kPkW3 + o], a, dir);
+      mag = fmaf(pk[kPkW3 + kH + o], a, mag);
+    }
+    const float u = dir * expf(mag * hp.exp_mult) * hp.step_mult;
+    d.p[e] = p_old - hp.lr * fmaf(hp.weight_decay, p_old, u);
+    float* st = d.st;
+    st[e] = x.m[0];
+    st[n + e] = x.m[1];
+    st[2 * n + e] = x.m[2];
+    st[3 * n + e] = x.v;
+    if (VEC) {
+      float* cs = st + 4 * n + 3;
+#pragma unroll
+      for (int k = 0; k < 3; ++k) cs[k * n + e] = cn[k];
+    }
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void k_apply_valu(StepCtx c, StepParams hp) {
+  const Chunk ch = c.chunks[blockIdx.x];
+  const TensorDesc d = c.desc[ch.tensor];
+  if (d.vec) apply_valu_body<true>(c, hp, ch, d);
+  else apply_valu_body<false>(c, hp, ch, d);
+}
+
+// ---------------------------------------------------------------------------
+// k_apply_mfma: the page's kernel 2 with layers 1 and 2 of the MLP on the fp32
+// matrix cores.  A wave owns 64 elements per iteration, one per lane, for all
+// per-element work (loads, features, update, stores).  The MLP is a pair of
+// 32-element GEMM chains per wave, v_mfma_f32_32x32x2_f32 with the hidden
+// units as M (weights = A operand, register resident), the elements as N and
+// the features as K:
+//   layer 1: 14 K-steps of two features.  v_permlane32_swap of the feature
+//     pair (2s, 2s+1) gives, in one instruction, the B operands of both
+//     halves: [F_2s of elements 0..31 | F_2s+1 of elements 0..31] and
+//     [F_2s of elements 32..63 | F_2s+1 of elements 32..63].
+//   layer 2: the layer-1 accumulator register r of a lane holds hidden unit
+//     8(r/4) + 4(lane/32) + r%4 of element lane%32, which is exactly a K-step
+//     B operand if W2's columns are visited in that order (no data movement).
+//   layer 3 (32 -> 2) on the vector ALU: per-lane partial dot products over
+//     the lane's 16 hidden units, completed with one more swap.
+// Biases enter as the C operand of the first MFMA of each chain (read from
+// LDS with W3 each iteration, which keeps the kernel within 168 VGPRs); the
+// feature scales s_d are folded into W1's columns once per chunk.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ int acc_row(int r, int half) { return 8 * (r >> 2) + 4 * half + (r & 3); }
+
+__device__ __forceinline__ void swap_halves(float x, float y, float& lo, float& hi) {
+  // lo = [x lanes 0..31 | y lanes 0..31], hi = [x lanes 32..63 | y lanes 32..63]
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+
+template <bool VEC>
+__device__ __forceinline__ void apply_mfma_body(const StepCtx& c, const StepParams& hp, const Chunk& ch,
+                                                const TensorDesc& d) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int half = lane >> 5;
+  const int row = lane & 31;
+  const float* __restrict__ g = c.grads[ch.tensor];
+  const float* __restrict__ pk = c.packed;
+  const float* __restrict__ sc = c.scales + size_t(ch.tensor) * kStatStride;
+
+  float a1[kNF / 2];   // W1[row][2s + half] * s_(2s + half)
+  float a2[kH / 2];    // W2[row][acc_row(s, half)]
+#pragma unroll
+  for (int q = 0; q < kNF / 2; ++q) a1[q] = pk[kPkW1 + row * kNF + 2 * q + half] * sc[2 * q + half];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) a2[q] = pk[kPkW2 + row * kH + acc_row(q, half)];
+  // Biases and W3 in accumulator-row order per lane half; read with
+  // ds_read_b128 when needed instead of holding 64 registers.
+  __shared__ float4 tab[4][2][4];   // {b1, b2, W3 dir, W3 mag} x half x 16 floats
+  if (threadIdx.x < 128) {
+    const int which = threadIdx.x >> 5, h = (threadIdx.x >> 4) & 1, q = threadIdx.x & 15;
+    const int hr = acc_row(q, h);
+    const float v = which == 0 ? pk[kPkB1 + hr] : which == 1 ? pk[kPkB2 + hr]
+                    : which == 2 ? pk[kPkW3 + hr] : pk[kPkW3 + kH + hr];
+    reinterpret_cast<float*>(&tab[which][h][0])[q] = v;
+  }
+  __syncthreads();
+  const float b3d = pk[kPkB3], b3m = pk[kPkB3 + 1];
+  const size_t n = d.n;
+
+  uint32_t base = ch.e0 + wave * 64;
+  if (base >= ch.e1) return;  // this wave has no elements in the chunk
+  // Inputs are prefetched one iteration ahead so their latency overlaps the
+  // matrix-core chains of the current iteration.
+  Elem xn;
+  {
+    const uint32_t e = base + lane;
+    load_elem<VEC>(d, g, c.ws, e < ch.e1 ? e : ch.e0, xn);
+  }
+  for (; base < ch.e1; base += kBlock) {
+    const uint32_t e = base + lane;
+    const bool valid = e < ch.e1;
+    Elem x = xn;
+    if (base + kBlock < ch.e1) {
+      const uint32_t en = base + kBlock + lane;
+      load_elem<VEC>(d, g, c.ws, en < ch.e1 ? en : ch.e0, xn);
+    }
+    const float p_old = x.p;
+    float F[kNF], cn[3];
+    build_features<VEC>(hp, x, F, cn);
+
+    f32x16 bias1, bias2;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 v = tab[0][half][q];
+      bias1[4 * q] = v.x; bias1[4 * q + 1] = v.y; bias1[4 * q + 2] = v.z; bias1[4 * q + 3] = v.w;
+    }
+    f32x16 accA = bias1, accB = bias1;
+#pragma unroll
+    for (int q = 0; q < kNF / 2; ++q) {
+      float bA, bB;
+      swap_halves(F[2 * q], F[2 * q + 1], bA, bB);
+      accA = __builtin_amdgcn_mfma_f32_32x32x2f32(a1[q], bA, accA, 0, 0, 0);
+      accB = __builtin_amdgcn_mfma_f32_32x32x2f32(a1[q], bB, accB, 0, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      accA[q] = fmaxf(accA[q], 0.f);
+      accB[q] = fmaxf(accB[q], 0.f);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 v = tab[1][half][q];
+      bias2[4 * q] = v.x; bias2[4 * q + 1] = v.y; bias2[4 * q + 2] = v.z; bias2[4 * q + 3] = v.w;
+    }
+    f32x16 acc2A = bias2, acc2B = bias2;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      acc2A = __builtin_amdgcn_mfma_f32_32x32x2f32(a2[q], accA[q], acc2A, 0, 0, 0);
+      acc2B = __builtin_amdgcn_mfma_f32_32x32x2f32(a2[q], accB[q], acc2B, 0, 0, 0);
+    }
+    float dA = 0.f, mA = 0.f, dB = 0.f, mB = 0.f;
+    float w3d[16], w3m[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 v = tab[2][half][q], u = tab[3][half][q];
+      w3d[4 * q] = v.x; w3d[4 * q + 1] = v.y; w3d[4 * q + 2] = v.z; w3d[4 * q + 3] = v.w;
+      w3m[4 * q] = u.x; w3m[4 * q + 1] = u.y; w3m[4 * q + 2] = u.z; w3m[4 * q + 3] = u.w;
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const float hA = fmaxf(acc2A[q], 0.f), hB = fmaxf(acc2B[q], 0.f);
+      dA = fmaf(w3d[q], hA, dA);
+      mA = fmaf(w3m[q], hA, mA);
+      dB = fmaf(w3d[q], hB, dB);
+      mB = fmaf(w3m[q], hB, mB);
+    }
+    // lane l < 32 holds chain A's partials of element l (its half) and lane
+    // l + 32 the other half; chain B likewise for element 32 + l.
+    float d0, d1, m0, m1;
+    swap_halves(dA, dB, d0, d1);
+    swap_halves(mA, mB, m0, m1);
+    const float dir = (d0 + d1) + b3d;
+    const float mag = (m0 + m1) + b3m;
+    if (valid) {
+      const float u = dir * expf(mag * hp.exp_mult) * hp.step_mult;
+      gptr(d.p)[e] = p_old - hp.lr * fmaf(hp.weight_decay, p_old, u);
+      gfloat* st = gptr(d.st);
+      st[e] = x.m[0];
+      st[n + e] = x.m[1];
+      st[2 * n + e] = x.m[2];
+      st[3 * n + e] = x.v;
+      if (VEC) {
+        gfloat* cs = st + 4 * n + 3;
+#pragma unroll
+        for (int k = 0; k < 3; ++k) cs[k * n + e] = cn[k];
+      }
+    }
+  }
+}
+
+// Three waves per SIMD (<= 168 VGPRs): while one wave streams its inputs or
+// runs the feature / layer-3 vector code, another keeps the matrix core busy.
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void k_apply_mfma(StepCtx c, StepParams hp) {
+  const Chunk ch = c.chunks[blockIdx.x];
+  const TensorDesc d = c.desc[ch.tensor];
+  if (d.vec) apply_mfma_body<true>(c, hp, ch, d);
+  else apply_mfma_body<false>(c, hp, ch, d);
+}
+
+hipError_t launch_apply(const StepCtx& c, const StepParams& p, hipStream_t s) {
+  if (c.mlp_impl == 1)
+    hipLaunchKernelGGL(k_apply_valu, dim3(c.n_chunks), dim3(kBlock), 0, s, c, p);
+  else
+    hipLaunchKernelGGL(k_apply_mfma, dim3(c.n_chunks), dim3(kBlock), 0, s, c, p);
+  return hipGetLastError();
+}
+
+}  // namespace lopt

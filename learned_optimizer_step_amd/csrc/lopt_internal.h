@@ -113,6 +113,7 @@ hipError_t launch_zero_state(const StepCtx& c, hipStream_t s);
 constexpr int kNumKernels = 5;
 // events: nullptr, or kNumKernels + 1 events recorded around the launches.
 hipError_t launch_step(const StepCtx& c, const StepParams& p, hipStream_t s, const hipEvent_t* events);
+hipError_t launch_apply(const StepCtx& c, const StepParams& p, hipStream_t s);
 
 // Fast division by a 32-bit divisor for numerators below 2^31
 // (round-up multiplier method, Granlund & Montgomery 1994).

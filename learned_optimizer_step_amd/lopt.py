@@ -62,7 +62,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     global _lib
     if _lib is not None and path is None:
         return _lib
-    p = path or LIB_PATH
+    p = path or os.environ.get("LOPT_LIBRARY") or LIB_PATH
     if not os.path.exists(p):
         raise RuntimeError(f"{p} is missing: build it with `python -m learned_optimizer_step_amd.build`")
     try:
