@@ -82,7 +82,8 @@ typedef struct lopt_config {
  *            m1 | m2 | m3 | v      (rows*cols each, row-major)
  *            r1 | r2 | r3          (rows each)
  *            c1 | c2 | c3          (cols each)
- *   rows, cols: >= 1 and rows*cols < 2^31.  A 1-D tensor of length n is
+ *   rows, cols: >= 1, rows*cols < 2^31, and cols < 2^28 when rows > 1
+ *          (UNSUPPORTED otherwise).  A 1-D tensor of length n is
  *          passed as rows = 1, cols = n; then c_k is per element and r_k is a
  *          single value.
  * grad must not overlap param or state; no two tensors may overlap. */

@@ -122,6 +122,8 @@ void validate_tensors(const lopt_tensor* ts, int32_t n, bool require_grads) {
     if (t.rows < 1 || t.cols < 1) fail(LOPT_ERR_INVALID_ARGUMENT, at + "rows and cols must be >= 1");
     if (t.rows > INT32_MAX || t.cols > INT32_MAX || t.rows * t.cols >= (int64_t(1) << 31))
       fail(LOPT_ERR_UNSUPPORTED, at + "tensors must have fewer than 2^31 elements");
+    if (t.rows > 1 && t.cols >= (int64_t(1) << 28))
+      fail(LOPT_ERR_UNSUPPORTED, at + "matrices must have fewer than 2^28 columns");
     if ((reinterpret_cast<uintptr_t>(t.param) | reinterpret_cast<uintptr_t>(t.grad) |
          reinterpret_cast<uintptr_t>(t.state)) & 3u)
       fail(LOPT_ERR_UNSUPPORTED, at + "pointers must be 4-byte aligned");
@@ -227,9 +229,9 @@ Plan build_plan(const lopt_tensor* ts, int32_t n) {
     fl += size_t(d.nrb) * d.C;
     fl = align_up(fl, 4);
     d.off_rq = int64_t(fl);
-    fl += align_up(3 * size_t(d.R), 4);
+    fl += 4 * size_t(d.R);
     d.off_cq = int64_t(fl);
-    fl += d.vec ? 0 : align_up(3 * size_t(d.C), 4);
+    fl += d.vec ? 0 : 4 * size_t(d.C);
 
     // moving-average segments
     d.rseg0 = rseg;
@@ -248,7 +250,8 @@ Plan build_plan(const lopt_tensor* ts, int32_t n) {
     // statistics / apply chunks
     d.chunk0 = int32_t(pl.chunks.size());
     for (uint64_t e = 0; e < d.n; e += kChunkElems)
-      pl.chunks.push_back(Chunk{ti, uint32_t(e), uint32_t(std::min<uint64_t>(e + kChunkElems, d.n)), 0});
+      pl.chunks.push_back(Chunk{ti, uint32_t(e), uint32_t(std::min<uint64_t>(e + kChunkElems, d.n)),
+                                uint32_t(e / uint64_t(d.C))});
     d.nchunk = int32_t(pl.chunks.size()) - d.chunk0;
   }
   pl.n_rseg = rseg;
@@ -326,8 +329,11 @@ StepParams make_params(const lopt_handle* h, int64_t t) {
   for (int a = 0; a < 3; ++a) {
     p.beta_m[a] = c.beta_m[a];
     p.beta_f[a] = c.beta_f[a];
+    p.omb_m[a] = 1.0f - c.beta_m[a];
+    p.omb_f[a] = 1.0f - c.beta_f[a];
   }
   p.beta_v = c.beta_v;
+  p.omb_v = 1.0f - c.beta_v;
   p.eps_v = c.eps_v;
   p.eps_f = c.eps_f;
   p.eps_norm = c.eps_norm;
@@ -335,6 +341,9 @@ StepParams make_params(const lopt_handle* h, int64_t t) {
   p.step_mult = c.step_mult;
   p.lr = c.lr;
   p.weight_decay = c.weight_decay;
+  p.decay = 1.0f - c.lr * c.weight_decay;
+  p.lr_step = c.lr * c.step_mult;
+  p.exp2_mult = float(double(c.exp_mult) * 1.4426950408889634);  // log2(e)
   p.t = float(t);
   p.n_time = c.n_time;
   for (int q = 0; q < kMaxTime; ++q) p.timescales[q] = q < c.n_time ? c.timescales[q] : 1.f;

@@ -17,14 +17,13 @@ namespace lopt {
 // takes its weight from a scalar register.
 template <bool VEC>
 __device__ __forceinline__ void apply_valu_body(const StepCtx& c, const StepParams& hp, const Chunk& ch,
-                                                const TensorDesc& d) {
-  const float* __restrict__ g = c.grads[ch.tensor];
+                                                const TensorDesc& d, const float* g) {
+  const Streams s = make_streams(d, g, c.ws, ch);
   const float* __restrict__ pk = c.packed;
   const float* __restrict__ sc = c.scales + size_t(ch.tensor) * kStatStride;
-  const size_t n = d.n;
   for (uint32_t e = ch.e0 + threadIdx.x; e < ch.e1; e += kBlock) {
     Elem x;
-    load_elem<VEC>(d, g, c.ws, e, x);
+    load_elem<VEC>(s, e, x);
     const float p_old = x.p;
     float F[kNF], cn[3];
     build_features<VEC>(hp, x, F, cn);
@@ -48,26 +47,17 @@ __device__ __forceinline__ void apply_valu_body(const StepCtx& c, const StepPara
       dir = fmaf(pk[kPkW3 + o], a, dir);
       mag = fmaf(pk[kPkW3 + kH + o], a, mag);
     }
-    const float u = dir * expf(mag * hp.exp_mult) * hp.step_mult;
-    d.p[e] = p_old - hp.lr * fmaf(hp.weight_decay, p_old, u);
-    float* st = d.st;
-    st[e] = x.m[0];
-    st[n + e] = x.m[1];
-    st[2 * n + e] = x.m[2];
-    st[3 * n + e] = x.v;
-    if (VEC) {
-      float* cs = st + 4 * n + 3;
-#pragma unroll
-      for (int k = 0; k < 3; ++k) cs[k * n + e] = cn[k];
-    }
+    store_elem<VEC>(s, e, fmaf(-hp.lr_step, dir * __builtin_amdgcn_exp2f(mag * hp.exp2_mult), p_old * hp.decay), x, cn);
   }
 }
 
 __global__ __launch_bounds__(kBlock) void k_apply_valu(StepCtx c, StepParams hp) {
-  const Chunk ch = c.chunks[blockIdx.x];
-  const TensorDesc d = c.desc[ch.tensor];
-  if (d.vec) apply_valu_body<true>(c, hp, ch, d);
-  else apply_valu_body<false>(c, hp, ch, d);
+  Chunk ch;
+  TensorDesc d;
+  const float* g;
+  load_chunk(c, blockIdx.x, ch, d, g);
+  if (d.vec) apply_valu_body<true>(c, hp, ch, d, g);
+  else apply_valu_body<false>(c, hp, ch, d, g);
 }
 
 // ---------------------------------------------------------------------------
@@ -102,12 +92,12 @@ __device__ __forceinline__ void swap_halves(float x, float y, float& lo, float& 
 
 template <bool VEC>
 __device__ __forceinline__ void apply_mfma_body(const StepCtx& c, const StepParams& hp, const Chunk& ch,
-                                                const TensorDesc& d) {
+                                                const TensorDesc& d, const float* g) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform loop control
   const int half = lane >> 5;
   const int row = lane & 31;
-  const float* __restrict__ g = c.grads[ch.tensor];
+  const Streams s = make_streams(d, g, c.ws, ch);
   const float* __restrict__ pk = c.packed;
   const float* __restrict__ sc = c.scales + size_t(ch.tensor) * kStatStride;
 
@@ -117,6 +107,7 @@ __device__ __forceinline__ void apply_mfma_body(const StepCtx& c, const StepPara
   for (int q = 0; q < kNF / 2; ++q) a1[q] = pk[kPkW1 + row * kNF + 2 * q + half] * sc[2 * q + half];
 #pragma unroll
   for (int q = 0; q < 16; ++q) a2[q] = pk[kPkW2 + row * kH + acc_row(q, half)];
+
   // Biases and W3 in accumulator-row order per lane half; read with
   // ds_read_b128 when needed instead of holding 64 registers.
   __shared__ float4 tab[4][2][4];   // {b1, b2, W3 dir, W3 mag} x half x 16 floats
@@ -129,25 +120,13 @@ __device__ __forceinline__ void apply_mfma_body(const StepCtx& c, const StepPara
   }
   __syncthreads();
   const float b3d = pk[kPkB3], b3m = pk[kPkB3 + 1];
-  const size_t n = d.n;
-
   uint32_t base = ch.e0 + wave * 64;
   if (base >= ch.e1) return;  // this wave has no elements in the chunk
-  // Inputs are prefetched one iteration ahead so their latency overlaps the
-  // matrix-core chains of the current iteration.
-  Elem xn;
-  {
-    const uint32_t e = base + lane;
-    load_elem<VEC>(d, g, c.ws, e < ch.e1 ? e : ch.e0, xn);
-  }
   for (; base < ch.e1; base += kBlock) {
     const uint32_t e = base + lane;
     const bool valid = e < ch.e1;
-    Elem x = xn;
-    if (base + kBlock < ch.e1) {
-      const uint32_t en = base + kBlock + lane;
-      load_elem<VEC>(d, g, c.ws, en < ch.e1 ? en : ch.e0, xn);
-    }
+    Elem x;
+    load_elem<VEC>(s, valid ? e : ch.e0, x);
     const float p_old = x.p;
     float F[kNF], cn[3];
     build_features<VEC>(hp, x, F, cn);
@@ -163,8 +142,9 @@ __device__ __forceinline__ void apply_mfma_body(const StepCtx& c, const StepPara
     for (int q = 0; q < kNF / 2; ++q) {
       float bA, bB;
       swap_halves(F[2 * q], F[2 * q + 1], bA, bB);
-      accA = __builtin_amdgcn_mfma_f32_32x32x2f32(a1[q], bA, accA, 0, 0, 0);
-      accB = __builtin_amdgcn_mfma_f32_32x32x2f32(a1[q], bB, accB, 0, 0, 0);
+      const float aq = a1[q];
+      accA = __builtin_amdgcn_mfma_f32_32x32x2f32(aq, bA, accA, 0, 0, 0);
+      accB = __builtin_amdgcn_mfma_f32_32x32x2f32(aq, bB, accB, 0, 0, 0);
     }
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
@@ -179,8 +159,9 @@ __device__ __forceinline__ void apply_mfma_body(const StepCtx& c, const StepPara
     f32x16 acc2A = bias2, acc2B = bias2;
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-      acc2A = __builtin_amdgcn_mfma_f32_32x32x2f32(a2[q], accA[q], acc2A, 0, 0, 0);
-      acc2B = __builtin_amdgcn_mfma_f32_32x32x2f32(a2[q], accB[q], acc2B, 0, 0, 0);
+      const float aq = a2[q];
+      acc2A = __builtin_amdgcn_mfma_f32_32x32x2f32(aq, accA[q], acc2A, 0, 0, 0);
+      acc2B = __builtin_amdgcn_mfma_f32_32x32x2f32(aq, accB[q], acc2B, 0, 0, 0);
     }
     float dA = 0.f, mA = 0.f, dB = 0.f, mB = 0.f;
     float w3d[16], w3m[16];
@@ -206,29 +187,18 @@ __device__ __forceinline__ void apply_mfma_body(const StepCtx& c, const StepPara
     const float dir = (d0 + d1) + b3d;
     const float mag = (m0 + m1) + b3m;
     if (valid) {
-      const float u = dir * expf(mag * hp.exp_mult) * hp.step_mult;
-      gptr(d.p)[e] = p_old - hp.lr * fmaf(hp.weight_decay, p_old, u);
-      gfloat* st = gptr(d.st);
-      st[e] = x.m[0];
-      st[n + e] = x.m[1];
-      st[2 * n + e] = x.m[2];
-      st[3 * n + e] = x.v;
-      if (VEC) {
-        gfloat* cs = st + 4 * n + 3;
-#pragma unroll
-        for (int k = 0; k < 3; ++k) cs[k * n + e] = cn[k];
-      }
+      store_elem<VEC>(s, e, fmaf(-hp.lr_step, dir * __builtin_amdgcn_exp2f(mag * hp.exp2_mult), p_old * hp.decay), x, cn);
     }
   }
 }
 
-// Three waves per SIMD (<= 168 VGPRs): while one wave streams its inputs or
-// runs the feature / layer-3 vector code, another keeps the matrix core busy.
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void k_apply_mfma(StepCtx c, StepParams hp) {
-  const Chunk ch = c.chunks[blockIdx.x];
-  const TensorDesc d = c.desc[ch.tensor];
-  if (d.vec) apply_mfma_body<true>(c, hp, ch, d);
-  else apply_mfma_body<false>(c, hp, ch, d);
+  Chunk ch;
+  TensorDesc d;
+  const float* g;
+  load_chunk(c, blockIdx.x, ch, d, g);
+  if (d.vec) apply_mfma_body<true>(c, hp, ch, d, g);
+  else apply_mfma_body<false>(c, hp, ch, d, g);
 }
 
 hipError_t launch_apply(const StepCtx& c, const StepParams& p, hipStream_t s) {

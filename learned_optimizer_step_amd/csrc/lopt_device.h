@@ -40,6 +40,108 @@ typedef __attribute__((address_space(1))) float gfloat;
 __device__ __forceinline__ const gfloat* gptr(const float* p) { return (const gfloat*)p; }
 __device__ __forceinline__ gfloat* gptr(float* p) { return (gfloat*)p; }
 
+// Wave-uniform copies (scalar registers) of values loaded from the work lists.
+// The compiler reads the lists with vector loads (it cannot prove that the
+// kernel's own stores leave them untouched); readfirstlane keeps the result
+// in scalar registers instead of per-lane copies.
+__device__ __forceinline__ uint32_t uni(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int32_t uni(int32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+template <class T>
+__device__ __forceinline__ T* uni(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
+  return reinterpret_cast<T*>((uint64_t(hi) << 32) | lo);
+}
+__device__ __forceinline__ int64_t uni(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(x));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(x) >> 32));
+  return int64_t((uint64_t(hi) << 32) | lo);
+}
+
+// The chunk record, its tensor's descriptor and gradient pointer, as
+// wave-uniform values.
+__device__ __forceinline__ void load_chunk(const StepCtx& c, uint32_t idx, Chunk& ch, TensorDesc& d,
+                                           const float*& g) {
+  const Chunk cr = c.chunks[idx];
+  ch.tensor = uni(cr.tensor);
+  ch.e0 = uni(cr.e0);
+  ch.e1 = uni(cr.e1);
+  ch.row0 = uni(cr.row0);
+  const TensorDesc dr = c.desc[ch.tensor];
+  d.p = uni(dr.p);
+  d.st = uni(dr.st);
+  d.R = uni(dr.R);
+  d.C = uni(dr.C);
+  d.n = uni(dr.n);
+  d.cmagic = uni(dr.cmagic);
+  d.cshift = uni(dr.cshift);
+  d.vec = uni(dr.vec);
+  d.ncw = uni(dr.ncw);
+  d.nrb = uni(dr.nrb);
+  d.rseg0 = uni(dr.rseg0);
+  d.nrseg = uni(dr.nrseg);
+  d.chunk0 = uni(dr.chunk0);
+  d.nchunk = uni(dr.nchunk);
+  d.off_rowpart = uni(dr.off_rowpart);
+  d.off_colpart = uni(dr.off_colpart);
+  d.off_rq = uni(dr.off_rq);
+  d.off_cq = uni(dr.off_cq);
+  g = uni(c.grads[ch.tensor]);
+}
+
+// Uniform base pointers of one chunk's per-element streams and of its
+// row/column vectors.  Every stream is rebased at the chunk's first element
+// (and the row vectors at its first row), so a lane's access is a uniform
+// 64-bit base plus a small 32-bit byte offset (global_load v, voff, s[base]).
+struct Streams {
+  const gfloat* g;
+  gfloat* p;
+  gfloat* m[3];
+  gfloat* v;
+  gfloat* c[3];          // 1-D tensors: per-element c_k
+  const gfloat* rq;      // [row][4] r_k^(-1/2) from the chunk's first row (1-D: one record)
+  const gfloat* cq;      // [col][4] c_k^(-1/2) (2-D)
+  uint32_t e0, i0, C, cmagic, cshift;
+};
+
+__device__ __forceinline__ Streams make_streams(const TensorDesc& d, const float* g, const float* ws,
+                                                const Chunk& ch) {
+  Streams s;
+  const size_t n = d.n;
+  const uint32_t e0 = ch.e0;
+  gfloat* st = (gfloat*)d.st;
+  s.e0 = e0;
+  s.i0 = ch.row0;
+  s.g = gptr(g) + e0;
+  s.p = gptr(d.p) + e0;
+#pragma unroll
+  for (int a = 0; a < 3; ++a) s.m[a] = st + a * n + e0;
+  s.v = st + 3 * n + e0;
+#pragma unroll
+  for (int k = 0; k < 3; ++k) s.c[k] = st + 4 * n + 3 + k * n + e0;   // 1-D tensors only (R = 1)
+  s.rq = gptr(ws) + d.off_rq + 4 * size_t(d.vec ? 0 : s.i0);
+  s.cq = gptr(ws) + d.off_cq;
+  s.C = uint32_t(d.C);
+  s.cmagic = d.cmagic;
+  s.cshift = d.cshift;
+  return s;
+}
+
+// base[byte_off / 4] with a 32-bit byte offset.
+typedef __attribute__((address_space(1))) char gchar;
+__device__ __forceinline__ float ldb(const gfloat* base, uint32_t byte_off) {
+  return *(const gfloat*)((const gchar*)base + byte_off);
+}
+__device__ __forceinline__ void stb(gfloat* base, uint32_t byte_off, float v) {
+  *(gfloat*)((gchar*)base + byte_off) = v;
+}
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) f32x4 gf32x4;
+__device__ __forceinline__ f32x4 ldb4(const gfloat* base, uint32_t byte_off) {
+  return *(const gf32x4*)((const gchar*)base + byte_off);
+}
+
 // Per-element inputs of the feature construction.
 struct Elem {
   float g, p, m[3], v;
@@ -59,13 +161,13 @@ __device__ __forceinline__ void build_features(const StepParams& hp, Elem& x, fl
   const float g = x.g;
   const float g2 = g * g;
 #pragma unroll
-  for (int a = 0; a < 3; ++a) x.m[a] = fmaf(hp.beta_m[a], x.m[a], (1.0f - hp.beta_m[a]) * g);
-  x.v = fmaf(hp.beta_v, x.v, (1.0f - hp.beta_v) * g2);
+  for (int a = 0; a < 3; ++a) x.m[a] = fmaf(hp.beta_m[a], x.m[a], hp.omb_m[a] * g);
+  x.v = fmaf(hp.beta_v, x.v, hp.omb_v * g2);
   float cq[3], rho[3];
 #pragma unroll
   for (int k = 0; k < 3; ++k) {
     if (VEC) {
-      cn[k] = fmaf(hp.beta_f[k], x.cq[k], (1.0f - hp.beta_f[k]) * (g2 + hp.eps_f));
+      cn[k] = fmaf(hp.beta_f[k], x.cq[k], hp.omb_f[k] * (g2 + hp.eps_f));
       cq[k] = rsqrtf(cn[k]);
       rho[k] = cq[k];
     } else {
@@ -93,34 +195,45 @@ __device__ __forceinline__ void build_features(const StepParams& hp, Elem& x, fl
 }
 
 // Loads the inputs of element e of tensor d.
+// Loads the inputs of element e of the chunk.  All byte offsets fit in 32
+// bits: a chunk spans at most kChunkElems elements (and rows), and the host
+// rejects 2-D tensors with 2^28 or more columns (16-byte column records).
 template <bool VEC>
-__device__ __forceinline__ void load_elem(const TensorDesc& d, const float* __restrict__ g_,
-                                          const float* __restrict__ ws_, uint32_t e, Elem& x) {
-  const size_t n = d.n;
-  const gfloat* st = gptr(d.st);
-  const gfloat* g = gptr(g_);
-  const gfloat* ws = gptr(ws_);
-  x.g = g[e];
-  x.p = gptr(d.p)[e];
-  x.m[0] = st[e];
-  x.m[1] = st[n + e];
-  x.m[2] = st[2 * n + e];
-  x.v = st[3 * n + e];
+__device__ __forceinline__ void load_elem(const Streams& s, uint32_t e, Elem& x) {
+  const uint32_t off = (e - s.e0) * 4u;
+  x.g = ldb(s.g, off);
+  x.p = ldb(s.p, off);
+#pragma unroll
+  for (int a = 0; a < 3; ++a) x.m[a] = ldb(s.m[a], off);
+  x.v = ldb(s.v, off);
   if (VEC) {
-    const gfloat* c = st + 4 * n + 3;  // R = 1
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
-      x.cq[k] = c[k * n + e];
-      x.rq[k] = ws[d.off_rq + k];
+      x.cq[k] = ldb(s.c[k], off);
+      x.rq[k] = s.rq[k];
     }
   } else {
-    const uint32_t i = div_c(e, d.cmagic, d.cshift);
-    const uint32_t j = e - i * uint32_t(d.C);
+    const uint32_t i = div_c(e, s.cmagic, s.cshift);
+    const uint32_t j = e - i * s.C;
+    const f32x4 r4 = ldb4(s.rq, (i - s.i0) * 16u);
+    const f32x4 c4 = ldb4(s.cq, j * 16u);
+    x.rq[0] = r4.x; x.rq[1] = r4.y; x.rq[2] = r4.z;
+    x.cq[0] = c4.x; x.cq[1] = c4.y; x.cq[2] = c4.z;
+  }
+}
+
+// Stores the updated parameter and per-element accumulators of element e.
+template <bool VEC>
+__device__ __forceinline__ void store_elem(const Streams& s, uint32_t e, float p_new, const Elem& x,
+                                           const float cn[3]) {
+  const uint32_t off = (e - s.e0) * 4u;
+  stb(s.p, off, p_new);
 #pragma unroll
-    for (int k = 0; k < 3; ++k) {
-      x.rq[k] = ws[d.off_rq + size_t(k) * d.R + i];
-      x.cq[k] = ws[d.off_cq + size_t(k) * d.C + j];
-    }
+  for (int a = 0; a < 3; ++a) stb(s.m[a], off, x.m[a]);
+  stb(s.v, off, x.v);
+  if (VEC) {
+#pragma unroll
+    for (int k = 0; k < 3; ++k) stb(s.c[k], off, cn[k]);
   }
 }
 

@@ -47,8 +47,8 @@ struct TensorDesc {
   int32_t chunk0, nchunk;    // statistics / apply chunks
   int64_t off_rowpart;       // floats: [ncw][R]
   int64_t off_colpart;       // floats: [nrb][C]       (2-D only)
-  int64_t off_rq;            // floats: [3][R]  r_k^(-1/2)
-  int64_t off_cq;            // floats: [3][C]  c_k^(-1/2) (2-D only)
+  int64_t off_rq;            // floats: [R][4]  (r_1, r_2, r_3)^(-1/2), 4th unused
+  int64_t off_cq;            // floats: [C][4]  (c_1, c_2, c_3)^(-1/2) (2-D only)
 };
 
 // Row/column sum-of-squares tile.
@@ -73,11 +73,11 @@ struct Seg1 {
   int32_t pad[3];
 };
 
-// Statistics / apply chunk: elements [e0, e1) of one tensor.
+// Statistics / apply chunk: elements [e0, e1) of one tensor; row0 = e0 / cols.
 struct Chunk {
   int32_t tensor;
   uint32_t e0, e1;
-  int32_t pad;
+  uint32_t row0;
 };
 
 // Hyperparameters as the kernels see them.
@@ -85,8 +85,14 @@ struct StepParams {
   float beta_m[3];
   float beta_v;
   float beta_f[3];
+  float omb_m[3], omb_v, omb_f[3];   // 1 - beta, rounded to fp32 once on the host
   float eps_v, eps_f, eps_norm;
   float exp_mult, step_mult, lr, weight_decay;
+  // Update constants folded once on the host:
+  //   p <- p * decay - lr_step * dir * exp2(mag * exp2_mult)
+  float decay;               // 1 - lr * weight_decay
+  float lr_step;             // lr * step_mult
+  float exp2_mult;           // exp_mult * log2(e)
   float t;                   // 1-based step index of this step
   int32_t n_time;
   float timescales[kMaxTime];

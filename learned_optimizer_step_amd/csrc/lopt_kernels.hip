@@ -44,15 +44,17 @@ __global__ __launch_bounds__(kBlock) void k_rowcol_sumsq(StepCtx c) {
   __shared__ float red[4];
 
   if (tl.flat) {
-    float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     uint32_t e = tl.c0 + tid;
-    for (; e + 3 * kBlock < uint32_t(tl.c1); e += 4 * kBlock) {
-      const float a = g[e], b = g[e + kBlock], cc = g[e + 2 * kBlock], dd = g[e + 3 * kBlock];
-      acc0 = fmaf(a, a, acc0); acc1 = fmaf(b, b, acc1);
-      acc2 = fmaf(cc, cc, acc2); acc3 = fmaf(dd, dd, acc3);
+    for (; e + 7 * kBlock < uint32_t(tl.c1); e += 8 * kBlock) {
+      float x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = g[e + u * kBlock];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc[u] = fmaf(x[u], x[u], acc[u]);
     }
-    for (; e < uint32_t(tl.c1); e += kBlock) { const float a = g[e]; acc0 = fmaf(a, a, acc0); }
-    const float s = block_sum((acc0 + acc1) + (acc2 + acc3), red);
+    for (; e < uint32_t(tl.c1); e += kBlock) { const float a = g[e]; acc[0] = fmaf(a, a, acc[0]); }
+    const float s = block_sum(((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7])), red);
     if (tid == 0) ws[d.off_rowpart + tl.win] = s;
     return;
   }
@@ -68,15 +70,16 @@ __global__ __launch_bounds__(kBlock) void k_rowcol_sumsq(StepCtx c) {
   const int iters = (tl.r1 - tl.r0 + RS - 1) / RS;
   const int wave = tid >> 6;
   float colacc = 0.f;
-  for (int q0 = 0; q0 < iters; q0 += 4) {
-    float x[4];
+  constexpr int kRowBatch = 16;  // rows loaded per thread before reducing (bytes in flight)
+  for (int q0 = 0; q0 < iters; q0 += kRowBatch) {
+    float x[kRowBatch];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kRowBatch; ++u) {
       const int i = tl.r0 + slot + RS * (q0 + u);
       x[u] = (colok && q0 + u < iters && i < tl.r1) ? g[size_t(i) * C + j] : 0.f;
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kRowBatch; ++u) {
       const int q = q0 + u;
       if (q >= iters) break;  // uniform across the block
       const int i = tl.r0 + slot + RS * q;
@@ -133,13 +136,15 @@ __global__ __launch_bounds__(kBlock) void k_moving_avg(StepCtx c, StepParams hp)
       float s = 0.f;
       for (int w = 0; w < d.ncw; ++w) s += ws[d.off_rowpart + size_t(w) * d.R + i];
       const float mean = s / float(d.C);
+      float q[3];
 #pragma unroll
       for (int k = 0; k < 3; ++k) {
-        const float rk = fmaf(hp.beta_f[k], r[size_t(k) * d.R + i], (1.0f - hp.beta_f[k]) * (mean + hp.eps_f));
+        const float rk = fmaf(hp.beta_f[k], r[size_t(k) * d.R + i], hp.omb_f[k] * (mean + hp.eps_f));
         r[size_t(k) * d.R + i] = rk;
-        ws[d.off_rq + size_t(k) * d.R + i] = rsqrtf(rk);
+        q[k] = rsqrtf(rk);
         loc[k] = rk;
       }
+      reinterpret_cast<float4*>(ws + d.off_rq)[i] = make_float4(q[0], q[1], q[2], 0.f);
     }
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
@@ -152,12 +157,14 @@ __global__ __launch_bounds__(kBlock) void k_moving_avg(StepCtx c, StepParams hp)
       float s = 0.f;
       for (int b = 0; b < d.nrb; ++b) s += ws[d.off_colpart + size_t(b) * d.C + j];
       const float mean = s / float(d.R);
+      float q[3];
 #pragma unroll
       for (int k = 0; k < 3; ++k) {
-        const float ck = fmaf(hp.beta_f[k], cst[size_t(k) * d.C + j], (1.0f - hp.beta_f[k]) * (mean + hp.eps_f));
+        const float ck = fmaf(hp.beta_f[k], cst[size_t(k) * d.C + j], hp.omb_f[k] * (mean + hp.eps_f));
         cst[size_t(k) * d.C + j] = ck;
-        ws[d.off_cq + size_t(k) * d.C + j] = rsqrtf(ck);
+        q[k] = rsqrtf(ck);
       }
+      reinterpret_cast<float4*>(ws + d.off_cq)[j] = make_float4(q[0], q[1], q[2], 0.f);
     }
   } else {  // 1-D tensor: r_k is one value per tensor
     float s = 0.f;
@@ -167,7 +174,7 @@ __global__ __launch_bounds__(kBlock) void k_moving_avg(StepCtx c, StepParams hp)
       const float mean = s / float(d.C);
 #pragma unroll
       for (int k = 0; k < 3; ++k) {
-        const float rk = fmaf(hp.beta_f[k], r[k], (1.0f - hp.beta_f[k]) * (mean + hp.eps_f));
+        const float rk = fmaf(hp.beta_f[k], r[k], hp.omb_f[k] * (mean + hp.eps_f));
         r[k] = rk;
         ws[d.off_rq + k] = rsqrtf(rk);
         c.rbar_part[sg.slot * 4 + k] = rk;
@@ -181,28 +188,45 @@ __global__ __launch_bounds__(kBlock) void k_moving_avg(StepCtx c, StepParams hp)
 // kernel 1).  Accumulators are updated in registers only; the apply kernel
 // recomputes them from the same inputs.
 template <bool VEC>
-__device__ __forceinline__ void stats_body(const StepCtx& c, const StepParams& hp, const Chunk& ch,
-                                           const TensorDesc& d, float acc[kNF]) {
-  const float* __restrict__ g = c.grads[ch.tensor];
-  for (uint32_t e = ch.e0 + threadIdx.x; e < ch.e1; e += kBlock) {
-    Elem x;
-    load_elem<VEC>(d, g, c.ws, e, x);
-    float F[kNF], cn[3];
-    build_features<VEC>(hp, x, F, cn);
+__device__ __forceinline__ void stats_accumulate(const StepParams& hp, Elem& x, float acc[kNF]) {
+  float F[kNF], cn[3];
+  build_features<VEC>(hp, x, F, cn);
 #pragma unroll
-    for (int f = 0; f < kNF; ++f) acc[f] = fmaf(F[f], F[f], acc[f]);
+  for (int f = 0; f < kNF; ++f) acc[f] = fmaf(F[f], F[f], acc[f]);
+}
+
+// Four elements per thread per iteration, their loads issued together, so
+// each thread keeps ~100 bytes of HBM reads in flight.
+template <bool VEC>
+__device__ __forceinline__ void stats_body(const StepCtx& c, const StepParams& hp, const Chunk& ch,
+                                           const TensorDesc& d, const float* g, float acc[kNF]) {
+  const Streams st = make_streams(d, g, c.ws, ch);
+  uint32_t e = ch.e0 + threadIdx.x;
+  for (; e + 3 * kBlock < ch.e1; e += 4 * kBlock) {
+    Elem x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) load_elem<VEC>(st, e + u * kBlock, x[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) stats_accumulate<VEC>(hp, x[u], acc);
+  }
+  for (; e < ch.e1; e += kBlock) {
+    Elem x;
+    load_elem<VEC>(st, e, x);
+    stats_accumulate<VEC>(hp, x, acc);
   }
 }
 
 __global__ __launch_bounds__(kBlock) void k_stats(StepCtx c, StepParams hp) {
-  const Chunk ch = c.chunks[blockIdx.x];
-  const TensorDesc d = c.desc[ch.tensor];
+  Chunk ch;
+  TensorDesc d;
+  const float* g;
+  load_chunk(c, blockIdx.x, ch, d, g);
   __shared__ float lds[4][kNF];
   float acc[kNF];
 #pragma unroll
   for (int f = 0; f < kNF; ++f) acc[f] = 0.f;
-  if (d.vec) stats_body<true>(c, hp, ch, d, acc);
-  else stats_body<false>(c, hp, ch, d, acc);
+  if (d.vec) stats_body<true>(c, hp, ch, d, g, acc);
+  else stats_body<false>(c, hp, ch, d, g, acc);
   const int w = threadIdx.x >> 6;
 #pragma unroll
   for (int f = 0; f < kNF; ++f) {

@@ -97,6 +97,7 @@ def test_workspace_bytes_accepts_null_grads(lib):
     (lambda t: setattr(t, "state", None), L.LOPT_ERR_INVALID_ARGUMENT),
     (lambda t: setattr(t, "param", t.param + 2), L.LOPT_ERR_UNSUPPORTED),
     (lambda t: (setattr(t, "rows", 1 << 16), setattr(t, "cols", 1 << 15)), L.LOPT_ERR_UNSUPPORTED),
+    (lambda t: (setattr(t, "rows", 2), setattr(t, "cols", 1 << 28)), L.LOPT_ERR_UNSUPPORTED),
     (lambda t: setattr(t, "grad", t.param), L.LOPT_ERR_INVALID_ARGUMENT),
     (lambda t: setattr(t, "grad", t.state + 64), L.LOPT_ERR_INVALID_ARGUMENT),
     (lambda t: setattr(t, "state", t.param + 4), L.LOPT_ERR_INVALID_ARGUMENT),
