@@ -32,6 +32,37 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+# Sources of the apply kernel; the committed HBM-traffic figure is only valid
+# for the exact sources it was measured on.
+APPLY_SOURCES = ("learned_optimizer_step_amd/csrc/lopt_apply.hip", "learned_optimizer_step_amd/csrc/lopt_device.h",
+                 "learned_optimizer_step_amd/csrc/lopt_internal.h")
+
+
+def apply_sources_sha() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for p in APPLY_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(workload: str, kernel: str = "k_apply_mfma"):
+    """HBM bytes per launch of ``kernel`` from the rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary in profiles/, or None when absent or measured on other sources."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        for line in f:
+            if not line.startswith("bench-traffic:"):
+                continue
+            kv = dict(x.split("=", 1) for x in line.split()[1:])
+            if kv.get("kernel") == kernel and kv.get("workload") == workload:
+                return int(kv["bytes"]) if kv.get("sources_sha256") == apply_sources_sha() else None
+    return None
+
+
 def cpu_baseline(blocks: int = 5):
     """The oracle on the first ``blocks`` ViT-B/16 transformer blocks, one step, on host cores."""
     import numpy as np
@@ -154,7 +185,8 @@ def main():
                    "mlp_impl": "mfma" if use_mfma else "valu", "state": "zero-init, gradients fixed"},
         "roofline": {"bound": "mfma" if use_mfma else "alu", "kernel": "k_apply",
                      "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "frac": round(achieved / peak, 4),
+                     "traffic": committed_traffic(w.key) if use_mfma else None,
                      "flop_per_elem": FLOP_PER_ELEM, "elems_per_launch": n},
         "step_frac_fp32_peak": round(FLOP_PER_ELEM * n / (ms * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4),
         "kernels_ms": {name: round(float(t), 4) for name, t in zip(L.KERNEL_NAMES, kern_ms)},
