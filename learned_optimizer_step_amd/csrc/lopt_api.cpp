@@ -74,6 +74,7 @@ struct Plan {
   std::vector<Seg1> segs1;
   std::vector<Chunk> chunks;
   int32_t n_rseg = 0;
+  uint32_t chunk_elems = 0;
   // byte offsets inside the workspace
   size_t off_desc = 0, off_grads = 0, off_tiles0 = 0, off_segs1 = 0, off_chunks = 0;
   size_t off_rbar = 0, off_stats = 0, off_scales = 0, off_packed = 0, off_floats = 0;
@@ -163,6 +164,11 @@ Plan build_plan(const lopt_tensor* ts, int32_t n) {
   pl.grads.resize(n);
   size_t fl = 0;  // floats of per-tensor arrays
   int32_t rseg = 0;
+  uint64_t total = 0;
+  for (int32_t ti = 0; ti < n; ++ti) total += uint64_t(ts[ti].rows * ts[ti].cols);
+  const uint64_t chunk = std::min<uint64_t>(
+      kChunkElems, std::max<uint64_t>(kMinChunkElems, align_up((total + kTargetChunks - 1) / kTargetChunks, 256)));
+  pl.chunk_elems = uint32_t(chunk);
   for (int32_t ti = 0; ti < n; ++ti) {
     const lopt_tensor& t = ts[ti];
     TensorDesc& d = pl.desc[ti];
@@ -249,8 +255,8 @@ Plan build_plan(const lopt_tensor* ts, int32_t n) {
 
     // statistics / apply chunks
     d.chunk0 = int32_t(pl.chunks.size());
-    for (uint64_t e = 0; e < d.n; e += kChunkElems)
-      pl.chunks.push_back(Chunk{ti, uint32_t(e), uint32_t(std::min<uint64_t>(e + kChunkElems, d.n)),
+    for (uint64_t e = 0; e < d.n; e += chunk)
+      pl.chunks.push_back(Chunk{ti, uint32_t(e), uint32_t(std::min<uint64_t>(e + chunk, d.n)),
                                 uint32_t(e / uint64_t(d.C))});
     d.nchunk = int32_t(pl.chunks.size()) - d.chunk0;
   }

@@ -19,7 +19,13 @@ constexpr int kStatStride = 32;    // floats per stats partial / per-tensor scal
 constexpr int kTile0Elems = 16384;   // elements per row/column-sum tile
 constexpr int kTile0Iters = 64;      // row iterations per 2-D tile (bounds the LDS buffer)
 constexpr int kSeg1 = 256;           // rows or columns per moving-average segment
-constexpr int kChunkElems = 16384;   // elements per statistics / apply chunk
+// Statistics / apply chunks: the plan picks one chunk size for the whole
+// tensor list, aiming at kTargetChunks chunks (several rounds of the ~768
+// workgroups the apply kernel keeps resident, so the last round is nearly
+// full), between kMinChunkElems and kChunkElems elements, a multiple of 256.
+constexpr int kChunkElems = 16384;
+constexpr int kMinChunkElems = 256;
+constexpr int kTargetChunks = 4096;
 
 // Packed MLP in the workspace, written once per step by the finalize kernel:
 // W1 feature columns [32][28], b1 with the step features folded in [32],
