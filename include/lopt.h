@@ -140,20 +140,38 @@ lopt_status lopt_workspace_bytes(const lopt_handle* h, const lopt_tensor* ts, in
 lopt_status lopt_init_state(lopt_handle* h, const lopt_tensor* ts, int32_t n, void* workspace,
                             size_t ws_bytes, void* stream);
 
-/* One optimizer step over the bound tensor list: t <- t + 1, then queues the
- * five kernels of the step on `stream` and returns (asynchronous).  ts must
+/* One optimizer step over the bound tensor list: queues the five kernels of
+ * the step on `stream` and returns (asynchronous); the step's finalize kernel
+ * advances t.  An empty list queues nothing and leaves t unchanged.  ts must
  * list the same tensors (param, state, rows, cols) in the same order as
  * lopt_init_state; grad pointers may differ (the plan's copy is refreshed,
- * which synchronises the stream).  Errors: a different list -> STATE; bad
- * pointers -> INVALID_ARGUMENT; launch failure -> HIP.  On error nothing is
- * queued and t is unchanged.  NaN/Inf in the inputs propagate. */
+ * which synchronises the stream, so it cannot happen while the stream is
+ * being captured into a graph).  Errors: a different list -> STATE; bad
+ * pointers -> INVALID_ARGUMENT; launch failure -> HIP.  On a validation
+ * error nothing is queued.  Non-finite inputs are not checked (they propagate
+ * into the accumulators). */
 lopt_status lopt_step(lopt_handle* h, const lopt_tensor* ts, int32_t n, void* stream);
 
-/* Step counter: the number of steps taken (t of the last step). */
+/* Step counter: the number of steps taken (t of the last step).  The counter
+ * lives in the workspace and the step's finalize kernel advances it, so steps
+ * replayed from a captured HIP graph see t = 1, 2, 3, ...  Waits for the
+ * device (hipDeviceSynchronize); 0 before lopt_init_state. */
 lopt_status lopt_get_step(const lopt_handle* h, int64_t* t);
 
-/* Sets the step counter (to resume from saved state); t >= 0. */
+/* Sets the step counter (to resume from saved state); t >= 0.  Waits for the
+ * device, then writes the counter.  Errors: t < 0 -> INVALID_ARGUMENT; no
+ * bound list -> STATE. */
 lopt_status lopt_set_step(lopt_handle* h, int64_t t);
+
+/* Replaces the hyperparameters for the following lopt_step calls, e.g. a
+ * learning-rate schedule or a new weight decay (the PyLO page, "Library
+ * design" and "Effect of learning-rate schedules and weight decay": the
+ * optimizer composes with torch LR schedulers and decoupled weight decay).
+ * Host-side only: steps already queued keep the values they were launched
+ * with; a step captured in a HIP graph keeps the values of its capture.
+ * Errors: invalid config, or n_time different from lopt_create's ->
+ * INVALID_ARGUMENT (the handle keeps its previous config). */
+lopt_status lopt_set_config(lopt_handle* h, const lopt_config* cfg);
 
 /* Kernels of one step, in launch order. */
 #define LOPT_N_KERNELS 5 /* row/col sums, moving averages, statistics, finalize, apply */

@@ -77,7 +77,7 @@ struct Plan {
   uint32_t chunk_elems = 0;
   // byte offsets inside the workspace
   size_t off_desc = 0, off_grads = 0, off_tiles0 = 0, off_segs1 = 0, off_chunks = 0;
-  size_t off_rbar = 0, off_stats = 0, off_scales = 0, off_packed = 0, off_floats = 0;
+  size_t off_rbar = 0, off_stats = 0, off_scales = 0, off_packed = 0, off_step = 0, off_floats = 0;
   size_t floats = 0;  // per-tensor float arrays (row/col partials, rq, cq)
   size_t total = 0;
   std::vector<lopt_tensor> bound;
@@ -278,6 +278,7 @@ Plan build_plan(const lopt_tensor* ts, int32_t n) {
   pl.off_stats = take(sizeof(float) * kStatStride * pl.chunks.size());
   pl.off_scales = take(sizeof(float) * kStatStride * pl.desc.size());
   pl.off_packed = take(sizeof(float) * kPkFloats);
+  pl.off_step = take(sizeof(int64_t));
   pl.off_floats = take(sizeof(float) * pl.floats);
   pl.total = off;
   // per-tensor float offsets are relative to the workspace base
@@ -301,7 +302,6 @@ struct lopt_handle {
   Plan plan;
   char* ws = nullptr;
   size_t ws_bytes = 0;
-  int64_t t = 0;
   std::vector<hipEvent_t> events;  // optional timing events (kNumKernels + 1)
 };
 
@@ -320,6 +320,7 @@ StepCtx make_ctx(const lopt_handle* h) {
   c.stats_part = reinterpret_cast<float*>(h->ws + pl.off_stats);
   c.scales = reinterpret_cast<float*>(h->ws + pl.off_scales);
   c.packed = reinterpret_cast<float*>(h->ws + pl.off_packed);
+  c.step = reinterpret_cast<int64_t*>(h->ws + pl.off_step);
   c.mlp = h->d_mlp;
   c.n_tensors = int32_t(pl.desc.size());
   c.n_tiles0 = int32_t(pl.tiles0.size());
@@ -329,7 +330,7 @@ StepCtx make_ctx(const lopt_handle* h) {
   return c;
 }
 
-StepParams make_params(const lopt_handle* h, int64_t t) {
+StepParams make_params(const lopt_handle* h) {
   const lopt_config& c = h->cfg;
   StepParams p{};
   for (int a = 0; a < 3; ++a) {
@@ -350,7 +351,6 @@ StepParams make_params(const lopt_handle* h, int64_t t) {
   p.decay = 1.0f - c.lr * c.weight_decay;
   p.lr_step = c.lr * c.step_mult;
   p.exp2_mult = float(double(c.exp_mult) * 1.4426950408889634);  // log2(e)
-  p.t = float(t);
   p.n_time = c.n_time;
   for (int q = 0; q < kMaxTime; ++q) p.timescales[q] = q < c.n_time ? c.timescales[q] : 1.f;
   return p;
@@ -469,12 +469,12 @@ lopt_status lopt_init_state(lopt_handle* h, const lopt_tensor* ts, int32_t n, vo
     upload(ws, pl.off_tiles0, pl.tiles0, s);
     upload(ws, pl.off_segs1, pl.segs1, s);
     upload(ws, pl.off_chunks, pl.chunks, s);
+    upload(ws, pl.off_step, std::vector<int64_t>{0}, s);
     hip_check(hipStreamSynchronize(s), "hipStreamSynchronize(plan upload)");
     h->plan = std::move(pl);
     h->ws = ws;
     h->ws_bytes = ws_bytes;
     h->bound = true;
-    h->t = 0;
     hip_check(launch_zero_state(make_ctx(h), s), "launch(zero state)");
   });
 }
@@ -493,16 +493,20 @@ lopt_status lopt_step(lopt_handle* h, const lopt_tensor* ts, int32_t n, void* st
       upload(h->ws, h->plan.off_grads, h->plan.grads, s);
       hip_check(hipStreamSynchronize(s), "hipStreamSynchronize(grad pointer upload)");
     }
-    const StepParams p = make_params(h, h->t + 1);
+    const StepParams p = make_params(h);
     hip_check(launch_step(make_ctx(h), p, s, h->events.empty() ? nullptr : h->events.data()), "launch(step)");
-    h->t += 1;
   });
 }
 
 lopt_status lopt_get_step(const lopt_handle* h, int64_t* t) {
   return guarded([&] {
     if (!h || !t) fail(LOPT_ERR_INVALID_ARGUMENT, "NULL handle or output");
-    *t = h->t;
+    if (!h->bound) {
+      *t = 0;
+      return;
+    }
+    hip_check(hipDeviceSynchronize(), "hipDeviceSynchronize");
+    hip_check(hipMemcpy(t, h->ws + h->plan.off_step, sizeof(int64_t), hipMemcpyDeviceToHost), "hipMemcpy(step)");
   });
 }
 
@@ -510,7 +514,19 @@ lopt_status lopt_set_step(lopt_handle* h, int64_t t) {
   return guarded([&] {
     if (!h) fail(LOPT_ERR_INVALID_ARGUMENT, "handle is NULL");
     if (t < 0) fail(LOPT_ERR_INVALID_ARGUMENT, "step must be >= 0");
-    h->t = t;
+    if (!h->bound) fail(LOPT_ERR_STATE, "lopt_init_state has not been called");
+    hip_check(hipDeviceSynchronize(), "hipDeviceSynchronize");
+    hip_check(hipMemcpy(h->ws + h->plan.off_step, &t, sizeof(int64_t), hipMemcpyHostToDevice), "hipMemcpy(step)");
+  });
+}
+
+lopt_status lopt_set_config(lopt_handle* h, const lopt_config* cfg) {
+  return guarded([&] {
+    if (!h) fail(LOPT_ERR_INVALID_ARGUMENT, "handle is NULL");
+    validate_config(cfg);
+    if (cfg->n_time != h->cfg.n_time)
+      fail(LOPT_ERR_INVALID_ARGUMENT, "n_time is fixed by the MLP weights given to lopt_create");
+    h->cfg = *cfg;
   });
 }
 

@@ -99,7 +99,6 @@ struct StepParams {
   float decay;               // 1 - lr * weight_decay
   float lr_step;             // lr * step_mult
   float exp2_mult;           // exp_mult * log2(e)
-  float t;                   // 1-based step index of this step
   int32_t n_time;
   float timescales[kMaxTime];
 };
@@ -116,6 +115,7 @@ struct StepCtx {
   float* stats_part;                 // [n_chunks][32]
   float* scales;                     // [n_tensors][32]: s_0..s_27, sqrt(rbar_k) at 28..30
   float* packed;                     // kPkFloats
+  int64_t* step;                     // steps taken; advanced by k_finalize (graph-replay safe)
   const float* mlp;                  // raw weights (handle-owned)
   int32_t n_tensors, n_tiles0, n_segs1, n_chunks;
   int32_t mlp_impl;                  // 1 = VALU, 2 = MFMA

@@ -283,6 +283,11 @@ __global__ __launch_bounds__(kBlock) void k_finalize(StepCtx c, StepParams hp) {
   }
 
   if (t == 0) {
+    // The step counter lives in device memory so that a captured step, replayed
+    // from a graph, still sees t = 1, 2, 3, ...  Every thread reads it, then
+    // thread 0 advances it after the barrier below.
+    const int64_t step = *c.step + 1;
+    const float tf = float(step);
     const int din = kNF + hp.n_time;
     const float* W1 = c.mlp;
     const float* b1 = W1 + kH * din;
@@ -298,7 +303,7 @@ __global__ __launch_bounds__(kBlock) void k_finalize(StepCtx c, StepParams hp) {
     if (threadIdx.x < kH) {
       const int o = threadIdx.x;
       float b = b1[o];
-      for (int s = 0; s < hp.n_time; ++s) b = fmaf(W1[o * din + kNF + s], tanhf(hp.t / hp.timescales[s]), b);
+      for (int s = 0; s < hp.n_time; ++s) b = fmaf(W1[o * din + kNF + s], tanhf(tf / hp.timescales[s]), b);
       pk[kPkB1 + o] = b;
       pk[kPkB2 + o] = b2[o];
       pk[kPkW3 + o] = W3[o];
@@ -306,6 +311,8 @@ __global__ __launch_bounds__(kBlock) void k_finalize(StepCtx c, StepParams hp) {
     }
     for (int q = threadIdx.x; q < kH * kH; q += kBlock) pk[kPkW2 + q] = W2[q];
     if (threadIdx.x < 2) pk[kPkB3 + threadIdx.x] = b3[threadIdx.x];
+    __syncthreads();
+    if (threadIdx.x == 0) *c.step = step;
   }
 }
 

@@ -85,6 +85,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "lopt_get_step": (st, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64)]),
         "lopt_set_step": (st, [ctypes.c_void_p, ctypes.c_int64]),
         "lopt_set_timing_events": (st, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32]),
+        "lopt_set_config": (st, [ctypes.c_void_p, ctypes.POINTER(lopt_config)]),
         "lopt_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -162,6 +163,10 @@ def lopt_get_step(h) -> int:
 
 def lopt_set_step(h, t: int) -> None:
     _check(load_library().lopt_set_step(h, t))
+
+
+def lopt_set_config(h, cfg: lopt_config) -> None:
+    _check(load_library().lopt_set_config(h, ctypes.byref(cfg)))
 
 
 LOPT_N_KERNELS = 5
@@ -264,3 +269,54 @@ class LOpt:
             self.close()
         except Exception:
             pass
+
+
+def _torch_optimizer_base():
+    import torch
+    return torch.optim.Optimizer
+
+
+class LearnedOptimizer(_torch_optimizer_base()):
+    """small_fc_lopt as a ``torch.optim.Optimizer`` over fp32 device parameters.
+
+    Each ``step()`` is one ``lopt_step`` over every parameter, with the
+    gradients in ``p.grad``.  ``lr`` and ``weight_decay`` are read from the
+    (single) parameter group, so ``torch.optim.lr_scheduler`` schedules drive
+    them; a change is passed to the library with ``lopt_set_config``.  The
+    accumulators live in ``self.lopt.states`` (layout of ``include/lopt.h``).
+    """
+
+    def __init__(self, params, mlp: np.ndarray, lr: float = 1.0, weight_decay: float = 0.0,
+                 config: Optional[lopt_config] = None):
+        super().__init__(params, dict(lr=lr, weight_decay=weight_decay))
+        plist = [p for g in self.param_groups for p in g["params"]]
+        cfg = config if config is not None else lopt_default_config()
+        cfg.lr, cfg.weight_decay = lr, weight_decay
+        self.lopt = LOpt(plist, mlp, cfg)
+        self._applied = (float(cfg.lr), float(cfg.weight_decay))
+
+    def _hyper(self):
+        hv = {(float(g["lr"]), float(g["weight_decay"])) for g in self.param_groups}
+        if len(hv) != 1:
+            raise ValueError("all parameter groups must share lr and weight_decay")
+        return hv.pop()
+
+    def step(self, closure=None):
+        import torch
+        loss = None
+        if closure is not None:
+            with torch.enable_grad():
+                loss = closure()
+        lr, wd = self._hyper()
+        if (lr, wd) != self._applied:
+            cfg = self.lopt.cfg
+            cfg.lr, cfg.weight_decay = lr, wd
+            lopt_set_config(self.lopt.handle, cfg)
+            self._applied = (float(cfg.lr), float(cfg.weight_decay))
+        grads = []
+        for p in self.lopt.params:
+            if p.grad is None:
+                raise ValueError("every parameter needs a gradient (the tensor list is fixed)")
+            grads.append(p.grad)
+        self.lopt.step(grads)
+        return loss

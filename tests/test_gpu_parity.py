@@ -7,6 +7,7 @@ r1..r3 and c1..c3 after each case's step count.  Integer/bitwise properties
 import numpy as np
 import pytest
 
+import oracle
 from gpu_harness import GpuRun, compare, hyper_from_cfg, oracle_run, parity, parity_one_step_rows, say
 
 torch = pytest.importorskip("torch")
@@ -180,4 +181,89 @@ def test_step_rejects_a_different_list():
                     torch.cuda.current_stream().cuda_stream)
     assert e.value.status == L.LOPT_ERR_STATE
     assert opt.t == 0
+    opt.close()
+
+
+def test_lr_schedule_and_weight_decay_through_torch_optimizer():
+    shapes = [(48, 40), (1, 100)]
+    m = mlp(bias_std=0.1)
+    w = W.custom_workload("sched", shapes, steps=6, wid=107)
+    params = [torch.from_numpy(W.param_init(w, i).reshape(t.shape)).cuda() for i, t in enumerate(w.tensors)]
+    opt = L.LearnedOptimizer(params, m, lr=0.8, weight_decay=0.05)
+    sched = torch.optim.lr_scheduler.CosineAnnealingLR(opt, T_max=6)
+    ps = [W.param_init(w, i) for i in range(2)]
+    sts = [W.state_init(w, i) for i in range(2)]
+    for t in range(1, 7):
+        lr = opt.param_groups[0]["lr"]
+        gs = [W.grad_at(w, i, t) for i in range(2)]
+        for p, g, tt in zip(params, gs, w.tensors):
+            p.grad = torch.from_numpy(g.reshape(tt.shape)).cuda()
+        opt.step()
+        ps, sts = oracle.step(ps, gs, sts, t, m, oracle.Hyper(lr=lr, weight_decay=0.05))
+        sched.step()
+    torch.cuda.synchronize()
+    assert opt.lopt.t == 6
+    errs = []
+    for i, tt in enumerate(w.tensors):
+        v = opt.lopt.state_views(i)
+        got = {"p": params[i].cpu().numpy().reshape(tt.rows, tt.cols)}
+        got.update({k: v[k].cpu().numpy() for k in ("m", "v", "r", "c")})
+        errs += compare(got, dict(p=ps[i], **sts[i]), f"sched[{i}]")
+    check(errs)
+
+
+def test_graph_replay_matches_eager_steps():
+    shapes = [(64, 96), (1, 500), (300, 7)]
+    m = mlp(bias_std=0.1)
+    w = W.custom_workload("graph", shapes, steps=5, wid=108)
+    grads = [torch.from_numpy(W.grad_at(w, i, 1).reshape(t.shape)).cuda() for i, t in enumerate(w.tensors)]
+
+    def fresh():
+        ps = [torch.from_numpy(W.param_init(w, i).reshape(t.shape)).cuda() for i, t in enumerate(w.tensors)]
+        return ps, L.LOpt(ps, m, L.config_from())
+
+    pe, eager = fresh()
+    pg, graphed = fresh()
+    eager.step(grads)
+    graphed.step(grads)          # binds the gradient pointers outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        graphed.step(grads)
+    for k in range(2, 6):
+        eager.step(grads)
+        g.replay()
+        torch.cuda.synchronize()
+        for i in range(len(shapes)):
+            assert torch.equal(pe[i], pg[i]), (k, i)
+            assert torch.equal(eager.states[i], graphed.states[i]), (k, i)
+    assert eager.t == 5 and graphed.t == 5
+    eager.close()
+    graphed.close()
+
+
+def test_set_config_rejects_other_n_time_and_timing_events_api():
+    p = torch.zeros(8, 8, device="cuda")
+    opt = L.LOpt([p], mlp(), L.config_from())
+    with pytest.raises(L.LoptError):
+        L.lopt_set_config(opt.handle, L.config_from(n_time=0))
+    L.lopt_set_config(opt.handle, L.config_from(lr=0.5))
+    with pytest.raises(L.LoptError):
+        L.lopt_set_timing_events(opt.handle, [1, 2])
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(L.LOPT_N_KERNELS + 1)]
+    for e in ev:
+        e.record()
+    L.lopt_set_timing_events(opt.handle, [e.cuda_event for e in ev])
+    opt.step([torch.full((8, 8), 1e-3, device="cuda")])
+    L.lopt_set_timing_events(opt.handle, [])
+    torch.cuda.synchronize()
+    times = [ev[j].elapsed_time(ev[j + 1]) for j in range(L.LOPT_N_KERNELS)]
+    assert all(t >= 0 for t in times)
+    opt.close()
+
+
+def test_empty_tensor_list_steps():
+    opt = L.LOpt([], mlp(), L.config_from())
+    opt.step([])
+    assert opt.t == 0     # no kernels, so the device counter does not advance
     opt.close()
