@@ -249,8 +249,8 @@ Plan build_plan(const lopt_tensor* ts, int32_t n) {
       d.nrseg = (d.R + kSeg1 - 1) / kSeg1;
       for (int a = 0; a < d.R; a += kSeg1)
         pl.segs1.push_back(Seg1{ti, kSegRows, a, std::min(d.R, a + kSeg1), rseg++, {0, 0, 0}});
-      for (int a = 0; a < d.C; a += kSeg1)
-        pl.segs1.push_back(Seg1{ti, kSegCols, a, std::min(d.C, a + kSeg1), -1, {0, 0, 0}});
+      for (int a = 0; a < d.C; a += kSegCols1)
+        pl.segs1.push_back(Seg1{ti, kSegCols, a, std::min(d.C, a + kSegCols1), -1, {0, 0, 0}});
     }
 
     // statistics / apply chunks

@@ -18,7 +18,9 @@ constexpr int kStatStride = 32;    // floats per stats partial / per-tensor scal
 // Work sizes.
 constexpr int kTile0Elems = 16384;   // elements per row/column-sum tile
 constexpr int kTile0Iters = 64;      // row iterations per 2-D tile (bounds the LDS buffer)
-constexpr int kSeg1 = 256;           // rows or columns per moving-average segment
+constexpr int kSeg1 = 256;           // rows per moving-average row segment
+constexpr int kSegCols1 = 64;        // columns per moving-average column segment ...
+constexpr int kColGroups = 4;        // ... each summed by 4 thread groups (64 x 4 = 256 threads)
 // Statistics / apply chunks: the plan picks one chunk size for the whole
 // tensor list, aiming at kTargetChunks chunks (several rounds of the ~768
 // workgroups the apply kernel keeps resident, so the last round is nearly

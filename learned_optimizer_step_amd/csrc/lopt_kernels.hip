@@ -59,6 +59,45 @@ __global__ __launch_bounds__(kBlock) void k_rowcol_sumsq(StepCtx c) {
     return;
   }
 
+  if (tl.cw_log2 == 8 && (d.C & 3) == 0 && (reinterpret_cast<uintptr_t>(g) & 15) == 0) {
+    // 256-column window, rows 16-byte aligned: each wave reads whole row
+    // segments with 16-byte loads (lane = 4 columns), waves take rows
+    // r0 + wave + 4u; a row's window sum completes inside one wave.
+    constexpr int kB = 8;  // rows per wave per batch
+    const int lane = tid & 63, wave = tid >> 6;
+    const int cb = tl.c0 + 4 * lane;
+    const bool act = cb < tl.c1;  // cols % 4 == 0: all four columns valid
+    const float4* __restrict__ g4 = reinterpret_cast<const float4*>(g);
+    const int C4 = d.C >> 2;
+    float4 ca = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int r = tl.r0 + wave; r < tl.r1; r += 4 * kB) {
+      float4 x[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        const int i = r + 4 * u;
+        x[u] = (act && i < tl.r1) ? g4[size_t(i) * C4 + (cb >> 2)] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        const float4 v = make_float4(x[u].x * x[u].x, x[u].y * x[u].y, x[u].z * x[u].z, x[u].w * x[u].w);
+        ca.x += v.x; ca.y += v.y; ca.z += v.z; ca.w += v.w;
+        const float rs = wave_sum((v.x + v.y) + (v.z + v.w));
+        const int i = r + 4 * u;
+        if (lane == 0 && i < tl.r1) ws[d.off_rowpart + size_t(tl.win) * d.R + i] = rs;
+      }
+    }
+    __shared__ float lds_c4[4][kBlock];
+    lds_c4[wave][4 * lane] = ca.x;
+    lds_c4[wave][4 * lane + 1] = ca.y;
+    lds_c4[wave][4 * lane + 2] = ca.z;
+    lds_c4[wave][4 * lane + 3] = ca.w;
+    __syncthreads();
+    const int j = tl.c0 + tid;
+    if (j < tl.c1)
+      ws[d.off_colpart + size_t(tl.rb) * d.C + j] = (lds_c4[0][tid] + lds_c4[1][tid]) + (lds_c4[2][tid] + lds_c4[3][tid]);
+    return;
+  }
+
   const int cwl = tl.cw_log2;
   const int CW = 1 << cwl;
   const int RS = kBlock >> cwl;
@@ -81,17 +120,18 @@ __global__ __launch_bounds__(kBlock) void k_rowcol_sumsq(StepCtx c) {
 #pragma unroll
     for (int u = 0; u < kRowBatch; ++u) {
       const int q = q0 + u;
-      if (q >= iters) break;  // uniform across the block
-      const int i = tl.r0 + slot + RS * q;
-      const float x2 = x[u] * x[u];
-      colacc += x2;
-      float rs = x2;
-      if (CW <= 64) {
-        for (int o = CW >> 1; o > 0; o >>= 1) rs += __shfl_xor(rs, o);
-        if (lc == 0 && i < tl.r1) ws[d.off_rowpart + size_t(tl.win) * R + i] = rs;
-      } else {
-        rs = wave_sum(rs);
-        if ((tid & 63) == 0) lds_rows[wave * kTile0Iters + q] = rs;
+      if (q < iters) {  // uniform across the block
+        const int i = tl.r0 + slot + RS * q;
+        const float x2 = x[u] * x[u];
+        colacc += x2;
+        float rs = x2;
+        if (CW <= 64) {
+          for (int o = CW >> 1; o > 0; o >>= 1) rs += __shfl_xor(rs, o);
+          if (lc == 0 && i < tl.r1) ws[d.off_rowpart + size_t(tl.win) * R + i] = rs;
+        } else {
+          rs = wave_sum(rs);
+          if ((tid & 63) == 0) lds_rows[wave * kTile0Iters + q] = rs;
+        }
       }
     }
   }
@@ -152,10 +192,18 @@ __global__ __launch_bounds__(kBlock) void k_moving_avg(StepCtx c, StepParams hp)
       if (tid == 0) c.rbar_part[sg.slot * 4 + k] = s;
     }
   } else if (sg.kind == kSegCols) {
-    const int j = sg.a + tid;
-    if (j < sg.b) {
-      float s = 0.f;
-      for (int b = 0; b < d.nrb; ++b) s += ws[d.off_colpart + size_t(b) * d.C + j];
+    // 64 columns per segment, 4 thread groups per column over the row-block
+    // partials (b = group, group + 4, ...), combined in LDS in group order.
+    __shared__ float part[kColGroups][kSegCols1];
+    const int jl = tid % kSegCols1, grp = tid / kSegCols1;
+    const int j = sg.a + jl;
+    float s = 0.f;
+    if (j < sg.b)
+      for (int b = grp; b < d.nrb; b += kColGroups) s += ws[d.off_colpart + size_t(b) * d.C + j];
+    part[grp][jl] = s;
+    __syncthreads();
+    if (grp == 0 && j < sg.b) {
+      s = (part[0][jl] + part[1][jl]) + (part[2][jl] + part[3][jl]);
       const float mean = s / float(d.R);
       float q[3];
 #pragma unroll

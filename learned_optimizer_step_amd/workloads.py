@@ -14,6 +14,7 @@ transformers; for an optimizer step only the parameter shapes matter):
 * ``vit_b16``     the ViT-B/16 parameter set (86,563,584 params, 147 tensors)
 * ``llama1b``     a Llama-style 1.26 G-parameter set (200 tensors)
 * ``ragged10k``   10,000 tensors with log-uniform sizes 16..1e6
+* ``gpt2_355m``   the GPT-2 355M parameter set (354,823,168 params, 292 tensors)
 
 Random numbers: numpy ``Generator(PCG64(SeedSequence([...])))`` keyed by
 (workload id, tensor index, step, stream) so any tensor can be regenerated on
@@ -108,6 +109,24 @@ def llama1b_tensors() -> Tuple[TensorSpec, ...]:
     return tuple(ts)
 
 
+def gpt2_355m_tensors() -> Tuple[TensorSpec, ...]:
+    """GPT-2 medium (24 layers, d_model 1024, vocab 50257, 1024 positions), the
+    page's second step-time workload.  Weights are stored (in, out) as GPT-2's
+    Conv1D layers do; the output head is tied to the token embedding."""
+    d, f, v, ctx = 1024, 4096, 50257, 1024
+    ts = [_mat("wte", v, d), _mat("wpe", ctx, d)]
+    for layer in range(24):
+        p = f"h.{layer}."
+        ts += [_vec(p + "ln_1.weight", d), _vec(p + "ln_1.bias", d),
+               _mat(p + "attn.c_attn.weight", d, 3 * d), _vec(p + "attn.c_attn.bias", 3 * d),
+               _mat(p + "attn.c_proj.weight", d, d), _vec(p + "attn.c_proj.bias", d),
+               _vec(p + "ln_2.weight", d), _vec(p + "ln_2.bias", d),
+               _mat(p + "mlp.c_fc.weight", d, f), _vec(p + "mlp.c_fc.bias", f),
+               _mat(p + "mlp.c_proj.weight", f, d), _vec(p + "mlp.c_proj.bias", d)]
+    ts += [_vec("ln_f.weight", d), _vec("ln_f.bias", d)]
+    return tuple(ts)
+
+
 def ragged_tensors(count: int = 10000, lo: int = 16, hi: int = 1_000_000,
                    seed: int = 5) -> Tuple[TensorSpec, ...]:
     """Log-uniform sizes; half 1-D, half 2-D with log-uniform aspect in [1/64, 64]."""
@@ -138,13 +157,16 @@ def get_workload(key: str) -> Workload:
     if key == "llama1b":
         return Workload(key, 4, llama1b_tensors(), 0.02, 1e-4, 1,
                         description="Llama-style parameter set, 1,261,527,040 fp32 params in 200 tensors")
+    if key == "gpt2_355m":
+        return Workload(key, 6, gpt2_355m_tensors(), 0.02, 1e-3, 1,
+                        description="GPT-2 355M parameter set, 354,823,168 fp32 params in 292 tensors")
     if key == "ragged10k":
         return Workload(key, 5, ragged_tensors(), 0.02, 1e-3, 1,
                         description="10,000 ragged tensors, sizes log-uniform 16..1e6")
     raise KeyError(key)
 
 
-WORKLOADS = ("single256", "single4096", "vit_b16", "llama1b", "ragged10k")
+WORKLOADS = ("single256", "single4096", "vit_b16", "llama1b", "ragged10k", "gpt2_355m")
 
 
 def custom_workload(key: str, shapes: Sequence[Tuple[int, ...]], param_std=0.02,

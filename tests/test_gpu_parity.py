@@ -267,3 +267,14 @@ def test_empty_tensor_list_steps():
     opt.step([])
     assert opt.t == 0     # no kernels, so the device counter does not advance
     opt.close()
+
+
+def test_gpt2_355m_one_step_sampled():
+    w = W.get_workload("gpt2_355m")
+    names = [t.name for t in w.tensors]
+    picks = {names.index("wte"): sample_rows(50257, 16, 5),
+             names.index("h.0.attn.c_attn.weight"): sample_rows(1024, 24, 6),
+             names.index("h.23.mlp.c_proj.weight"): sample_rows(4096, 24, 7),
+             names.index("h.11.mlp.c_fc.bias"): None,
+             names.index("ln_f.weight"): None}
+    check(parity_one_step_rows(w, mlp(), L.config_from(), torch, picks))
