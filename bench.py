@@ -98,6 +98,8 @@ def main():
     ap.add_argument("--workload", default="vit_b16")
     ap.add_argument("--impl", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--peaks", action="store_true",
+                    help="also run the machine-figure microbenchmark and include it as measured_peaks")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, run one plain 1 GiB device copy (reference for HBM counters)")
     args = ap.parse_args()
@@ -191,6 +193,12 @@ def main():
         "step_frac_fp32_peak": round(FLOP_PER_ELEM * n / (ms * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4),
         "kernels_ms": {name: round(float(t), 4) for name, t in zip(L.KERNEL_NAMES, kern_ms)},
     }
+    if args.peaks:
+        import subprocess
+        exe = os.path.join(ROOT, "learned_optimizer_step_amd", "lopt_microbench")
+        log("[bench] machine-figure microbenchmark")
+        res = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+        out["measured_peaks"] = json.loads(res.stdout) if res.returncode == 0 else {"error": res.stderr[-300:]}
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle on host cores)")
         out["cpu_baseline"] = cpu_baseline()

@@ -55,7 +55,21 @@ def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
     out_tmp = out + ".tmp"
     _run([hipcc(), "-shared", "-fPIC", *objs, "-o", out_tmp], verbose)
     os.replace(out_tmp, out)
+    if out == LIB:
+        build_microbench(verbose)
     return out
+
+
+MICROBENCH = os.path.join(PKG, "lopt_microbench")
+
+
+def build_microbench(verbose: bool = False) -> str:
+    """The machine-figure microbenchmark (read bandwidth, matrix vs vector issue)."""
+    tmp = MICROBENCH + ".tmp"
+    _run([hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", *DEVICE_FLAGS,
+          os.path.join(CSRC, "microbench.hip"), "-o", tmp], verbose)
+    os.replace(tmp, MICROBENCH)
+    return MICROBENCH
 
 
 if __name__ == "__main__":
