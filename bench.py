@@ -155,6 +155,7 @@ def main():
     kern = np.array([[events[k][j].elapsed_time(events[k][j + 1]) for j in range(nk)]
                      for k in range(args.steps)])
     kern_ms = kern.mean(axis=0)
+    per_step = np.array([events[k][0].elapsed_time(events[k][nk]) for k in range(args.steps)])
     opt.close()
     if args.calibrate_copy:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
@@ -165,7 +166,13 @@ def main():
         del src, dst
 
     n = w.n_params
+    n_vec = sum(t.n for t in w.tensors if t.rows == 1)
     value = n / (ms * 1e-3) / 1e9
+    # compulsory bytes of a step: read p, g, m1..3, v and write p, m1..3, v (44 B per element);
+    # a 1-D tensor also reads and writes its per-element c1..c3 (68 B)
+    step_bytes = 44 * (n - n_vec) + 68 * n_vec
+    # algorithmic bytes of the two streaming kernels: g (4 B); g, p, m1..3, v (24 B, 1-D + 12 B)
+    stream_bytes = {"k_rowcol_sumsq": 4 * n, "k_stats": 24 * n + 12 * n_vec}
     apply_ms = float(kern_ms[4])
     achieved = FLOP_PER_ELEM * n / (apply_ms * 1e-3) / 1e12
     use_mfma = impl != L.LOPT_MLP_VALU
@@ -192,13 +199,32 @@ def main():
                      "flop_per_elem": FLOP_PER_ELEM, "elems_per_launch": n},
         "step_frac_fp32_peak": round(FLOP_PER_ELEM * n / (ms * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4),
         "kernels_ms": {name: round(float(t), 4) for name, t in zip(L.KERNEL_NAMES, kern_ms)},
+        "step_ms_median": round(float(np.median(per_step)), 4),
+        "step_ms_min": round(float(per_step.min()), 4),
+        "step_frac_hbm": round(step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "hbm_kernels": {},
     }
+    for j, name in enumerate(L.KERNEL_NAMES):
+        if name in stream_bytes:
+            gbs = stream_bytes[name] / (kern_ms[j] * 1e-3) / 1e9
+            out["hbm_kernels"][name] = {"achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                        "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes": stream_bytes[name]}
     if args.peaks:
         import subprocess
         exe = os.path.join(ROOT, "learned_optimizer_step_amd", "lopt_microbench")
         log("[bench] machine-figure microbenchmark")
         res = subprocess.run([exe], capture_output=True, text=True, timeout=120)
-        out["measured_peaks"] = json.loads(res.stdout) if res.returncode == 0 else {"error": res.stderr[-300:]}
+        if res.returncode == 0:
+            mp = json.loads(res.stdout)
+            out["measured_peaks"] = mp
+            # the same kernels against what the microbenchmark sustains on this GPU
+            out["frac_of_measured"] = {
+                "k_apply_vs_mfma_4waves_2chains": round(achieved / mp["mfma_4waves_2chains_tflops"], 4)
+                if use_mfma else None,
+                "k_stats_vs_read_bw": round(out["hbm_kernels"]["k_stats"]["achieved"] / (mp["read_bw_TBps"] * 1e3), 4),
+            }
+        else:
+            out["measured_peaks"] = {"error": res.stderr[-300:]}
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle on host cores)")
         out["cpu_baseline"] = cpu_baseline()

@@ -64,9 +64,9 @@ MICROBENCH = os.path.join(PKG, "lopt_microbench")
 
 
 def build_microbench(verbose: bool = False) -> str:
-    """The machine-figure microbenchmark (read bandwidth, matrix vs vector issue)."""
+    """The machine-figure microbenchmark (read bandwidth, matrix throughput, vector-op costs)."""
     tmp = MICROBENCH + ".tmp"
-    _run([hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", *DEVICE_FLAGS,
+    _run([hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", *DEVICE_FLAGS, "-fno-honor-nans",
           os.path.join(CSRC, "microbench.hip"), "-o", tmp], verbose)
     os.replace(tmp, MICROBENCH)
     return MICROBENCH

@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cfloat>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -351,6 +352,11 @@ StepParams make_params(const lopt_handle* h) {
   p.decay = 1.0f - c.lr * c.weight_decay;
   p.lr_step = c.lr * c.step_mult;
   p.exp2_mult = float(double(c.exp_mult) * 1.4426950408889634);  // log2(e)
+  // Arguments of the per-element 1/sqrt: v + eps_v >= eps_v, and (1-D tensors)
+  // beta_f c + (1 - beta_f)(g^2 + eps_f) >= fl((1 - beta_f) eps_f) for c >= 0.
+  bool normal = c.eps_v >= 2.0f * FLT_MIN;
+  for (int k = 0; k < 3; ++k) normal = normal && p.omb_f[k] * c.eps_f >= 2.0f * FLT_MIN;
+  p.rsq_normal = normal ? 1 : 0;
   p.n_time = c.n_time;
   for (int q = 0; q < kMaxTime; ++q) p.timescales[q] = q < c.n_time ? c.timescales[q] : 1.f;
   return p;

@@ -15,7 +15,7 @@ namespace lopt {
 // k_apply_valu: the page's kernel 2 with the MLP on the vector ALU.  Weights
 // are read through uniform (scalar) loads from the packed copy, so every FMA
 // takes its weight from a scalar register.
-template <bool VEC>
+template <bool VEC, bool NORMAL>
 __device__ __forceinline__ void apply_valu_body(const StepCtx& c, const StepParams& hp, const Chunk& ch,
                                                 const TensorDesc& d, const float* g) {
   const Streams s = make_streams(d, g, c.ws, ch);
@@ -26,7 +26,8 @@ __device__ __forceinline__ void apply_valu_body(const StepCtx& c, const StepPara
     load_elem<VEC>(s, e, x);
     const float p_old = x.p;
     float F[kNF], cn[3];
-    build_features<VEC>(hp, x, F, cn);
+    build_features<VEC, NORMAL>(hp, x, F, cn);
+    store_state<VEC>(s, e, x, cn);
 #pragma unroll
     for (int f = 0; f < kNF; ++f) F[f] *= sc[f];
     float h1[kH];
@@ -47,7 +48,7 @@ __device__ __forceinline__ void apply_valu_body(const StepCtx& c, const StepPara
       dir = fmaf(pk[kPkW3 + o], a, dir);
       mag = fmaf(pk[kPkW3 + kH + o], a, mag);
     }
-    store_elem<VEC>(s, e, fmaf(-hp.lr_step, dir * __builtin_amdgcn_exp2f(mag * hp.exp2_mult), p_old * hp.decay), x, cn);
+    store_param(s, e, fmaf(-hp.lr_step, dir * __builtin_amdgcn_exp2f(mag * hp.exp2_mult), p_old * hp.decay));
   }
 }
 
@@ -56,8 +57,13 @@ __global__ __launch_bounds__(kBlock) void k_apply_valu(StepCtx c, StepParams hp)
   TensorDesc d;
   const float* g;
   load_chunk(c, blockIdx.x, ch, d, g);
-  if (d.vec) apply_valu_body<true>(c, hp, ch, d, g);
-  else apply_valu_body<false>(c, hp, ch, d, g);
+  if (d.vec) {
+    if (hp.rsq_normal) apply_valu_body<true, true>(c, hp, ch, d, g);
+    else apply_valu_body<true, false>(c, hp, ch, d, g);
+  } else {
+    if (hp.rsq_normal) apply_valu_body<false, true>(c, hp, ch, d, g);
+    else apply_valu_body<false, false>(c, hp, ch, d, g);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -90,7 +96,7 @@ __device__ __forceinline__ void swap_halves(float x, float y, float& lo, float& 
   hi = __uint_as_float(r[1]);
 }
 
-template <bool VEC>
+template <bool VEC, bool NORMAL>
 __device__ __forceinline__ void apply_mfma_body(const StepCtx& c, const StepParams& hp, const Chunk& ch,
                                                 const TensorDesc& d, const float* g) {
   const int lane = threadIdx.x & 63;
@@ -129,7 +135,10 @@ __device__ __forceinline__ void apply_mfma_body(const StepCtx& c, const StepPara
     load_elem<VEC>(s, valid ? e : ch.e0, x);
     const float p_old = x.p;
     float F[kNF], cn[3];
-    build_features<VEC>(hp, x, F, cn);
+    build_features<VEC, NORMAL>(hp, x, F, cn);
+    // the accumulators are final here: storing them now frees their registers
+    // (and the copies the lane swaps below would need) during the MLP
+    if (valid) store_state<VEC>(s, e, x, cn);
 
     f32x16 bias1, bias2;
 #pragma unroll
@@ -192,7 +201,7 @@ __device__ __forceinline__ void apply_mfma_body(const StepCtx& c, const StepPara
     const float dir = (d0 + d1) + b3d;
     const float mag = (m0 + m1) + b3m;
     if (valid) {
-      store_elem<VEC>(s, e, fmaf(-hp.lr_step, dir * __builtin_amdgcn_exp2f(mag * hp.exp2_mult), p_old * hp.decay), x, cn);
+      store_param(s, e, fmaf(-hp.lr_step, dir * __builtin_amdgcn_exp2f(mag * hp.exp2_mult), p_old * hp.decay));
     }
   }
 }
@@ -202,8 +211,13 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   TensorDesc d;
   const float* g;
   load_chunk(c, blockIdx.x, ch, d, g);
-  if (d.vec) apply_mfma_body<true>(c, hp, ch, d, g);
-  else apply_mfma_body<false>(c, hp, ch, d, g);
+  if (d.vec) {
+    if (hp.rsq_normal) apply_mfma_body<true, true>(c, hp, ch, d, g);
+    else apply_mfma_body<true, false>(c, hp, ch, d, g);
+  } else {
+    if (hp.rsq_normal) apply_mfma_body<false, true>(c, hp, ch, d, g);
+    else apply_mfma_body<false, false>(c, hp, ch, d, g);
+  }
 }
 
 hipError_t launch_apply(const StepCtx& c, const StepParams& p, hipStream_t s) {

@@ -156,7 +156,15 @@ struct Elem {
 //   1-D (rows = 1): c_k is per element and rbar_k = r_k, so rho_k = c_k^(-1/2).
 // Features 10..12 and 19..27 are linear in rho_k, so the finalize kernel moves
 // sqrt(rbar_k) into their normalisation scales (rho_feature below).
-template <bool VEC>
+// 1/sqrt(x).  NORMAL: x is known to be >= FLT_MIN, 0, inf or NaN, where the
+// hardware instruction alone is exact to its spec; rsqrtf adds a rescaling of
+// subnormal arguments (five more vector instructions per call).
+template <bool NORMAL>
+__device__ __forceinline__ float rsq(float x) {
+  return NORMAL ? __builtin_amdgcn_rsqf(x) : rsqrtf(x);
+}
+
+template <bool VEC, bool NORMAL>
 __device__ __forceinline__ void build_features(const StepParams& hp, Elem& x, float F[kNF], float cn[3]) {
   const float g = x.g;
   const float g2 = g * g;
@@ -168,14 +176,14 @@ __device__ __forceinline__ void build_features(const StepParams& hp, Elem& x, fl
   for (int k = 0; k < 3; ++k) {
     if (VEC) {
       cn[k] = fmaf(hp.beta_f[k], x.cq[k], hp.omb_f[k] * (g2 + hp.eps_f));
-      cq[k] = rsqrtf(cn[k]);
+      cq[k] = rsq<NORMAL>(cn[k]);
       rho[k] = cq[k];
     } else {
       cq[k] = x.cq[k];
       rho[k] = x.rq[k] * cq[k];
     }
   }
-  const float q = rsqrtf(x.v + hp.eps_v);
+  const float q = rsq<NORMAL>(x.v + hp.eps_v);
   F[0] = g;
   F[1] = x.p;
   F[2] = x.m[0]; F[3] = x.m[1]; F[4] = x.m[2];
@@ -222,12 +230,10 @@ __device__ __forceinline__ void load_elem(const Streams& s, uint32_t e, Elem& x)
   }
 }
 
-// Stores the updated parameter and per-element accumulators of element e.
+// Stores the updated per-element accumulators of element e (m, v; 1-D: c).
 template <bool VEC>
-__device__ __forceinline__ void store_elem(const Streams& s, uint32_t e, float p_new, const Elem& x,
-                                           const float cn[3]) {
+__device__ __forceinline__ void store_state(const Streams& s, uint32_t e, const Elem& x, const float cn[3]) {
   const uint32_t off = (e - s.e0) * 4u;
-  stb(s.p, off, p_new);
 #pragma unroll
   for (int a = 0; a < 3; ++a) stb(s.m[a], off, x.m[a]);
   stb(s.v, off, x.v);
@@ -235,6 +241,11 @@ __device__ __forceinline__ void store_elem(const Streams& s, uint32_t e, float p
 #pragma unroll
     for (int k = 0; k < 3; ++k) stb(s.c[k], off, cn[k]);
   }
+}
+
+// Stores the updated parameter of element e.
+__device__ __forceinline__ void store_param(const Streams& s, uint32_t e, float p_new) {
+  stb(s.p, (e - s.e0) * 4u, p_new);
 }
 
 // sqrt(mean_i r_k[i]) from the per-segment partial sums of r_k, summed by the

@@ -101,6 +101,11 @@ struct StepParams {
   float decay;               // 1 - lr * weight_decay
   float lr_step;             // lr * step_mult
   float exp2_mult;           // exp_mult * log2(e)
+  // 1 when every argument of a per-element 1/sqrt is >= FLT_MIN, 0, inf or NaN
+  // (eps_v and (1 - beta_f) eps_f are at least 2 FLT_MIN): the kernels then use
+  // the bare hardware reciprocal square root, which only differs from rsqrtf
+  // on subnormal arguments.
+  int32_t rsq_normal;
   int32_t n_time;
   float timescales[kMaxTime];
 };

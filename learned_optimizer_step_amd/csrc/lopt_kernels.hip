@@ -235,17 +235,17 @@ __global__ __launch_bounds__(kBlock) void k_moving_avg(StepCtx c, StepParams hp)
 // k_stats: per-chunk sums of the squares of the 28 features (the page's
 // kernel 1).  Accumulators are updated in registers only; the apply kernel
 // recomputes them from the same inputs.
-template <bool VEC>
+template <bool VEC, bool NORMAL>
 __device__ __forceinline__ void stats_accumulate(const StepParams& hp, Elem& x, float acc[kNF]) {
   float F[kNF], cn[3];
-  build_features<VEC>(hp, x, F, cn);
+  build_features<VEC, NORMAL>(hp, x, F, cn);
 #pragma unroll
   for (int f = 0; f < kNF; ++f) acc[f] = fmaf(F[f], F[f], acc[f]);
 }
 
 // Four elements per thread per iteration, their loads issued together, so
 // each thread keeps ~100 bytes of HBM reads in flight.
-template <bool VEC>
+template <bool VEC, bool NORMAL>
 __device__ __forceinline__ void stats_body(const StepCtx& c, const StepParams& hp, const Chunk& ch,
                                            const TensorDesc& d, const float* g, float acc[kNF]) {
   const Streams st = make_streams(d, g, c.ws, ch);
@@ -255,12 +255,12 @@ __device__ __forceinline__ void stats_body(const StepCtx& c, const StepParams& h
 #pragma unroll
     for (int u = 0; u < 4; ++u) load_elem<VEC>(st, e + u * kBlock, x[u]);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) stats_accumulate<VEC>(hp, x[u], acc);
+    for (int u = 0; u < 4; ++u) stats_accumulate<VEC, NORMAL>(hp, x[u], acc);
   }
   for (; e < ch.e1; e += kBlock) {
     Elem x;
     load_elem<VEC>(st, e, x);
-    stats_accumulate<VEC>(hp, x, acc);
+    stats_accumulate<VEC, NORMAL>(hp, x, acc);
   }
 }
 
@@ -273,8 +273,13 @@ __global__ __launch_bounds__(kBlock) void k_stats(StepCtx c, StepParams hp) {
   float acc[kNF];
 #pragma unroll
   for (int f = 0; f < kNF; ++f) acc[f] = 0.f;
-  if (d.vec) stats_body<true>(c, hp, ch, d, g, acc);
-  else stats_body<false>(c, hp, ch, d, g, acc);
+  if (d.vec) {
+    if (hp.rsq_normal) stats_body<true, true>(c, hp, ch, d, g, acc);
+    else stats_body<true, false>(c, hp, ch, d, g, acc);
+  } else {
+    if (hp.rsq_normal) stats_body<false, true>(c, hp, ch, d, g, acc);
+    else stats_body<false, false>(c, hp, ch, d, g, acc);
+  }
   const int w = threadIdx.x >> 6;
 #pragma unroll
   for (int f = 0; f < kNF; ++f) {

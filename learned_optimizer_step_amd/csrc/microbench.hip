@@ -1,10 +1,14 @@
 // Measured machine figures behind the roofline of the optimizer step:
-//   1. streaming read bandwidth of HBM (the bound of the statistics pass),
-//   2. fp32 matrix-core vs vector-ALU issue: the time of a loop of
-//      independent v_mfma_f32_32x32x2_f32, of a loop of independent v_fma_f32,
-//      and of both interleaved (if the two co-execute, "both" ~ max; if they
-//      share the SIMD's issue, "both" ~ sum).
-// Prints one JSON object.  Every kernel stays inside its buffers.
+//   1. streaming read bandwidth of HBM (the bound of the statistics pass);
+//   2. sustained fp32 matrix throughput (v_mfma_f32_32x32x2_f32) for 1, 2 and
+//      4 waves per SIMD and 1, 2 or 4 independent accumulator chains per wave
+//      (the apply kernel runs 4 waves with 2 chains each);
+//   3. what one vector instruction of a given kind adds to a stream of
+//      matrix instructions (4 waves x 2 chains): on gfx950 the fp32 matrix
+//      instructions and the vector ALU share the SIMD's issue, so vector work
+//      adds to the matrix time instead of hiding under it.
+// Prints one JSON object.  Every kernel writes only out[block * 64 + lane],
+// and out is sized for the largest grid launched.
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
@@ -24,29 +28,58 @@ __global__ __launch_bounds__(256) void read_stream(const float4* __restrict__ a,
   out[size_t(blockIdx.x) * 256 + threadIdx.x] = acc;
 }
 
-// MODE 1: 4 MFMAs per iteration; 2: 64 FMAs per iteration; 3: both.
-template <int MODE>
-__global__ __launch_bounds__(64) void issue_mix(float* out, int iters, float s) {
-  f32x16 a0 = {0}, a1 = {0}, a2 = {0}, a3 = {0};
-  float v[16];
-  for (int i = 0; i < 16; ++i) v[i] = threadIdx.x * 0.001f + i;
+// 16 matrix instructions per iteration over NACC independent accumulators.
+template <int NACC>
+__global__ __launch_bounds__(64) void mfma_chains(float* out, int iters, float s) {
+  f32x16 a[NACC];
+#pragma unroll
+  for (int k = 0; k < NACC; ++k) a[k] = f32x16{0};
   const float x = s * threadIdx.x, y = s + threadIdx.x;
   for (int it = 0; it < iters; ++it) {
-    if (MODE & 1) {
-      a0 = __builtin_amdgcn_mfma_f32_32x32x2f32(x, y, a0, 0, 0, 0);
-      a1 = __builtin_amdgcn_mfma_f32_32x32x2f32(x, y, a1, 0, 0, 0);
-      a2 = __builtin_amdgcn_mfma_f32_32x32x2f32(x, y, a2, 0, 0, 0);
-      a3 = __builtin_amdgcn_mfma_f32_32x32x2f32(x, y, a3, 0, 0, 0);
-    }
-    if (MODE & 2) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < 16 / NACC; ++r)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = fmaf(v[i], s, x);
+      for (int k = 0; k < NACC; ++k) a[k] = __builtin_amdgcn_mfma_f32_32x32x2f32(x, y, a[k], 0, 0, 0);
+  }
+  float acc = 0.f;
+#pragma unroll
+  for (int k = 0; k < NACC; ++k)
+    for (int i = 0; i < 16; ++i) acc += a[k][i];
+  out[size_t(blockIdx.x) * 64 + threadIdx.x] = acc;
+}
+
+// 4 matrix instructions (2 chains) plus 16 independent vector instructions of
+// one kind per iteration.  OP 0: none, 1: v_fma_f32, 2: v_max_f32 (ReLU form),
+// 3: v_permlane32_swap (8 instructions, each swapping a pair), 4: v_add_u32.
+template <int OP>
+__global__ __launch_bounds__(64) void mfma_plus(float* out, int iters, float s) {
+  f32x16 a0 = {0}, a1 = {0};
+  float v[16];
+  unsigned u[16];
+  for (int i = 0; i < 16; ++i) {
+    v[i] = threadIdx.x * 0.001f + i;
+    u[i] = threadIdx.x * 7u + i;
+  }
+  const float x = s * threadIdx.x, y = s + threadIdx.x;
+  for (int it = 0; it < iters; ++it) {
+    a0 = __builtin_amdgcn_mfma_f32_32x32x2f32(x, y, a0, 0, 0, 0);
+    a1 = __builtin_amdgcn_mfma_f32_32x32x2f32(x, y, a1, 0, 0, 0);
+    a0 = __builtin_amdgcn_mfma_f32_32x32x2f32(x, y, a0, 0, 0, 0);
+    a1 = __builtin_amdgcn_mfma_f32_32x32x2f32(x, y, a1, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (OP == 1) v[i] = fmaf(v[i], s, x);
+      if (OP == 2) v[i] = __builtin_fmaxf(-v[i], 0.f);
+      if (OP == 3 && (i & 1) == 0) {
+        const auto p = __builtin_amdgcn_permlane32_swap(u[i], u[i + 1], false, false);
+        u[i] = p[0];
+        u[i + 1] = p[1];
+      }
+      if (OP == 4) u[i] = u[i] + u[(i + 1) & 15];
     }
   }
   float acc = 0.f;
-  for (int i = 0; i < 16; ++i) acc += a0[i] + a1[i] + a2[i] + a3[i] + v[i];
+  for (int i = 0; i < 16; ++i) acc += a0[i] + a1[i] + v[i] + float(u[i]);
   out[size_t(blockIdx.x) * 64 + threadIdx.x] = acc;
 }
 
@@ -58,60 +91,99 @@ __global__ __launch_bounds__(64) void issue_mix(float* out, int iters, float s) 
     }                                                                 \
   } while (0)
 
+static hipEvent_t e0, e1;
+
+// Best of 3 timed launches (the first of 4 warms up), in ms; < 0 on error.
+template <class F>
+static float time_ms(F launch) {
+  float best = 1e30f;
+  for (int rep = 0; rep < 4; ++rep) {
+    if (hipEventRecord(e0) != hipSuccess) return -1.f;
+    launch();
+    if (hipEventRecord(e1) != hipSuccess || hipEventSynchronize(e1) != hipSuccess) return -1.f;
+    float ms;
+    if (hipEventElapsedTime(&ms, e0, e1) != hipSuccess) return -1.f;
+    if (rep > 0 && ms < best) best = ms;
+  }
+  return hipGetLastError() == hipSuccess ? best : -1.f;
+}
+
 int main() {
   hipDeviceProp_t prop;
   CHECK(hipGetDeviceProperties(&prop, 0));
   const int cus = prop.multiProcessorCount;
-  hipEvent_t e0, e1;
   CHECK(hipEventCreate(&e0));
   CHECK(hipEventCreate(&e1));
 
-  // 1. read bandwidth, 2 GiB, best of 5 per grid size
+  // 1. read bandwidth, 2 GiB, best per grid size
   const size_t bytes = size_t(2) << 30;
-  float *buf, *out;
   const int max_grid = 65536;
+  float *buf, *out;
   CHECK(hipMalloc(&buf, bytes));
-  CHECK(hipMalloc(&out, size_t(max_grid) * 256 * sizeof(float)));
+  CHECK(hipMalloc(&out, size_t(max_grid) * 256 * sizeof(float)));  // also >= cus * 16 * 64 floats
+  if (size_t(max_grid) * 256 < size_t(cus) * 16 * 64) return 1;
   CHECK(hipMemset(buf, 0, bytes));
   double best_bw = 0.0;
   int best_grid = 0;
   for (int grid : {2048, 4096, 8192, 16384, 65536}) {
-    for (int r = 0; r < 5; ++r) {
-      CHECK(hipEventRecord(e0));
-      hipLaunchKernelGGL(read_stream, dim3(grid), dim3(256), 0, 0, reinterpret_cast<const float4*>(buf),
-                         bytes / 16, out);
-      CHECK(hipEventRecord(e1));
-      CHECK(hipEventSynchronize(e1));
-      float ms;
-      CHECK(hipEventElapsedTime(&ms, e0, e1));
-      const double bw = bytes / (ms * 1e-3) / 1e12;
-      if (bw > best_bw) { best_bw = bw; best_grid = grid; }
+    const float ms = time_ms([&] {
+      hipLaunchKernelGGL(read_stream, dim3(grid), dim3(256), 0, 0, reinterpret_cast<const float4*>(buf), bytes / 16,
+                         out);
+    });
+    if (ms <= 0.f) return 1;
+    const double bw = bytes / (ms * 1e-3) / 1e12;
+    if (bw > best_bw) {
+      best_bw = bw;
+      best_grid = grid;
     }
   }
   CHECK(hipFree(buf));
-
-  // 2. matrix vs vector issue, one and four waves per SIMD
-  const int iters = 20000;
   printf("{\"device\": \"%s\", \"cus\": %d, \"read_bw_TBps\": %.3f, \"read_bw_grid\": %d", prop.gcnArchName, cus,
          best_bw, best_grid);
-  for (int wps : {1, 4}) {
-    const int blocks = cus * 4 * wps;
-    float ms[3];
-    for (int m = 0; m < 3; ++m) {
-      for (int rep = 0; rep < 2; ++rep) {  // first launch warms up
-        CHECK(hipEventRecord(e0));
-        if (m == 0) hipLaunchKernelGGL(issue_mix<1>, dim3(blocks), dim3(64), 0, 0, out, iters, 1.0001f);
-        if (m == 1) hipLaunchKernelGGL(issue_mix<2>, dim3(blocks), dim3(64), 0, 0, out, iters, 1.0001f);
-        if (m == 2) hipLaunchKernelGGL(issue_mix<3>, dim3(blocks), dim3(64), 0, 0, out, iters, 1.0001f);
-        CHECK(hipEventRecord(e1));
-        CHECK(hipEventSynchronize(e1));
-        CHECK(hipEventElapsedTime(&ms[m], e0, e1));
-      }
+
+  // 2. matrix throughput: waves per SIMD x accumulator chains per wave
+  const int iters = 4000;
+  printf(", \"mfma_tflops\": {");
+  double w4c2 = 0.0;
+  bool first = true;
+  for (int w : {1, 2, 4}) {
+    const int blocks = cus * 4 * w;
+    for (int nacc : {1, 2, 4}) {
+      const float ms = time_ms([&] {
+        if (nacc == 1) hipLaunchKernelGGL(mfma_chains<1>, dim3(blocks), dim3(64), 0, 0, out, iters, 1.0001f);
+        if (nacc == 2) hipLaunchKernelGGL(mfma_chains<2>, dim3(blocks), dim3(64), 0, 0, out, iters, 1.0001f);
+        if (nacc == 4) hipLaunchKernelGGL(mfma_chains<4>, dim3(blocks), dim3(64), 0, 0, out, iters, 1.0001f);
+      });
+      if (ms <= 0.f) return 1;
+      const double tf = double(blocks) * iters * 16 * 4096 / (ms * 1e-3) / 1e12;  // 4096 FLOP per instruction
+      if (w == 4 && nacc == 2) w4c2 = tf;
+      printf("%s\"waves%d_chains%d\": %.1f", first ? "" : ", ", w, nacc, tf);
+      first = false;
     }
-    const double mx = ms[0] > ms[1] ? ms[0] : ms[1];
-    printf(", \"waves_per_simd_%d\": {\"mfma_ms\": %.3f, \"valu_ms\": %.3f, \"both_ms\": %.3f, "
-           "\"both_over_max\": %.3f, \"both_over_sum\": %.3f}",
-           wps, ms[0], ms[1], ms[2], ms[2] / mx, ms[2] / (ms[0] + ms[1]));
+  }
+  printf("}, \"mfma_4waves_2chains_tflops\": %.1f", w4c2);
+
+  // 3. added cycles per vector instruction, 4 waves x 2 chains: alone, the 4
+  // matrix instructions of an iteration take 4 x 64 = 256 SIMD cycles
+  {
+    const int blocks = cus * 4 * 4, it2 = 8000;
+    float ms[5];
+    for (int op = 0; op < 5; ++op) {
+      ms[op] = time_ms([&] {
+        if (op == 0) hipLaunchKernelGGL(mfma_plus<0>, dim3(blocks), dim3(64), 0, 0, out, it2, 1.0001f);
+        if (op == 1) hipLaunchKernelGGL(mfma_plus<1>, dim3(blocks), dim3(64), 0, 0, out, it2, 1.0001f);
+        if (op == 2) hipLaunchKernelGGL(mfma_plus<2>, dim3(blocks), dim3(64), 0, 0, out, it2, 1.0001f);
+        if (op == 3) hipLaunchKernelGGL(mfma_plus<3>, dim3(blocks), dim3(64), 0, 0, out, it2, 1.0001f);
+        if (op == 4) hipLaunchKernelGGL(mfma_plus<4>, dim3(blocks), dim3(64), 0, 0, out, it2, 1.0001f);
+      });
+      if (ms[op] <= 0.f) return 1;
+    }
+    const char* names[5] = {"", "v_fma_f32", "v_max_f32", "v_permlane32_swap", "v_add_u32"};
+    const int count[5] = {0, 16, 16, 8, 16};  // instructions per iteration
+    printf(", \"added_cycles_per_vector_op\": {");
+    for (int op = 1; op < 5; ++op)
+      printf("%s\"%s\": %.2f", op == 1 ? "" : ", ", names[op], (ms[op] - ms[0]) / ms[0] * 256.0 / count[op]);
+    printf("}");
   }
   printf("}\n");
   CHECK(hipFree(out));
