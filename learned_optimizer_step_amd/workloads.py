@@ -29,7 +29,8 @@ from typing import List, Optional, Sequence, Tuple
 import numpy as np
 
 HIDDEN = 32
-N_FEATURES = 28
+N_FEATURES = 28        # small_fc_lopt's per-element features
+VELO_FEATURES = 19     # the d_feat = 30 VeLO-shaped variant's per-element features
 N_TIME = 11
 
 # RNG stream ids inside a (workload, tensor, step) key
@@ -224,12 +225,13 @@ def state_init(w: Workload, tidx: int) -> dict:
     return {"m": m, "v": v, "r": r, "c": c}
 
 
-def mlp_weights(n_time: int = N_TIME, seed=MLP_SEED, bias_std: float = 0.0) -> np.ndarray:
-    """Packed fp32 MLP weights W1[32][28+n_time], b1[32], W2[32][32], b2[32], W3[2][32], b3[2].
+def mlp_weights(n_time: int = N_TIME, seed=MLP_SEED, bias_std: float = 0.0,
+                n_feat: int = N_FEATURES) -> np.ndarray:
+    """Packed fp32 MLP weights W1[32][n_feat+n_time], b1[32], W2[32][32], b2[32], W3[2][32], b3[2].
 
     Weights ~ N(0, 1/fan_in) (variance 1/fan_in); biases zero unless ``bias_std`` > 0.
     """
-    d_in = N_FEATURES + n_time
+    d_in = n_feat + n_time
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(list(seed))))
     parts = []
     for fan_out, fan_in in ((HIDDEN, d_in), (HIDDEN, HIDDEN), (2, HIDDEN)):
@@ -239,6 +241,6 @@ def mlp_weights(n_time: int = N_TIME, seed=MLP_SEED, bias_std: float = 0.0) -> n
     return np.concatenate(parts).astype(np.float32)
 
 
-def mlp_floats(n_time: int = N_TIME) -> int:
-    d_in = N_FEATURES + n_time
+def mlp_floats(n_time: int = N_TIME, n_feat: int = N_FEATURES) -> int:
+    d_in = n_feat + n_time
     return HIDDEN * d_in + HIDDEN + HIDDEN * HIDDEN + HIDDEN + 2 * HIDDEN + 2

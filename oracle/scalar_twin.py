@@ -81,7 +81,7 @@ def twin_step(p, g, st, t, w, hp):
                 out.append(ma[a] * rho[k])
         return out
 
-    nf = 28
+    nf = getattr(hp, "n_feat", 28)   # the VeLO-shaped variant uses the first 19
     sums = [0.0] * nf
     for i in range(R):
         for j in range(C):
@@ -115,9 +115,9 @@ def twin_step(p, g, st, t, w, hp):
     return p_new, st_new, raw
 
 
-def unpack(flat, n_time):
-    """Packed layout W1[32][28+n_time], b1, W2[32][32], b2, W3[2][32], b3 -> dict of lists."""
-    d_in = 28 + n_time
+def unpack(flat, n_time, n_feat=28):
+    """Packed layout W1[32][n_feat+n_time], b1, W2[32][32], b2, W3[2][32], b3 -> dict of lists."""
+    d_in = n_feat + n_time
     flat = [float(x) for x in flat]
     o = 0
 

@@ -41,6 +41,11 @@ them as follows (each choice is one "reading"):
       (default 0): p <- p - lr*u - lr*wd*p.
   R18 hyperparameters are fp32 numbers (they are passed as fp32).
   R24 no bias correction of the moving averages.
+  R26 the VeLO-shaped variant (n_feat = 19): the same page gives VeLO's feature
+      width as about 30 and runs it through the same two fused kernels, but
+      lists no feature; here it keeps F0..F18 (every family: parameter,
+      gradient, momentum and RMS averages, factored row/column terms) and the
+      11 step features, 30 inputs, with the same MLP shape and update rule.
 
 Per element (i, j) of a tensor viewed as R x C, with a = 1..3 and k = 1..3:
   m_a <- b_a m_a + (1 - b_a) g            v <- b_v v + (1 - b_v) g^2
@@ -64,7 +69,9 @@ from typing import List, Optional, Sequence, Tuple
 
 import numpy as np
 
-N_FEATURES = 28
+N_FEATURES = 28          # per-element features of small_fc_lopt (R1)
+VELO_FEATURES = 19       # per-element features of the VeLO-shaped variant (R26)
+FEATURE_SETS = (N_FEATURES, VELO_FEATURES)
 HIDDEN = 32
 DEFAULT_TIMESCALES = (1.0, 3.0, 10.0, 30.0, 100.0, 300.0, 1e3, 3e3, 1e4, 3e4, 1e5)
 
@@ -92,6 +99,7 @@ class Hyper:
     weight_decay: float = 0.0
     n_time: int = 11
     timescales: Tuple[float, ...] = DEFAULT_TIMESCALES
+    n_feat: int = N_FEATURES   # per-element MLP inputs: the first n_feat of F0..F27
 
     def as_f32(self) -> "Hyper":
         """The same hyperparameters rounded to fp32 (what the fp32 config holds)."""
@@ -99,12 +107,12 @@ class Hyper:
                      tuple(_f32(b) for b in self.beta_f), _f32(self.eps_v), _f32(self.eps_f),
                      _f32(self.eps_norm), _f32(self.exp_mult), _f32(self.step_mult),
                      _f32(self.lr), _f32(self.weight_decay), int(self.n_time),
-                     tuple(_f32(x) for x in self.timescales[: self.n_time]))
+                     tuple(_f32(x) for x in self.timescales[: self.n_time]), int(self.n_feat))
 
 
 @dataclass
 class Mlp:
-    W1: np.ndarray  # (32, 28 + n_time)
+    W1: np.ndarray  # (32, n_feat + n_time)
     b1: np.ndarray  # (32,)
     W2: np.ndarray  # (32, 32)
     b2: np.ndarray
@@ -112,17 +120,17 @@ class Mlp:
     b3: np.ndarray  # (2,)
 
 
-def mlp_size(n_time: int) -> int:
-    d_in = N_FEATURES + n_time
+def mlp_size(n_time: int, n_feat: int = N_FEATURES) -> int:
+    d_in = n_feat + n_time
     return HIDDEN * d_in + HIDDEN + HIDDEN * HIDDEN + HIDDEN + 2 * HIDDEN + 2
 
 
-def unpack_mlp(flat: np.ndarray, n_time: int) -> Mlp:
+def unpack_mlp(flat: np.ndarray, n_time: int, n_feat: int = N_FEATURES) -> Mlp:
     """Packed row-major (out x in) layout: W1, b1, W2, b2, W3, b3."""
     flat = np.asarray(flat, dtype=np.float64)
-    d_in = N_FEATURES + n_time
-    if flat.size != mlp_size(n_time):
-        raise ValueError(f"expected {mlp_size(n_time)} MLP floats, got {flat.size}")
+    d_in = n_feat + n_time
+    if flat.size != mlp_size(n_time, n_feat):
+        raise ValueError(f"expected {mlp_size(n_time, n_feat)} MLP floats, got {flat.size}")
     sizes = [(HIDDEN, d_in), (HIDDEN,), (HIDDEN, HIDDEN), (HIDDEN,), (2, HIDDEN), (2,)]
     out, o = [], 0
     for s in sizes:
@@ -186,7 +194,8 @@ def accumulate(g: np.ndarray, state: dict, hp: Hyper) -> Accumulators:
 # ------------------------------------------------------------------- features
 def features(p: np.ndarray, g: np.ndarray, acc: Accumulators, hp: Hyper,
              rows: slice = slice(None)) -> np.ndarray:
-    """The 28 per-element features of the rows ``rows``; shape (rows, C, 28)."""
+    """The first ``hp.n_feat`` of the 28 per-element features of the rows ``rows``;
+    shape (rows, C, n_feat)."""
     p = as_matrix(p)[rows].astype(np.float64)
     g = as_matrix(g)[rows].astype(np.float64)
     m = acc.m[:, rows]
@@ -212,7 +221,7 @@ def features(p: np.ndarray, g: np.ndarray, acc: Accumulators, hp: Hyper,
         F[..., 16 + k] = (1.0 / np.sqrt(c[k]))[None, :]
         for a in range(3):
             F[..., cross_index(a, k)] = m[a] * rho
-    return F
+    return F[..., : hp.n_feat]
 
 
 def time_features(t: int, hp: Hyper) -> np.ndarray:
@@ -240,11 +249,11 @@ def update_from_output(direction, magnitude, hp: Hyper):
 # ------------------------------------------------------------------ one tensor
 @dataclass
 class StepInfo:
-    sum_sq: np.ndarray          # (28,) sum of F_d^2 over the tensor
-    scales: np.ndarray          # (28,) s_d
+    sum_sq: np.ndarray          # (n_feat,) sum of F_d^2 over the tensor
+    scales: np.ndarray          # (n_feat,) s_d
     u: Optional[np.ndarray] = None
-    F: Optional[np.ndarray] = None       # (R, C, 28) raw features
-    x: Optional[np.ndarray] = None       # (R, C, 28 + n_time) MLP input
+    F: Optional[np.ndarray] = None       # (R, C, n_feat) raw features
+    x: Optional[np.ndarray] = None       # (R, C, n_feat + n_time) MLP input
     acc: Optional[Accumulators] = None
 
 
@@ -271,18 +280,19 @@ def step_tensor(p, g, state: dict, t: int, mlp: Mlp, hp: Hyper,
     blocks = [slice(i, min(i + block_rows, R)) for i in range(0, R, block_rows)]
 
     # pass 1: sum of squares of each feature over the tensor
-    sum_sq = np.zeros(N_FEATURES)
+    nf = hp.n_feat
+    sum_sq = np.zeros(nf)
     for rs in blocks:
         F = features(P, G, acc, hp, rs)
-        sum_sq += (F * F).reshape(-1, N_FEATURES).sum(axis=0)
+        sum_sq += (F * F).reshape(-1, nf).sum(axis=0)
     scales = feature_scales(sum_sq, n, hp)
     T = time_features(t, hp)
 
     # pass 2: normalised features -> MLP -> update
     p_new = np.empty((R, C))
     u_all = np.empty((R, C)) if keep else None
-    F_all = np.empty((R, C, N_FEATURES)) if keep else None
-    x_all = np.empty((R, C, N_FEATURES + hp.n_time)) if keep else None
+    F_all = np.empty((R, C, nf)) if keep else None
+    x_all = np.empty((R, C, nf + hp.n_time)) if keep else None
     for rs in blocks:
         F = features(P, G, acc, hp, rs)
         nr = F.shape[0]
@@ -320,10 +330,11 @@ def step_tensor_rows(p, g, state: dict, t: int, mlp: Mlp, hp: Hyper, rows: Seque
     acc = accumulate(G, state, hp)
     if block_rows is None:
         block_rows = max(1, (1 << 14) // max(C, 1))
-    sum_sq = np.zeros(N_FEATURES)
+    nf = hp.n_feat
+    sum_sq = np.zeros(nf)
     for r0 in range(0, R, block_rows):
         F = features(P, G, acc, hp, slice(r0, min(r0 + block_rows, R)))
-        sum_sq += (F * F).reshape(-1, N_FEATURES).sum(axis=0)
+        sum_sq += (F * F).reshape(-1, nf).sum(axis=0)
     scales = feature_scales(sum_sq, n, hp)
     T = time_features(t, hp)
     sub = Accumulators(acc.m[:, rows], acc.v[rows], acc.r[:, rows], acc.c, acc.rbar)
@@ -345,7 +356,9 @@ def step(params: Sequence[np.ndarray], grads: Sequence[np.ndarray], states: Sequ
     ``t`` is the 1-based index of this step.  Returns (new params, new states).
     """
     hp32 = hp.as_f32()
-    mlp = unpack_mlp(mlp_flat, hp32.n_time)
+    if hp32.n_feat not in FEATURE_SETS:
+        raise ValueError(f"n_feat must be one of {FEATURE_SETS}")
+    mlp = unpack_mlp(mlp_flat, hp32.n_time, hp32.n_feat)
     outs_p, outs_s = [], []
     for p, g, s in zip(params, grads, states):
         pn, sn, _ = step_tensor(p, g, s, t, mlp, hp32, **kw)
