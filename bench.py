@@ -19,7 +19,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-FLOP_PER_ELEM = 2 * (28 * 32 + 32 * 32 + 32 * 2)   # MLP with step features folded into the bias
+
+def flop_per_elem(n_feat: int = 28) -> int:
+    """MLP FLOP per element with the step features folded into the first bias."""
+    return 2 * (n_feat * 32 + 32 * 32 + 32 * 2)
+
+
 PEAK_FP32_MFMA_TFLOPS = 157.3                      # MI355X dense fp32 matrix
 PEAK_FP32_VALU_TFLOPS = 78.6                       # 256 CU x 4 SIMD x 16 lanes x 2 x 2.4 GHz (no packed fp32)
 PEAK_HBM_GBS = 8000.0
@@ -97,6 +102,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="vit_b16")
     ap.add_argument("--impl", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--n-feat", type=int, default=28, choices=(28, 19),
+                    help="per-element features: 28 (small_fc_lopt) or 19 (the VeLO-shaped variant)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--peaks", action="store_true",
                     help="also run the machine-figure microbenchmark and include it as measured_peaks")
@@ -122,8 +129,8 @@ def main():
     for i, t in enumerate(w.tensors):
         params.append(torch.from_numpy(W.param_init(w, i).reshape(t.shape)).to(dev))
         grads.append(torch.from_numpy(W.grad_at(w, i, 1).reshape(t.shape)).to(dev))
-    cfg = L.config_from(mlp_impl=impl)
-    opt = L.LOpt(params, W.mlp_weights(), cfg)
+    cfg = L.config_from(mlp_impl=impl, n_feat=args.n_feat)
+    opt = L.LOpt(params, W.mlp_weights(n_feat=args.n_feat), cfg)
     if w.prewarm_std is not None:
         for i in range(len(w.tensors)):
             st = W.state_init(w, i)
@@ -174,7 +181,8 @@ def main():
     # algorithmic bytes of the two streaming kernels: g (4 B); g, p, m1..3, v (24 B, 1-D + 12 B)
     stream_bytes = {"k_rowcol_sumsq": 4 * n, "k_stats": 24 * n + 12 * n_vec}
     apply_ms = float(kern_ms[4])
-    achieved = FLOP_PER_ELEM * n / (apply_ms * 1e-3) / 1e12
+    fpe = flop_per_elem(args.n_feat)
+    achieved = fpe * n / (apply_ms * 1e-3) / 1e12
     use_mfma = impl != L.LOPT_MLP_VALU
     peak = PEAK_FP32_MFMA_TFLOPS if use_mfma else PEAK_FP32_VALU_TFLOPS
     out = {
@@ -187,17 +195,19 @@ def main():
         "ms_per_step": round(ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": round(value / PAGE_VIT_GPARAMS_PER_S, 3) if w.key == "vit_b16" else None,
+        "vs_baseline": (round(value / PAGE_VIT_GPARAMS_PER_S, 3)
+                        if w.key == "vit_b16" and args.n_feat == 28 else None),
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"{w.key}: {w.description}", "n_params": n, "n_tensors": len(w.tensors),
-                   "mlp_impl": "mfma" if use_mfma else "valu", "state": "zero-init, gradients fixed"},
+                   "mlp_impl": "mfma" if use_mfma else "valu", "state": "zero-init, gradients fixed",
+                   "variant": "small_fc_lopt" if args.n_feat == 28 else "VeLO-shaped (19 features, 30 inputs)"},
         "roofline": {"bound": "mfma" if use_mfma else "alu", "kernel": "k_apply",
                      "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4),
-                     "traffic": committed_traffic(w.key) if use_mfma else None,
-                     "flop_per_elem": FLOP_PER_ELEM, "elems_per_launch": n},
-        "step_frac_fp32_peak": round(FLOP_PER_ELEM * n / (ms * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4),
+                     "traffic": committed_traffic(w.key) if use_mfma and args.n_feat == 28 else None,
+                     "flop_per_elem": fpe, "elems_per_launch": n},
+        "step_frac_fp32_peak": round(fpe * n / (ms * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4),
         "kernels_ms": {name: round(float(t), 4) for name, t in zip(L.KERNEL_NAMES, kern_ms)},
         "step_ms_median": round(float(np.median(per_step)), 4),
         "step_ms_min": round(float(per_step.min()), 4),

@@ -18,6 +18,9 @@
  *     rho_k = (r_k[i] c_k[j] / mean_i r_k)^(-1/2)
  *   each feature divided by sqrt(mean over the tensor of its square + eps_norm)
  *   x = [28 normalised features, tanh(t / tau_q) for q < n_time]
+ *   (the VeLO-shaped variant, n_feat = 19, feeds only the first 19 features:
+ *   the same page gives VeLO a feature width of about 30 and the same two
+ *   kernels; which features is this library's reading)
  *   (dir, mag) = W3 relu(W2 relu(W1 x + b1) + b2) + b3
  *   u = dir exp(mag exp_mult) step_mult;  p <- p - lr u - lr wd p
  *
@@ -35,7 +38,8 @@
 extern "C" {
 #endif
 
-#define LOPT_N_FEATURES 28 /* per-element features, each normalised per tensor */
+#define LOPT_N_FEATURES 28    /* per-element features, each normalised per tensor */
+#define LOPT_VELO_FEATURES 19 /* per-element features of the VeLO-shaped variant */
 #define LOPT_HIDDEN 32     /* width of both hidden layers */
 #define LOPT_MAX_TIME 11   /* maximum number of step (time) features */
 
@@ -70,6 +74,8 @@ typedef struct lopt_config {
   int32_t n_time;     /* number of tanh(t/tau) step features, 0..11, default 11 */
   float timescales[LOPT_MAX_TIME]; /* tau_q, default 1,3,10,30,100,300,1e3,3e3,1e4,3e4,1e5 */
   int32_t mlp_impl;   /* lopt_mlp_impl */
+  int32_t n_feat;     /* per-element MLP inputs: LOPT_N_FEATURES (small_fc_lopt,
+                         default) or LOPT_VELO_FEATURES (features 0..18 only) */
 } lopt_config;
 
 /* One parameter tensor.  All pointers are device pointers (hipMalloc / torch),
@@ -100,14 +106,14 @@ typedef struct lopt_handle lopt_handle;
 /* Fills *out with the default hyperparameters.  Errors: out == NULL. */
 lopt_status lopt_default_config(lopt_config* out);
 
-/* Number of floats in the packed MLP weights for n_time step features:
- * W1[32][28+n_time], b1[32], W2[32][32], b2[32], W3[2][32], b3[2]
- * (row-major, out x in).  2402 for n_time = 11.  Returns 0 if n_time is out
- * of range. */
-size_t lopt_mlp_floats(int32_t n_time);
+/* Number of floats in the packed MLP weights for n_feat per-element features
+ * and n_time step features: W1[32][n_feat+n_time], b1[32], W2[32][32],
+ * b2[32], W3[2][32], b3[2] (row-major, out x in).  2402 for (28, 11), 2114
+ * for (19, 11).  Returns 0 if n_feat or n_time is out of range. */
+size_t lopt_mlp_floats(int32_t n_feat, int32_t n_time);
 
 /* Creates a handle on the current HIP device.  cfg: hyperparameters (copied);
- * mlp_host: host pointer to lopt_mlp_floats(cfg->n_time) floats (copied to
+ * mlp_host: host pointer to lopt_mlp_floats(cfg->n_feat, cfg->n_time) floats (copied to
  * device memory that the handle owns).  The call is synchronous.
  * Errors: null pointers or out-of-range config -> INVALID_ARGUMENT;
  * allocation/copy failure -> HIP.  *out is set only on success. */
@@ -169,8 +175,8 @@ lopt_status lopt_set_step(lopt_handle* h, int64_t t);
  * optimizer composes with torch LR schedulers and decoupled weight decay).
  * Host-side only: steps already queued keep the values they were launched
  * with; a step captured in a HIP graph keeps the values of its capture.
- * Errors: invalid config, or n_time different from lopt_create's ->
- * INVALID_ARGUMENT (the handle keeps its previous config). */
+ * Errors: invalid config, or n_feat or n_time different from lopt_create's
+ * -> INVALID_ARGUMENT (the handle keeps its previous config). */
 lopt_status lopt_set_config(lopt_handle* h, const lopt_config* cfg);
 
 /* Kernels of one step, in launch order. */

@@ -102,6 +102,8 @@ void validate_config(const lopt_config* c) {
       fail(LOPT_ERR_INVALID_ARGUMENT, "timescales must be finite and > 0");
   if (c->mlp_impl < LOPT_MLP_AUTO || c->mlp_impl > LOPT_MLP_MFMA)
     fail(LOPT_ERR_INVALID_ARGUMENT, "unknown mlp_impl");
+  if (c->n_feat != LOPT_N_FEATURES && c->n_feat != LOPT_VELO_FEATURES)
+    fail(LOPT_ERR_INVALID_ARGUMENT, "n_feat must be 28 or 19");
 }
 
 struct Range {
@@ -358,6 +360,7 @@ StepParams make_params(const lopt_handle* h) {
   for (int k = 0; k < 3; ++k) normal = normal && p.omb_f[k] * c.eps_f >= 2.0f * FLT_MIN;
   p.rsq_normal = normal ? 1 : 0;
   p.n_time = c.n_time;
+  p.n_feat = c.n_feat;
   for (int q = 0; q < kMaxTime; ++q) p.timescales[q] = q < c.n_time ? c.timescales[q] : 1.f;
   return p;
 }
@@ -406,13 +409,15 @@ lopt_status lopt_default_config(lopt_config* out) {
     const float ts[LOPT_MAX_TIME] = {1.f, 3.f, 10.f, 30.f, 100.f, 300.f, 1e3f, 3e3f, 1e4f, 3e4f, 1e5f};
     std::memcpy(c.timescales, ts, sizeof(ts));
     c.mlp_impl = LOPT_MLP_AUTO;
+    c.n_feat = LOPT_N_FEATURES;
     *out = c;
   });
 }
 
-size_t lopt_mlp_floats(int32_t n_time) {
+size_t lopt_mlp_floats(int32_t n_feat, int32_t n_time) {
   if (n_time < 0 || n_time > LOPT_MAX_TIME) return 0;
-  const size_t din = size_t(kNF + n_time);
+  if (n_feat != LOPT_N_FEATURES && n_feat != LOPT_VELO_FEATURES) return 0;
+  const size_t din = size_t(n_feat + n_time);
   return size_t(kH) * din + kH + size_t(kH) * kH + kH + 2 * kH + 2;
 }
 
@@ -426,7 +431,7 @@ lopt_status lopt_create(const lopt_config* cfg, const float* mlp_host, lopt_hand
     if (!out) fail(LOPT_ERR_INVALID_ARGUMENT, "out is NULL");
     if (!mlp_host) fail(LOPT_ERR_INVALID_ARGUMENT, "mlp_host is NULL");
     validate_config(cfg);
-    const size_t nw = lopt_mlp_floats(cfg->n_time);
+    const size_t nw = lopt_mlp_floats(cfg->n_feat, cfg->n_time);
     for (size_t i = 0; i < nw; ++i)
       if (!std::isfinite(mlp_host[i])) fail(LOPT_ERR_INVALID_ARGUMENT, "MLP weights must be finite");
     auto* h = new lopt_handle();
@@ -530,8 +535,8 @@ lopt_status lopt_set_config(lopt_handle* h, const lopt_config* cfg) {
   return guarded([&] {
     if (!h) fail(LOPT_ERR_INVALID_ARGUMENT, "handle is NULL");
     validate_config(cfg);
-    if (cfg->n_time != h->cfg.n_time)
-      fail(LOPT_ERR_INVALID_ARGUMENT, "n_time is fixed by the MLP weights given to lopt_create");
+    if (cfg->n_time != h->cfg.n_time || cfg->n_feat != h->cfg.n_feat)
+      fail(LOPT_ERR_INVALID_ARGUMENT, "n_feat and n_time are fixed by the MLP weights given to lopt_create");
     h->cfg = *cfg;
   });
 }

@@ -15,7 +15,7 @@ namespace lopt {
 // k_apply_valu: the page's kernel 2 with the MLP on the vector ALU.  Weights
 // are read through uniform (scalar) loads from the packed copy, so every FMA
 // takes its weight from a scalar register.
-template <bool VEC, bool NORMAL>
+template <bool VEC, bool NORMAL, int NF>
 __device__ __forceinline__ void apply_valu_body(const StepCtx& c, const StepParams& hp, const Chunk& ch,
                                                 const TensorDesc& d, const float* g) {
   const Streams s = make_streams(d, g, c.ws, ch);
@@ -26,16 +26,16 @@ __device__ __forceinline__ void apply_valu_body(const StepCtx& c, const StepPara
     load_elem<VEC>(s, e, x);
     const float p_old = x.p;
     float F[kNF], cn[3];
-    build_features<VEC, NORMAL>(hp, x, F, cn);
+    build_features<VEC, NORMAL, NF>(hp, x, F, cn);
     store_state<VEC>(s, e, x, cn);
 #pragma unroll
-    for (int f = 0; f < kNF; ++f) F[f] *= sc[f];
+    for (int f = 0; f < NF; ++f) F[f] *= sc[f];
     float h1[kH];
 #pragma unroll
     for (int o = 0; o < kH; ++o) {
       float a = pk[kPkB1 + o];
 #pragma unroll
-      for (int f = 0; f < kNF; ++f) a = fmaf(pk[kPkW1 + o * kNF + f], F[f], a);
+      for (int f = 0; f < NF; ++f) a = fmaf(pk[kPkW1 + o * kNF + f], F[f], a);
       h1[o] = fmaxf(a, 0.f);
     }
     float dir = pk[kPkB3], mag = pk[kPkB3 + 1];
@@ -57,13 +57,10 @@ __global__ __launch_bounds__(kBlock) void k_apply_valu(StepCtx c, StepParams hp)
   TensorDesc d;
   const float* g;
   load_chunk(c, blockIdx.x, ch, d, g);
-  if (d.vec) {
-    if (hp.rsq_normal) apply_valu_body<true, true>(c, hp, ch, d, g);
-    else apply_valu_body<true, false>(c, hp, ch, d, g);
-  } else {
-    if (hp.rsq_normal) apply_valu_body<false, true>(c, hp, ch, d, g);
-    else apply_valu_body<false, false>(c, hp, ch, d, g);
-  }
+  dispatch_variant(d.vec, hp, [&](auto v) {
+    using V = decltype(v);
+    apply_valu_body<V::vec, V::normal, V::nf>(c, hp, ch, d, g);
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -73,7 +70,8 @@ __global__ __launch_bounds__(kBlock) void k_apply_valu(StepCtx c, StepParams hp)
 // 32-element GEMM chains per wave, v_mfma_f32_32x32x2_f32 with the hidden
 // units as M (weights = A operand, register resident), the elements as N and
 // the features as K:
-//   layer 1: 14 K-steps of two features.  v_permlane32_swap of the feature
+//   layer 1: 14 K-steps of two features (10 for the 19-feature variant, the
+//     last padded with a zero).  v_permlane32_swap of the feature
 //     pair (2s, 2s+1) gives, in one instruction, the B operands of both
 //     halves: [F_2s of elements 0..31 | F_2s+1 of elements 0..31] and
 //     [F_2s of elements 32..63 | F_2s+1 of elements 32..63].
@@ -96,7 +94,7 @@ __device__ __forceinline__ void swap_halves(float x, float y, float& lo, float& 
   hi = __uint_as_float(r[1]);
 }
 
-template <bool VEC, bool NORMAL>
+template <bool VEC, bool NORMAL, int NF>
 __device__ __forceinline__ void apply_mfma_body(const StepCtx& c, const StepParams& hp, const Chunk& ch,
                                                 const TensorDesc& d, const float* g) {
   const int lane = threadIdx.x & 63;
@@ -107,10 +105,14 @@ __device__ __forceinline__ void apply_mfma_body(const StepCtx& c, const StepPara
   const float* __restrict__ pk = c.packed;
   const float* __restrict__ sc = c.scales + size_t(ch.tensor) * kStatStride;
 
-  float a1[kNF / 2];   // W1[row][2s + half] * s_(2s + half)
+  constexpr int KS = (NF + 1) / 2;  // layer-1 K-steps (an odd NF pads with a zero feature)
+  float a1[KS];        // W1[row][2s + half] * s_(2s + half)
   float a2[kH / 2];    // W2[row][acc_row(s, half)]
 #pragma unroll
-  for (int q = 0; q < kNF / 2; ++q) a1[q] = pk[kPkW1 + row * kNF + 2 * q + half] * sc[2 * q + half];
+  for (int q = 0; q < KS; ++q) {
+    const int f = 2 * q + half;
+    a1[q] = f < NF ? pk[kPkW1 + row * kNF + f] * sc[f] : 0.f;
+  }
 #pragma unroll
   for (int q = 0; q < 16; ++q) a2[q] = pk[kPkW2 + row * kH + acc_row(q, half)];
 
@@ -135,7 +137,8 @@ __device__ __forceinline__ void apply_mfma_body(const StepCtx& c, const StepPara
     load_elem<VEC>(s, valid ? e : ch.e0, x);
     const float p_old = x.p;
     float F[kNF], cn[3];
-    build_features<VEC, NORMAL>(hp, x, F, cn);
+    build_features<VEC, NORMAL, NF>(hp, x, F, cn);
+    if (NF & 1) F[NF] = 0.f;
     // the accumulators are final here: storing them now frees their registers
     // (and the copies the lane swaps below would need) during the MLP
     if (valid) store_state<VEC>(s, e, x, cn);
@@ -152,7 +155,7 @@ __device__ __forceinline__ void apply_mfma_body(const StepCtx& c, const StepPara
     // (measured: 5 % fewer cycles than without).
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int q = 0; q < kNF / 2; ++q) {
+    for (int q = 0; q < KS; ++q) {
       float bA, bB;
       swap_halves(F[2 * q], F[2 * q + 1], bA, bB);
       const float aq = a1[q];
@@ -211,13 +214,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   TensorDesc d;
   const float* g;
   load_chunk(c, blockIdx.x, ch, d, g);
-  if (d.vec) {
-    if (hp.rsq_normal) apply_mfma_body<true, true>(c, hp, ch, d, g);
-    else apply_mfma_body<true, false>(c, hp, ch, d, g);
-  } else {
-    if (hp.rsq_normal) apply_mfma_body<false, true>(c, hp, ch, d, g);
-    else apply_mfma_body<false, false>(c, hp, ch, d, g);
-  }
+  dispatch_variant(d.vec, hp, [&](auto v) {
+    using V = decltype(v);
+    apply_mfma_body<V::vec, V::normal, V::nf>(c, hp, ch, d, g);
+  });
 }
 
 hipError_t launch_apply(const StepCtx& c, const StepParams& p, hipStream_t s) {

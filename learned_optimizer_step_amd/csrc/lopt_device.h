@@ -164,7 +164,41 @@ __device__ __forceinline__ float rsq(float x) {
   return NORMAL ? __builtin_amdgcn_rsqf(x) : rsqrtf(x);
 }
 
-template <bool VEC, bool NORMAL>
+// Compile-time variant of a chunk's per-element code: tensor kind (1-D or
+// factored 2-D), 1/sqrt mode, and number of per-element features (kNF for
+// small_fc_lopt, kVeloNF for the VeLO-shaped variant, which stops at F18).
+template <bool V, bool N, int F>
+struct Variant {
+  static constexpr bool vec = V;
+  static constexpr bool normal = N;
+  static constexpr int nf = F;
+};
+
+// Calls body(Variant<...>{}) for the chunk's tensor kind and the step's 1/sqrt
+// mode and feature count (all uniform over the workgroup).
+template <class Body>
+__device__ __forceinline__ void dispatch_variant(bool vec, const StepParams& hp, Body&& body) {
+  if (hp.n_feat == kNF) {
+    if (vec) {
+      if (hp.rsq_normal) body(Variant<true, true, kNF>{});
+      else body(Variant<true, false, kNF>{});
+    } else {
+      if (hp.rsq_normal) body(Variant<false, true, kNF>{});
+      else body(Variant<false, false, kNF>{});
+    }
+  } else {
+    if (vec) {
+      if (hp.rsq_normal) body(Variant<true, true, kVeloNF>{});
+      else body(Variant<true, false, kVeloNF>{});
+    } else {
+      if (hp.rsq_normal) body(Variant<false, true, kVeloNF>{});
+      else body(Variant<false, false, kVeloNF>{});
+    }
+  }
+}
+
+// Builds F[0..NF) (NF = kNF or kVeloNF; F[NF..kNF) are left unset).
+template <bool VEC, bool NORMAL, int NF>
 __device__ __forceinline__ void build_features(const StepParams& hp, Elem& x, float F[kNF], float cn[3]) {
   const float g = x.g;
   const float g2 = g * g;
@@ -196,10 +230,12 @@ __device__ __forceinline__ void build_features(const StepParams& hp, Elem& x, fl
     F[13 + k] = x.rq[k];
     F[16 + k] = cq[k];
   }
+  if (NF == kNF) {
 #pragma unroll
-  for (int a = 0; a < 3; ++a)
+    for (int a = 0; a < 3; ++a)
 #pragma unroll
-    for (int k = 0; k < 3; ++k) F[19 + 3 * a + k] = x.m[a] * rho[k];
+      for (int k = 0; k < 3; ++k) F[19 + 3 * a + k] = x.m[a] * rho[k];
+  }
 }
 
 // Loads the inputs of element e of tensor d.

@@ -10,7 +10,8 @@
 namespace lopt {
 
 constexpr int kBlock = 256;        // threads per workgroup in every kernel (4 wave64s)
-constexpr int kNF = 28;            // per-element features
+constexpr int kNF = 28;            // per-element features of small_fc_lopt
+constexpr int kVeloNF = 19;        // the VeLO-shaped variant feeds features 0..18
 constexpr int kH = 32;             // hidden width
 constexpr int kMaxTime = 11;
 constexpr int kStatStride = 32;    // floats per stats partial / per-tensor scale record
@@ -30,7 +31,8 @@ constexpr int kMinChunkElems = 256;
 constexpr int kTargetChunks = 4096;
 
 // Packed MLP in the workspace, written once per step by the finalize kernel:
-// W1 feature columns [32][28], b1 with the step features folded in [32],
+// W1 feature columns [32][28] (columns >= n_feat zero), b1 with the step
+// features folded in [32],
 // W2 [32][32], b2 [32], W3 [2][32], b3 [2].
 constexpr int kPkW1 = 0;
 constexpr int kPkB1 = kPkW1 + kH * kNF;
@@ -106,6 +108,7 @@ struct StepParams {
   // the bare hardware reciprocal square root, which only differs from rsqrtf
   // on subnormal arguments.
   int32_t rsq_normal;
+  int32_t n_feat;            // kNF or kVeloNF
   int32_t n_time;
   float timescales[kMaxTime];
 };

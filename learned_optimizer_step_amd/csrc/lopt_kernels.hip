@@ -235,17 +235,17 @@ __global__ __launch_bounds__(kBlock) void k_moving_avg(StepCtx c, StepParams hp)
 // k_stats: per-chunk sums of the squares of the 28 features (the page's
 // kernel 1).  Accumulators are updated in registers only; the apply kernel
 // recomputes them from the same inputs.
-template <bool VEC, bool NORMAL>
+template <bool VEC, bool NORMAL, int NF>
 __device__ __forceinline__ void stats_accumulate(const StepParams& hp, Elem& x, float acc[kNF]) {
   float F[kNF], cn[3];
-  build_features<VEC, NORMAL>(hp, x, F, cn);
+  build_features<VEC, NORMAL, NF>(hp, x, F, cn);
 #pragma unroll
-  for (int f = 0; f < kNF; ++f) acc[f] = fmaf(F[f], F[f], acc[f]);
+  for (int f = 0; f < NF; ++f) acc[f] = fmaf(F[f], F[f], acc[f]);
 }
 
 // Four elements per thread per iteration, their loads issued together, so
 // each thread keeps ~100 bytes of HBM reads in flight.
-template <bool VEC, bool NORMAL>
+template <bool VEC, bool NORMAL, int NF>
 __device__ __forceinline__ void stats_body(const StepCtx& c, const StepParams& hp, const Chunk& ch,
                                            const TensorDesc& d, const float* g, float acc[kNF]) {
   const Streams st = make_streams(d, g, c.ws, ch);
@@ -255,12 +255,12 @@ __device__ __forceinline__ void stats_body(const StepCtx& c, const StepParams& h
 #pragma unroll
     for (int u = 0; u < 4; ++u) load_elem<VEC>(st, e + u * kBlock, x[u]);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) stats_accumulate<VEC, NORMAL>(hp, x[u], acc);
+    for (int u = 0; u < 4; ++u) stats_accumulate<VEC, NORMAL, NF>(hp, x[u], acc);
   }
   for (; e < ch.e1; e += kBlock) {
     Elem x;
     load_elem<VEC>(st, e, x);
-    stats_accumulate<VEC, NORMAL>(hp, x, acc);
+    stats_accumulate<VEC, NORMAL, NF>(hp, x, acc);
   }
 }
 
@@ -273,13 +273,10 @@ __global__ __launch_bounds__(kBlock) void k_stats(StepCtx c, StepParams hp) {
   float acc[kNF];
 #pragma unroll
   for (int f = 0; f < kNF; ++f) acc[f] = 0.f;
-  if (d.vec) {
-    if (hp.rsq_normal) stats_body<true, true>(c, hp, ch, d, g, acc);
-    else stats_body<true, false>(c, hp, ch, d, g, acc);
-  } else {
-    if (hp.rsq_normal) stats_body<false, true>(c, hp, ch, d, g, acc);
-    else stats_body<false, false>(c, hp, ch, d, g, acc);
-  }
+  dispatch_variant(d.vec, hp, [&](auto v) {
+    using V = decltype(v);
+    stats_body<V::vec, V::normal, V::nf>(c, hp, ch, d, g, acc);
+  });
   const int w = threadIdx.x >> 6;
 #pragma unroll
   for (int f = 0; f < kNF; ++f) {
@@ -329,7 +326,8 @@ __global__ __launch_bounds__(kBlock) void k_finalize(StepCtx c, StepParams hp) {
     const int k = rho_feature(f);
     const float rb = k < 0 ? 1.0f : sr[k];
     const float S = ((lds[0][f] + lds[1][f]) + (lds[2][f] + lds[3][f])) * (rb * rb);
-    sc[f] = rb / sqrtf(S / float(d.n) + hp.eps_norm);
+    // features the variant does not feed get scale 0 (their weights are 0 too)
+    sc[f] = f < hp.n_feat ? rb / sqrtf(S / float(d.n) + hp.eps_norm) : 0.f;
   } else if (threadIdx.x < kNF + 3) {
     const int k = threadIdx.x - kNF;
     sc[kNF + k] = sr[k];
@@ -341,7 +339,8 @@ __global__ __launch_bounds__(kBlock) void k_finalize(StepCtx c, StepParams hp) {
     // thread 0 advances it after the barrier below.
     const int64_t step = *c.step + 1;
     const float tf = float(step);
-    const int din = kNF + hp.n_time;
+    const int nf = hp.n_feat;
+    const int din = nf + hp.n_time;
     const float* W1 = c.mlp;
     const float* b1 = W1 + kH * din;
     const float* W2 = b1 + kH;
@@ -351,12 +350,12 @@ __global__ __launch_bounds__(kBlock) void k_finalize(StepCtx c, StepParams hp) {
     float* pk = c.packed;
     for (int q = threadIdx.x; q < kH * kNF; q += kBlock) {
       const int o = q / kNF, f = q - o * kNF;
-      pk[kPkW1 + q] = W1[o * din + f];
+      pk[kPkW1 + q] = f < nf ? W1[o * din + f] : 0.f;
     }
     if (threadIdx.x < kH) {
       const int o = threadIdx.x;
       float b = b1[o];
-      for (int s = 0; s < hp.n_time; ++s) b = fmaf(W1[o * din + kNF + s], tanhf(tf / hp.timescales[s]), b);
+      for (int s = 0; s < hp.n_time; ++s) b = fmaf(W1[o * din + nf + s], tanhf(tf / hp.timescales[s]), b);
       pk[kPkB1 + o] = b;
       pk[kPkB2 + o] = b2[o];
       pk[kPkW3 + o] = W3[o];

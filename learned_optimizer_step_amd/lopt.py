@@ -31,6 +31,8 @@ LOPT_MLP_AUTO = 0
 LOPT_MLP_VALU = 1
 LOPT_MLP_MFMA = 2
 LOPT_MAX_TIME = 11
+LOPT_N_FEATURES = 28     # small_fc_lopt's per-element features
+LOPT_VELO_FEATURES = 19  # the VeLO-shaped variant's (features 0..18)
 
 
 class LoptError(RuntimeError):
@@ -46,7 +48,7 @@ class lopt_config(ctypes.Structure):
                 ("exp_mult", ctypes.c_float), ("step_mult", ctypes.c_float),
                 ("lr", ctypes.c_float), ("weight_decay", ctypes.c_float),
                 ("n_time", ctypes.c_int32), ("timescales", ctypes.c_float * LOPT_MAX_TIME),
-                ("mlp_impl", ctypes.c_int32)]
+                ("mlp_impl", ctypes.c_int32), ("n_feat", ctypes.c_int32)]
 
 
 class lopt_tensor(ctypes.Structure):
@@ -73,7 +75,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     st = ctypes.c_int
     sig = {
         "lopt_default_config": (st, [ctypes.POINTER(lopt_config)]),
-        "lopt_mlp_floats": (ctypes.c_size_t, [ctypes.c_int32]),
+        "lopt_mlp_floats": (ctypes.c_size_t, [ctypes.c_int32, ctypes.c_int32]),
         "lopt_create": (st, [ctypes.POINTER(lopt_config), ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)]),
         "lopt_destroy": (None, [ctypes.c_void_p]),
         "lopt_state_floats": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64]),
@@ -112,8 +114,8 @@ def lopt_default_config() -> lopt_config:
     return c
 
 
-def lopt_mlp_floats(n_time: int) -> int:
-    return int(load_library().lopt_mlp_floats(n_time))
+def lopt_mlp_floats(n_feat: int, n_time: int) -> int:
+    return int(load_library().lopt_mlp_floats(n_feat, n_time))
 
 
 def lopt_state_floats(rows: int, cols: int) -> int:
@@ -122,8 +124,9 @@ def lopt_state_floats(rows: int, cols: int) -> int:
 
 def lopt_create(cfg: lopt_config, mlp_host: np.ndarray) -> ctypes.c_void_p:
     w = np.ascontiguousarray(mlp_host, dtype=np.float32)
-    if w.size != lopt_mlp_floats(cfg.n_time):
-        raise ValueError(f"expected {lopt_mlp_floats(cfg.n_time)} MLP floats, got {w.size}")
+    nw = lopt_mlp_floats(cfg.n_feat, cfg.n_time)
+    if w.size != nw:
+        raise ValueError(f"expected {nw} MLP floats, got {w.size}")
     h = ctypes.c_void_p()
     _check(load_library().lopt_create(ctypes.byref(cfg), w.ctypes.data_as(ctypes.c_void_p), ctypes.byref(h)))
     return h

@@ -26,7 +26,7 @@ def hyper_from_cfg(cfg) -> oracle.Hyper:
                         eps_v=cfg.eps_v, eps_f=cfg.eps_f, eps_norm=cfg.eps_norm,
                         exp_mult=cfg.exp_mult, step_mult=cfg.step_mult, lr=cfg.lr,
                         weight_decay=cfg.weight_decay, n_time=cfg.n_time,
-                        timescales=tuple(cfg.timescales)[: cfg.n_time])
+                        timescales=tuple(cfg.timescales)[: cfg.n_time], n_feat=cfg.n_feat)
 
 
 def to_matrix_state(st: dict) -> dict:
@@ -124,7 +124,7 @@ def parity_one_step_rows(w: W.Workload, mlp: np.ndarray, cfg, torch, picks) -> L
     got = {i: run.fetch(i) for i in picks}
     run.close()
     hp = hyper_from_cfg(cfg).as_f32()
-    m = oracle.unpack_mlp(mlp, hp.n_time)
+    m = oracle.unpack_mlp(mlp, hp.n_time, hp.n_feat)
     errs = []
     for i, rows in picks.items():
         t = w.tensors[i]

@@ -43,15 +43,18 @@ def test_default_config_values(lib):
     assert c.eps_norm == pytest.approx(1e-30)
     assert c.exp_mult == pytest.approx(1e-3) and c.step_mult == pytest.approx(1e-3)
     assert c.lr == 1.0 and c.weight_decay == 0.0 and c.n_time == 11
+    assert c.n_feat == 28 and c.mlp_impl == L.LOPT_MLP_AUTO   # last field: the struct layouts agree
     assert list(c.timescales) == pytest.approx([1, 3, 10, 30, 100, 300, 1e3, 3e3, 1e4, 3e4, 1e5])
     assert lib.lopt_default_config(None) == L.LOPT_ERR_INVALID_ARGUMENT
     assert "NULL" in L.lopt_last_error()
 
 
 def test_sizes(lib):
-    assert L.lopt_mlp_floats(11) == 2402
-    assert L.lopt_mlp_floats(0) == 32 * 28 + 32 + 1024 + 32 + 64 + 2
-    assert L.lopt_mlp_floats(12) == 0 and L.lopt_mlp_floats(-1) == 0
+    assert L.lopt_mlp_floats(28, 11) == 2402
+    assert L.lopt_mlp_floats(28, 0) == 32 * 28 + 32 + 1024 + 32 + 64 + 2
+    assert L.lopt_mlp_floats(19, 11) == 32 * 30 + 32 + 1024 + 32 + 64 + 2 == 2114
+    assert L.lopt_mlp_floats(28, 12) == 0 and L.lopt_mlp_floats(28, -1) == 0
+    assert L.lopt_mlp_floats(20, 11) == 0 and L.lopt_mlp_floats(0, 11) == 0
     assert L.lopt_state_floats(4, 5) == 4 * 20 + 3 * 9
     assert L.lopt_state_floats(1, 7) == 4 * 7 + 3 * 8
     assert L.lopt_state_floats(0, 3) == 0
@@ -136,6 +139,9 @@ def test_create_rejects_bad_config_without_device(lib):
     assert lib.lopt_create(ctypes.byref(c), w, ctypes.byref(h)) == L.LOPT_ERR_INVALID_ARGUMENT
     c = L.config_from(timescales=[1.0, 0.0])
     assert lib.lopt_create(ctypes.byref(c), w, ctypes.byref(h)) == L.LOPT_ERR_INVALID_ARGUMENT
+    c = L.config_from(n_feat=20)
+    assert lib.lopt_create(ctypes.byref(c), w, ctypes.byref(h)) == L.LOPT_ERR_INVALID_ARGUMENT
+    assert "n_feat" in L.lopt_last_error()
     c = L.lopt_default_config()
     assert lib.lopt_create(ctypes.byref(c), None, ctypes.byref(h)) == L.LOPT_ERR_INVALID_ARGUMENT
     assert lib.lopt_create(None, w, ctypes.byref(h)) == L.LOPT_ERR_INVALID_ARGUMENT

@@ -278,3 +278,43 @@ def test_gpt2_355m_one_step_sampled():
              names.index("h.11.mlp.c_fc.bias"): None,
              names.index("ln_f.weight"): None}
     check(parity_one_step_rows(w, mlp(), L.config_from(), torch, picks))
+
+
+# ----------------------------------------------------------------- VeLO-shaped variant
+VNF = L.LOPT_VELO_FEATURES
+
+
+def vmlp(n_time=11, bias_std=0.1):
+    return W.mlp_weights(n_time, bias_std=bias_std, n_feat=VNF)
+
+
+@pytest.mark.parametrize("impl", IMPLS)
+def test_velo_shaped_edges_and_256_ten_steps(impl):
+    w = W.custom_workload("velo_edges", EDGE_SHAPES + [(256, 256)], grad_std=1e-2, steps=10, wid=110)
+    check(parity(w, vmlp(), L.config_from(mlp_impl=impl, n_feat=VNF), torch))
+
+
+@pytest.mark.parametrize("impl", IMPLS)
+def test_velo_shaped_vit_b16_subset_prewarmed_lr_wd(impl):
+    w = W.get_workload("vit_b16")
+    names = [t.name for t in w.tensors]
+    subset = [names.index(n) for n in ("pos_embed", "blocks.3.qkv.weight", "blocks.3.qkv.bias", "head")]
+    cfg = L.config_from(mlp_impl=impl, n_feat=VNF, lr=0.8, weight_decay=0.02)
+    check(parity(w, vmlp(), cfg, torch, steps=3, subset=subset))
+
+
+def test_velo_shaped_one_step_sampled_llama_rows():
+    w = W.get_workload("llama1b")
+    names = [t.name for t in w.tensors]
+    picks = {names.index("layers.7.gate"): sample_rows(2048, 16, 11), names.index("layers.7.mlp_norm"): None}
+    check(parity_one_step_rows(w, vmlp(), L.config_from(n_feat=VNF), torch, picks))
+
+
+def test_set_config_keeps_the_feature_count():
+    p = torch.zeros(4, 4, device="cuda")
+    opt = L.LOpt([p], vmlp(), L.config_from(n_feat=VNF))
+    with pytest.raises(L.LoptError):
+        L.lopt_set_config(opt.handle, L.config_from(n_feat=L.LOPT_N_FEATURES))
+    with pytest.raises(ValueError):       # weights sized for the other variant
+        L.LOpt([p], mlp(), L.config_from(n_feat=VNF))
+    opt.close()
