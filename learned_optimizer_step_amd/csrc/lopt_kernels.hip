@@ -157,6 +157,21 @@ __global__ __launch_bounds__(kBlock) void k_rowcol_sumsq(StepCtx c) {
 }
 
 // ---------------------------------------------------------------------------
+// Compensated (Kahan) running sum: the moving-average kernel adds up to
+// thousands of similar positive partials per row or column in sequence (a
+// tensor with 2^31 elements has 8192 row blocks), where a plain fp32 sum would
+// drift by ~sqrt(count) roundings.  The device code is compiled without
+// reassociation, so the compensation is kept as written.
+struct KahanSum {
+  float s = 0.f, comp = 0.f;
+  __device__ __forceinline__ void add(float x) {
+    const float y = x - comp;
+    const float t = s + y;
+    comp = (t - s) - y;
+    s = t;
+  }
+};
+
 // k_moving_avg: r_k and c_k moving averages (written to the state), their
 // inverse square roots (workspace) and per-segment partial sums of r_k.
 __global__ __launch_bounds__(kBlock) void k_moving_avg(StepCtx c, StepParams hp) {
@@ -173,9 +188,9 @@ __global__ __launch_bounds__(kBlock) void k_moving_avg(StepCtx c, StepParams hp)
     const int i = sg.a + tid;
     float loc[3] = {0.f, 0.f, 0.f};
     if (i < sg.b) {
-      float s = 0.f;
-      for (int w = 0; w < d.ncw; ++w) s += ws[d.off_rowpart + size_t(w) * d.R + i];
-      const float mean = s / float(d.C);
+      KahanSum ks;
+      for (int w = 0; w < d.ncw; ++w) ks.add(ws[d.off_rowpart + size_t(w) * d.R + i]);
+      const float mean = ks.s / float(d.C);
       float q[3];
 #pragma unroll
       for (int k = 0; k < 3; ++k) {
@@ -197,13 +212,13 @@ __global__ __launch_bounds__(kBlock) void k_moving_avg(StepCtx c, StepParams hp)
     __shared__ float part[kColGroups][kSegCols1];
     const int jl = tid % kSegCols1, grp = tid / kSegCols1;
     const int j = sg.a + jl;
-    float s = 0.f;
+    KahanSum ks;
     if (j < sg.b)
-      for (int b = grp; b < d.nrb; b += kColGroups) s += ws[d.off_colpart + size_t(b) * d.C + j];
-    part[grp][jl] = s;
+      for (int b = grp; b < d.nrb; b += kColGroups) ks.add(ws[d.off_colpart + size_t(b) * d.C + j]);
+    part[grp][jl] = ks.s;
     __syncthreads();
     if (grp == 0 && j < sg.b) {
-      s = (part[0][jl] + part[1][jl]) + (part[2][jl] + part[3][jl]);
+      const float s = (part[0][jl] + part[1][jl]) + (part[2][jl] + part[3][jl]);
       const float mean = s / float(d.R);
       float q[3];
 #pragma unroll
@@ -215,9 +230,9 @@ __global__ __launch_bounds__(kBlock) void k_moving_avg(StepCtx c, StepParams hp)
       reinterpret_cast<float4*>(ws + d.off_cq)[j] = make_float4(q[0], q[1], q[2], 0.f);
     }
   } else {  // 1-D tensor: r_k is one value per tensor
-    float s = 0.f;
-    for (int w = tid; w < d.ncw; w += kBlock) s += ws[d.off_rowpart + w];
-    s = block_sum(s, red);
+    KahanSum ks;
+    for (int w = tid; w < d.ncw; w += kBlock) ks.add(ws[d.off_rowpart + w]);
+    const float s = block_sum(ks.s, red);
     if (tid == 0) {
       const float mean = s / float(d.C);
 #pragma unroll
