@@ -159,15 +159,17 @@ __global__ __launch_bounds__(kBlock) void k_rowcol_sumsq(StepCtx c) {
 // ---------------------------------------------------------------------------
 // Compensated (Kahan) running sum: the moving-average kernel adds up to
 // thousands of similar positive partials per row or column in sequence (a
-// tensor with 2^31 elements has 8192 row blocks), where a plain fp32 sum would
+// 2^31-element matrix has ~11,000 row blocks), where a plain fp32 sum would
 // drift by ~sqrt(count) roundings.  The device code is compiled without
-// reassociation, so the compensation is kept as written.
+// reassociation, so the compensation is kept as written.  Once the sum is
+// infinite the compensation stays 0, so an infinite partial gives an
+// infinite sum (as a plain sum would), not inf - inf = NaN.
 struct KahanSum {
   float s = 0.f, comp = 0.f;
   __device__ __forceinline__ void add(float x) {
     const float y = x - comp;
     const float t = s + y;
-    comp = (t - s) - y;
+    comp = __builtin_isfinite(t) ? (t - s) - y : 0.f;
     s = t;
   }
 };

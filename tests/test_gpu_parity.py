@@ -318,3 +318,46 @@ def test_set_config_keeps_the_feature_count():
     with pytest.raises(ValueError):       # weights sized for the other variant
         L.LOpt([p], mlp(), L.config_from(n_feat=VNF))
     opt.close()
+
+
+@pytest.mark.parametrize("impl", IMPLS)
+@pytest.mark.parametrize("bad", [float("nan"), float("inf")])
+def test_non_finite_gradient_stays_in_its_tensor(impl, bad):
+    # Reading R23: non-finite inputs are not checked.  One bad gradient element
+    # of tensor 0 must show up in exactly the accumulators the step definition
+    # routes it to (its m and v, its row's r, its column's c), equal to the
+    # oracle everywhere else; tensor 1 of the same step is untouched by it.
+    # The parameters of tensor 0 are not compared (its per-tensor statistics
+    # are non-finite; the ReLU of a NaN is unspecified on the GPU).
+    shapes = [(12, 40), (9, 33)]
+    w = W.custom_workload("nonfinite", shapes, grad_std=1e-2, steps=1, wid=130)
+    cfg = L.config_from(mlp_impl=impl)
+    weights = mlp(bias_std=0.1)
+    run = GpuRun(w, weights, cfg, torch)
+    grads = [torch.from_numpy(W.grad_at(w, i, 1).reshape(t.shape)).cuda() for i, t in enumerate(w.tensors)]
+    grads[0][5, 17] = bad
+    run.opt.step(grads)
+    got = [run.fetch(i) for i in range(2)]
+    run.close()
+    hp = hyper_from_cfg(cfg)
+    g0 = W.grad_at(w, 0, 1).reshape(shapes[0]).copy()
+    g0[5, 17] = bad
+    gs = [g0, W.grad_at(w, 1, 1).reshape(shapes[1])]
+    with np.errstate(all="ignore"):    # the oracle's arithmetic on the bad element
+        ps, sts = oracle.step([W.param_init(w, i) for i in range(2)], gs,
+                              [W.state_init(w, i) for i in range(2)], 1, weights, hp)
+    check(compare(got[1], dict(p=ps[1], **sts[1]), "clean tensor"))
+    want = sts[0]
+    errs = []
+    for k in ("m", "v", "r", "c"):
+        a, b = np.asarray(got[0][k], np.float64), np.asarray(want[k], np.float64).reshape(got[0][k].shape)
+        if not (np.array_equal(np.isnan(a), np.isnan(b)) and np.array_equal(np.isposinf(a), np.isposinf(b))
+                and np.array_equal(np.isneginf(a), np.isneginf(b))):
+            errs.append(f"{k}: non-finite pattern differs ({int((~np.isfinite(a)).sum())} vs {int((~np.isfinite(b)).sum())})")
+            continue
+        fin = np.isfinite(b)
+        assert (~fin).any()
+        bound = 1e-7 + 1e-5 * np.abs(b[fin])
+        if not np.all(np.abs(a[fin] - b[fin]) <= bound):
+            errs.append(f"{k}: finite entries out of tolerance")
+    check(errs)
