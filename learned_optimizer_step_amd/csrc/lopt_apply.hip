@@ -57,7 +57,7 @@ __global__ __launch_bounds__(kBlock) void k_apply_valu(StepCtx c, StepParams hp)
   TensorDesc d;
   const float* g;
   load_chunk(c, blockIdx.x, ch, d, g);
-  dispatch_variant(d.vec, hp, [&](auto v) {
+  dispatch_variant<false>(d, hp, [&](auto v) {
     using V = decltype(v);
     apply_valu_body<V::vec, V::normal, V::nf>(c, hp, ch, d, g);
   });
@@ -94,7 +94,16 @@ __device__ __forceinline__ void swap_halves(float x, float y, float& lo, float& 
   hi = __uint_as_float(r[1]);
 }
 
-template <bool VEC, bool NORMAL, int NF>
+// Layer-1 K-step slots: two per K-step, slot s on lane half s % 2.  Normally
+// slot s holds feature s.  With RU (the wave iteration lies in one row) the
+// row features F13..F15 are constant over the iteration: their weighted sum,
+// the row term, becomes the A operand of slot 0 (whose B value is 1), and
+// slots 1, 2, ... hold the other features in order.  -1: the constant slot.
+__device__ constexpr int slot_feature(int s, bool ru) {
+  return !ru ? s : s == 0 ? -1 : (s - 1 < 13 ? s - 1 : s + 2);
+}
+
+template <bool VEC, bool NORMAL, int NF, bool RU>
 __device__ __forceinline__ void apply_mfma_body(const StepCtx& c, const StepParams& hp, const Chunk& ch,
                                                 const TensorDesc& d, const float* g) {
   const int lane = threadIdx.x & 63;
@@ -105,14 +114,18 @@ __device__ __forceinline__ void apply_mfma_body(const StepCtx& c, const StepPara
   const float* __restrict__ pk = c.packed;
   const float* __restrict__ sc = c.scales + size_t(ch.tensor) * kStatStride;
 
-  constexpr int KS = (NF + 1) / 2;  // layer-1 K-steps (an odd NF pads with a zero feature)
-  float a1[KS];        // W1[row][2s + half] * s_(2s + half)
+  constexpr int NS = RU ? NF - 2 : NF;  // used slots (RU: NF - 3 features + the constant)
+  constexpr int KS = (NS + 1) / 2;       // layer-1 K-steps (an odd count pads with a zero)
+  float a1[KS];        // W1[row][f] * s_f for the feature f of slot 2q + half
   float a2[kH / 2];    // W2[row][acc_row(s, half)]
 #pragma unroll
   for (int q = 0; q < KS; ++q) {
-    const int f = 2 * q + half;
-    a1[q] = f < NF ? pk[kPkW1 + row * kNF + f] * sc[f] : 0.f;
+    const int f = slot_feature(2 * q + half, RU);
+    a1[q] = (f >= 0 && f < NF) ? pk[kPkW1 + row * kNF + f] * sc[f] : 0.f;
   }
+  float arow[3];       // RU: W1[row][13 + k] * s_(13 + k), the row term's weights
+#pragma unroll
+  for (int k = 0; k < 3; ++k) arow[k] = RU ? pk[kPkW1 + row * kNF + 13 + k] * sc[13 + k] : 0.f;
 #pragma unroll
   for (int q = 0; q < 16; ++q) a2[q] = pk[kPkW2 + row * kH + acc_row(q, half)];
 
@@ -138,7 +151,6 @@ __device__ __forceinline__ void apply_mfma_body(const StepCtx& c, const StepPara
     const float p_old = x.p;
     float F[kNF], cn[3];
     build_features<VEC, NORMAL, NF>(hp, x, F, cn);
-    if (NF & 1) F[NF] = 0.f;
     // the accumulators are final here: storing them now frees their registers
     // (and the copies the lane swaps below would need) during the MLP
     if (valid) store_state<VEC>(s, e, x, cn);
@@ -150,15 +162,28 @@ __device__ __forceinline__ void apply_mfma_body(const StepCtx& c, const StepPara
       bias1[4 * q] = v.x; bias1[4 * q + 1] = v.y; bias1[4 * q + 2] = v.z; bias1[4 * q + 3] = v.w;
     }
     f32x16 accA = bias1, accB = bias1;
+    float a_first = a1[0];
+    if (RU) {
+      // the row term of hidden unit `row` for this iteration's row (lane 0's
+      // element is always inside the chunk)
+      const float r0 = __int_as_float(uni(__float_as_int(x.rq[0])));
+      const float r1 = __int_as_float(uni(__float_as_int(x.rq[1])));
+      const float r2 = __int_as_float(uni(__float_as_int(x.rq[2])));
+      const float rt = fmaf(arow[2], r2, fmaf(arow[1], r1, arow[0] * r0));
+      a_first = half ? a1[0] : rt;
+    }
     // Higher issue priority while this wave runs its matrix-core chains: the
     // chains then issue back to back ahead of the other waves' vector work
     // (measured: 5 % fewer cycles than without).
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int q = 0; q < KS; ++q) {
+      const int f0 = slot_feature(2 * q, RU), f1 = slot_feature(2 * q + 1, RU);
+      const float x0 = f0 < 0 ? 1.f : f0 < NF ? F[f0] : 0.f;
+      const float x1 = f1 < 0 ? 1.f : f1 < NF ? F[f1] : 0.f;
       float bA, bB;
-      swap_halves(F[2 * q], F[2 * q + 1], bA, bB);
-      const float aq = a1[q];
+      swap_halves(x0, x1, bA, bB);
+      const float aq = q == 0 ? a_first : a1[q];
       accA = __builtin_amdgcn_mfma_f32_32x32x2f32(aq, bA, accA, 0, 0, 0);
       accB = __builtin_amdgcn_mfma_f32_32x32x2f32(aq, bB, accB, 0, 0, 0);
     }
@@ -214,9 +239,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   TensorDesc d;
   const float* g;
   load_chunk(c, blockIdx.x, ch, d, g);
-  dispatch_variant(d.vec, hp, [&](auto v) {
+  dispatch_variant<true>(d, hp, [&](auto v) {
     using V = decltype(v);
-    apply_mfma_body<V::vec, V::normal, V::nf>(c, hp, ch, d, g);
+    apply_mfma_body<V::vec, V::normal, V::nf, V::rowuni>(c, hp, ch, d, g);
   });
 }
 

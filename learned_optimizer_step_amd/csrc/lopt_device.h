@@ -165,36 +165,39 @@ __device__ __forceinline__ float rsq(float x) {
 }
 
 // Compile-time variant of a chunk's per-element code: tensor kind (1-D or
-// factored 2-D), 1/sqrt mode, and number of per-element features (kNF for
-// small_fc_lopt, kVeloNF for the VeLO-shaped variant, which stops at F18).
-template <bool V, bool N, int F>
+// factored 2-D), 1/sqrt mode, number of per-element features (kNF for
+// small_fc_lopt, kVeloNF for the VeLO-shaped variant, which stops at F18), and
+// whether every 64-element wave iteration lies inside one row (2-D tensors
+// whose column count is a multiple of 64: the chunks start at multiples of
+// 256 elements).
+template <bool V, bool N, int F, bool RU = false>
 struct Variant {
   static constexpr bool vec = V;
   static constexpr bool normal = N;
   static constexpr int nf = F;
+  static constexpr bool rowuni = RU;
 };
 
+__device__ __forceinline__ bool rows_uniform(const TensorDesc& d) { return !d.vec && (d.C & 63) == 0; }
+
 // Calls body(Variant<...>{}) for the chunk's tensor kind and the step's 1/sqrt
-// mode and feature count (all uniform over the workgroup).
-template <class Body>
-__device__ __forceinline__ void dispatch_variant(bool vec, const StepParams& hp, Body&& body) {
-  if (hp.n_feat == kNF) {
-    if (vec) {
-      if (hp.rsq_normal) body(Variant<true, true, kNF>{});
-      else body(Variant<true, false, kNF>{});
+// mode and feature count (all uniform over the workgroup).  ROWS: also tell
+// row-uniform 2-D tensors apart (only the matrix-core apply kernel uses it).
+template <bool ROWS, class Body>
+__device__ __forceinline__ void dispatch_variant(const TensorDesc& d, const StepParams& hp, Body&& body) {
+  auto by_nf = [&](auto kind) {
+    using K = decltype(kind);
+    if (hp.n_feat == kNF) {
+      if (hp.rsq_normal) body(Variant<K::vec, true, kNF, K::rowuni>{});
+      else body(Variant<K::vec, false, kNF, K::rowuni>{});
     } else {
-      if (hp.rsq_normal) body(Variant<false, true, kNF>{});
-      else body(Variant<false, false, kNF>{});
+      if (hp.rsq_normal) body(Variant<K::vec, true, kVeloNF, K::rowuni>{});
+      else body(Variant<K::vec, false, kVeloNF, K::rowuni>{});
     }
-  } else {
-    if (vec) {
-      if (hp.rsq_normal) body(Variant<true, true, kVeloNF>{});
-      else body(Variant<true, false, kVeloNF>{});
-    } else {
-      if (hp.rsq_normal) body(Variant<false, true, kVeloNF>{});
-      else body(Variant<false, false, kVeloNF>{});
-    }
-  }
+  };
+  if (d.vec) by_nf(Variant<true, true, kNF, false>{});
+  else if (ROWS && rows_uniform(d)) by_nf(Variant<false, true, kNF, true>{});
+  else by_nf(Variant<false, true, kNF, false>{});
 }
 
 // Builds F[0..NF) (NF = kNF or kVeloNF; F[NF..kNF) are left unset).

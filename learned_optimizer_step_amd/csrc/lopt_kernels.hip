@@ -290,7 +290,7 @@ __global__ __launch_bounds__(kBlock) void k_stats(StepCtx c, StepParams hp) {
   float acc[kNF];
 #pragma unroll
   for (int f = 0; f < kNF; ++f) acc[f] = 0.f;
-  dispatch_variant(d.vec, hp, [&](auto v) {
+  dispatch_variant<false>(d, hp, [&](auto v) {
     using V = decltype(v);
     stats_body<V::vec, V::normal, V::nf>(c, hp, ch, d, g, acc);
   });

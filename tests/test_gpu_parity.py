@@ -26,6 +26,12 @@ EDGE_SHAPES = [(1,), (2,), (3,), (15,), (16,), (17,), (63,), (65,), (40000,),
                (129, 257), (600, 5), (5, 600), (1000, 1), (33, 64)]
 
 
+# 2-D shapes whose column count is a multiple of 64: every 64-element wave
+# iteration of the matrix-core apply kernel lies inside one row, and the row
+# features enter through the row-term slot
+ROW_UNIFORM_SHAPES = [(2, 64), (3, 128), (5, 192), (64, 64), (100, 320), (7, 4096), (300, 256)]
+
+
 def mlp(n_time=11, bias_std=0.0):
     return W.mlp_weights(n_time, bias_std=bias_std)
 
@@ -44,6 +50,13 @@ def test_single256_ten_steps(impl):
 def test_edge_shapes_ten_steps(impl):
     w = W.custom_workload("edges", EDGE_SHAPES, grad_std=1e-2, steps=10, wid=101)
     check(parity(w, mlp(bias_std=0.1), L.config_from(mlp_impl=impl), torch))
+
+
+@pytest.mark.parametrize("n_feat", [L.LOPT_N_FEATURES, L.LOPT_VELO_FEATURES])
+def test_row_uniform_shapes_ten_steps(n_feat):
+    w = W.custom_workload("rowuni", ROW_UNIFORM_SHAPES, grad_std=1e-2, steps=10, wid=104)
+    weights = W.mlp_weights(11, bias_std=0.1, n_feat=n_feat)
+    check(parity(w, weights, L.config_from(mlp_impl=L.LOPT_MLP_MFMA, n_feat=n_feat), torch))
 
 
 @pytest.mark.parametrize("impl", IMPLS)
