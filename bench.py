@@ -68,7 +68,7 @@ def committed_traffic(workload: str, kernel: str = "k_apply_mfma"):
     return None
 
 
-def cpu_baseline(blocks: int = 5):
+def cpu_baseline(blocks: int = 7):
     """The oracle on the first ``blocks`` ViT-B/16 transformer blocks, one step, on host cores."""
     import numpy as np
     from threadpoolctl import threadpool_info, threadpool_limits

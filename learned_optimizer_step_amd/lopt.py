@@ -204,46 +204,65 @@ def matrix_shape(shape) -> tuple:
     raise ValueError("parameters must be 1-D or 2-D")
 
 
+# numpy view of an array of lopt_tensor (three pointers and two int64 per entry)
+_TENSOR_DTYPE = np.dtype([("param", "<u8"), ("grad", "<u8"), ("state", "<u8"), ("rows", "<i8"), ("cols", "<i8")])
+
+
 class LOpt:
     """The optimizer over a list of fp32 CUDA (HIP) tensors.
 
-    params: torch tensors (1-D or 2-D, contiguous, float32, on one device).
+    params: torch tensors (1-D or 2-D, contiguous, float32, all on one device).
     mlp: packed fp32 MLP weights (numpy).  cfg: lopt_config.
+    The tensor table handed to lopt_step is kept between steps; each step only
+    writes the gradient addresses into it.
     """
 
     def __init__(self, params, mlp: np.ndarray, cfg: Optional[lopt_config] = None):
         import torch
         self.torch = torch
         self.params = list(params)
+        dev = self.params[0].device if self.params else torch.device("cuda")
         for p in self.params:
-            if p.dtype != torch.float32 or not p.is_cuda or not p.is_contiguous():
-                raise ValueError("parameters must be contiguous float32 device tensors")
+            if p.dtype != torch.float32 or not p.is_cuda or not p.is_contiguous() or p.device != dev:
+                raise ValueError("parameters must be contiguous float32 tensors on one device")
+        self.device = dev
         self.cfg = cfg if cfg is not None else lopt_default_config()
         self.shapes = [matrix_shape(p.shape) for p in self.params]
-        dev = self.params[0].device if self.params else torch.device("cuda")
         self.states = [torch.empty(lopt_state_floats(r, c), dtype=torch.float32, device=dev)
                        for r, c in self.shapes]
+        n = len(self.params)
+        assert _TENSOR_DTYPE.itemsize == ctypes.sizeof(lopt_tensor)
+        self._table = np.zeros(max(1, n), _TENSOR_DTYPE)
+        if n:
+            self._table["param"][:n] = [p.data_ptr() for p in self.params]
+            self._table["state"][:n] = [s.data_ptr() for s in self.states]
+            self._table["rows"][:n] = [r for r, _ in self.shapes]
+            self._table["cols"][:n] = [c for _, c in self.shapes]
+        self._table_ptr = self._table.ctypes.data_as(ctypes.POINTER(lopt_tensor))
         self.handle = lopt_create(self.cfg, mlp)
-        ts = self._tensors(None)  # gradients are first needed by lopt_step
-        self.ws_bytes = lopt_workspace_bytes(self.handle, ts)
+        lib = load_library()
+        ws = ctypes.c_size_t()
+        # gradients are first needed by lopt_step: NULL grad pointers here
+        _check(lib.lopt_workspace_bytes(self.handle, self._table_ptr, n, ctypes.byref(ws)))
+        self.ws_bytes = int(ws.value)
         self.workspace = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)
-        lopt_init_state(self.handle, ts, self.workspace.data_ptr(), self.ws_bytes,
-                        torch.cuda.current_stream(dev).cuda_stream)
-
-    def _tensors(self, grads) -> List[lopt_tensor]:
-        out = []
-        for i, (p, s, (r, c)) in enumerate(zip(self.params, self.states, self.shapes)):
-            g = grads[i].data_ptr() if grads is not None else None
-            out.append(lopt_tensor(p.data_ptr(), g, s.data_ptr(), r, c))
-        return out
+        _check(lib.lopt_init_state(self.handle, self._table_ptr, n, ctypes.c_void_p(self.workspace.data_ptr()),
+                                   self.ws_bytes, ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)))
 
     def step(self, grads) -> None:
+        grads = list(grads)
+        n = len(self.params)
+        if len(grads) != n:
+            raise ValueError(f"expected {n} gradients, got {len(grads)}")
+        f32, dev = self.torch.float32, self.device
         for g, p in zip(grads, self.params):
-            if g.dtype != self.torch.float32 or not g.is_contiguous() or g.numel() != p.numel():
-                raise ValueError("gradients must be contiguous float32 tensors shaped like the parameters")
-        dev = self.params[0].device if self.params else None
-        lopt_step(self.handle, self._tensors(list(grads)),
-                  self.torch.cuda.current_stream(dev).cuda_stream)
+            if g.dtype != f32 or not g.is_contiguous() or g.numel() != p.numel() or g.device != dev:
+                raise ValueError("gradients must be contiguous float32 tensors shaped like the parameters, "
+                                 "on the parameters' device")
+        if n:
+            self._table["grad"][:n] = [g.data_ptr() for g in grads]
+        _check(load_library().lopt_step(self.handle, self._table_ptr, n,
+                                        ctypes.c_void_p(self.torch.cuda.current_stream(dev).cuda_stream)))
 
     @property
     def t(self) -> int:

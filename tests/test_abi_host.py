@@ -160,3 +160,20 @@ def test_null_handle_calls(lib):
 def test_binding_has_the_c_names():
     for n in declared_functions():
         assert hasattr(L, n), n
+
+
+def test_numpy_tensor_table_matches_the_struct_layout(lib):
+    # LOpt hands lopt_step a persistent numpy table instead of ctypes structs
+    import numpy as np
+    assert L._TENSOR_DTYPE.itemsize == ctypes.sizeof(L.lopt_tensor)
+    ts = fake_list([(16, 16), (1, 9), (300, 7)])
+    tab = np.zeros(3, L._TENSOR_DTYPE)
+    for i, t in enumerate(ts):
+        tab[i] = (t.param, t.grad, t.state, t.rows, t.cols)
+    out = ctypes.c_size_t()
+    st = lib.lopt_workspace_bytes(None, tab.ctypes.data_as(ctypes.POINTER(L.lopt_tensor)), 3, ctypes.byref(out))
+    assert st == L.LOPT_OK
+    assert (st, out.value) == ws_status(ts)
+    tab[1]["rows"] = 0    # the library reads the rows field where the struct has it
+    st = lib.lopt_workspace_bytes(None, tab.ctypes.data_as(ctypes.POINTER(L.lopt_tensor)), 3, ctypes.byref(out))
+    assert st == L.LOPT_ERR_INVALID_ARGUMENT
