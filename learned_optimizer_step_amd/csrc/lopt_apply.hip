@@ -95,8 +95,8 @@ __device__ __forceinline__ void swap_halves(float x, float y, float& lo, float& 
 }
 
 // Layer-1 K-step slots: two per K-step, slot s on lane half s % 2.  Normally
-// slot s holds feature s.  With RU (the wave iteration lies in one row) the
-// row features F13..F15 are constant over the iteration: their weighted sum,
+// slot s holds feature s.  With RU (a 1-D tensor, or a wave iteration inside
+// one row) the row features F13..F15 are constant over the iteration: their weighted sum,
 // the row term, becomes the A operand of slot 0 (whose B value is 1), and
 // slots 1, 2, ... hold the other features in order.  -1: the constant slot.
 __device__ constexpr int slot_feature(int s, bool ru) {

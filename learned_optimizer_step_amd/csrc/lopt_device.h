@@ -167,9 +167,10 @@ __device__ __forceinline__ float rsq(float x) {
 // Compile-time variant of a chunk's per-element code: tensor kind (1-D or
 // factored 2-D), 1/sqrt mode, number of per-element features (kNF for
 // small_fc_lopt, kVeloNF for the VeLO-shaped variant, which stops at F18), and
-// whether every 64-element wave iteration lies inside one row (2-D tensors
-// whose column count is a multiple of 64: the chunks start at multiples of
-// 256 elements).
+// whether the row features are constant over every 64-element wave iteration:
+// 1-D tensors (one r_k per tensor) and 2-D tensors whose column count is a
+// multiple of 64 (the chunks start at multiples of 256 elements, so a wave
+// iteration lies inside one row).
 template <bool V, bool N, int F, bool RU = false>
 struct Variant {
   static constexpr bool vec = V;
@@ -181,8 +182,8 @@ struct Variant {
 __device__ __forceinline__ bool rows_uniform(const TensorDesc& d) { return !d.vec && (d.C & 63) == 0; }
 
 // Calls body(Variant<...>{}) for the chunk's tensor kind and the step's 1/sqrt
-// mode and feature count (all uniform over the workgroup).  ROWS: also tell
-// row-uniform 2-D tensors apart (only the matrix-core apply kernel uses it).
+// mode and feature count (all uniform over the workgroup).  ROWS: also mark
+// the row-uniform kinds (only the matrix-core apply kernel uses it).
 template <bool ROWS, class Body>
 __device__ __forceinline__ void dispatch_variant(const TensorDesc& d, const StepParams& hp, Body&& body) {
   auto by_nf = [&](auto kind) {
@@ -195,7 +196,7 @@ __device__ __forceinline__ void dispatch_variant(const TensorDesc& d, const Step
       else body(Variant<K::vec, false, kVeloNF, K::rowuni>{});
     }
   };
-  if (d.vec) by_nf(Variant<true, true, kNF, false>{});
+  if (d.vec) by_nf(Variant<true, true, kNF, ROWS>{});
   else if (ROWS && rows_uniform(d)) by_nf(Variant<false, true, kNF, true>{});
   else by_nf(Variant<false, true, kNF, false>{});
 }
