@@ -71,10 +71,11 @@ __global__ __launch_bounds__(kBlock) void k_apply_valu(StepCtx c, StepParams hp)
 // units as M (weights = A operand, register resident), the elements as N and
 // the features as K:
 //   layer 1: 14 K-steps of two features (10 for the 19-feature variant, the
-//     last padded with a zero).  v_permlane32_swap of the feature
-//     pair (2s, 2s+1) gives, in one instruction, the B operands of both
-//     halves: [F_2s of elements 0..31 | F_2s+1 of elements 0..31] and
-//     [F_2s of elements 32..63 | F_2s+1 of elements 32..63].
+//     last padded with a zero; one fewer with the row-term slot below).
+//     v_permlane32_swap of the feature pair (2s, 2s+1) gives, in one
+//     instruction, the B operands of both halves: [F_2s of elements 0..31 |
+//     F_2s+1 of elements 0..31] and [F_2s of elements 32..63 | F_2s+1 of
+//     elements 32..63].
 //   layer 2: the layer-1 accumulator register r of a lane holds hidden unit
 //     8(r/4) + 4(lane/32) + r%4 of element lane%32, which is exactly a K-step
 //     B operand if W2's columns are visited in that order (no data movement).
@@ -96,9 +97,10 @@ __device__ __forceinline__ void swap_halves(float x, float y, float& lo, float& 
 
 // Layer-1 K-step slots: two per K-step, slot s on lane half s % 2.  Normally
 // slot s holds feature s.  With RU (a 1-D tensor, or a wave iteration inside
-// one row) the row features F13..F15 are constant over the iteration: their weighted sum,
-// the row term, becomes the A operand of slot 0 (whose B value is 1), and
-// slots 1, 2, ... hold the other features in order.  -1: the constant slot.
+// one row) the row features F13..F15 are constant over the iteration: their
+// weighted sum, the row term, becomes the A operand of slot 0 (whose B value
+// is 1), and slots 1, 2, ... hold the other features in order.  -1: the
+// constant slot.
 __device__ constexpr int slot_feature(int s, bool ru) {
   return !ru ? s : s == 0 ? -1 : (s - 1 < 13 ? s - 1 : s + 2);
 }
@@ -148,7 +150,7 @@ __device__ __forceinline__ void apply_mfma_body(const StepCtx& c, const StepPara
     const bool valid = e < ch.e1;
     Elem x;
     load_elem<VEC>(s, valid ? e : ch.e0, x);
-    const float p_old = x.p;
+    const float p_decayed = x.p * hp.decay;  // before the swaps below overwrite F1 = p
     float F[kNF], cn[3];
     build_features<VEC, NORMAL, NF>(hp, x, F, cn);
     // the accumulators are final here: storing them now frees their registers
@@ -205,7 +207,9 @@ __device__ __forceinline__ void apply_mfma_body(const StepCtx& c, const StepPara
       acc2B = __builtin_amdgcn_mfma_f32_32x32x2f32(aq, accB[q], acc2B, 0, 0, 0);
     }
     __builtin_amdgcn_s_setprio(0);
-    float dA = 0.f, mA = 0.f, dB = 0.f, mB = 0.f;
+    // half 0's partial sums start at b3, so the sum of the two halves holds it once
+    const float d_init = half ? 0.f : b3d, m_init = half ? 0.f : b3m;
+    float dA = d_init, mA = m_init, dB = d_init, mB = m_init;
     float w3d[16], w3m[16];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -226,11 +230,9 @@ __device__ __forceinline__ void apply_mfma_body(const StepCtx& c, const StepPara
     float d0, d1, m0, m1;
     swap_halves(dA, dB, d0, d1);
     swap_halves(mA, mB, m0, m1);
-    const float dir = (d0 + d1) + b3d;
-    const float mag = (m0 + m1) + b3m;
-    if (valid) {
-      store_param(s, e, fmaf(-hp.lr_step, dir * __builtin_amdgcn_exp2f(mag * hp.exp2_mult), p_old * hp.decay));
-    }
+    const float dir = d0 + d1;
+    const float mag = m0 + m1;
+    if (valid) store_param(s, e, fmaf(-hp.lr_step, dir * __builtin_amdgcn_exp2f(mag * hp.exp2_mult), p_decayed));
   }
 }
 

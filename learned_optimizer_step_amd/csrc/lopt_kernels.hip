@@ -49,11 +49,14 @@ __global__ __launch_bounds__(kBlock) void k_rowcol_sumsq(StepCtx c) {
     for (; e + 7 * kBlock < uint32_t(tl.c1); e += 8 * kBlock) {
       float x[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) x[u] = g[e + u * kBlock];
+      for (int u = 0; u < 8; ++u) x[u] = __builtin_nontemporal_load(g + e + u * kBlock);
 #pragma unroll
       for (int u = 0; u < 8; ++u) acc[u] = fmaf(x[u], x[u], acc[u]);
     }
-    for (; e < uint32_t(tl.c1); e += kBlock) { const float a = g[e]; acc[0] = fmaf(a, a, acc[0]); }
+    for (; e < uint32_t(tl.c1); e += kBlock) {
+      const float a = __builtin_nontemporal_load(g + e);
+      acc[0] = fmaf(a, a, acc[0]);
+    }
     const float s = block_sum(((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7])), red);
     if (tid == 0) ws[d.off_rowpart + tl.win] = s;
     return;
@@ -67,15 +70,15 @@ __global__ __launch_bounds__(kBlock) void k_rowcol_sumsq(StepCtx c) {
     const int lane = tid & 63, wave = tid >> 6;
     const int cb = tl.c0 + 4 * lane;
     const bool act = cb < tl.c1;  // cols % 4 == 0: all four columns valid
-    const float4* __restrict__ g4 = reinterpret_cast<const float4*>(g);
+    const f32x4* __restrict__ g4 = reinterpret_cast<const f32x4*>(g);
     const int C4 = d.C >> 2;
     float4 ca = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int r = tl.r0 + wave; r < tl.r1; r += 4 * kB) {
-      float4 x[kB];
+      f32x4 x[kB];
 #pragma unroll
       for (int u = 0; u < kB; ++u) {
         const int i = r + 4 * u;
-        x[u] = (act && i < tl.r1) ? g4[size_t(i) * C4 + (cb >> 2)] : make_float4(0.f, 0.f, 0.f, 0.f);
+        x[u] = (act && i < tl.r1) ? __builtin_nontemporal_load(g4 + size_t(i) * C4 + (cb >> 2)) : f32x4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
       for (int u = 0; u < kB; ++u) {
@@ -115,7 +118,7 @@ __global__ __launch_bounds__(kBlock) void k_rowcol_sumsq(StepCtx c) {
 #pragma unroll
     for (int u = 0; u < kRowBatch; ++u) {
       const int i = tl.r0 + slot + RS * (q0 + u);
-      x[u] = (colok && q0 + u < iters && i < tl.r1) ? g[size_t(i) * C + j] : 0.f;
+      x[u] = (colok && q0 + u < iters && i < tl.r1) ? __builtin_nontemporal_load(g + size_t(i) * C + j) : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < kRowBatch; ++u) {
