@@ -98,7 +98,7 @@ def cpu_baseline(blocks: int = 7):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="vit_b16")
     ap.add_argument("--impl", default="auto", choices=["auto", "valu", "mfma"])
@@ -231,7 +231,8 @@ def main():
             out["frac_of_measured"] = {
                 "k_apply_vs_mfma_4waves_2chains": round(achieved / mp["mfma_4waves_2chains_tflops"], 4)
                 if use_mfma else None,
-                "k_stats_vs_read_bw": round(out["hbm_kernels"]["k_stats"]["achieved"] / (mp["read_bw_TBps"] * 1e3), 4),
+                "k_stats_vs_read_bw": round(out["hbm_kernels"]["k_stats"]["achieved"] /
+                                            (max(mp["read_bw_TBps"], mp["read_bw_nontemporal_TBps"]) * 1e3), 4),
             }
         else:
             out["measured_peaks"] = {"error": res.stderr[-300:]}

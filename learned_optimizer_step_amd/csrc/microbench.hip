@@ -1,5 +1,6 @@
 // Measured machine figures behind the roofline of the optimizer step:
-//   1. streaming read bandwidth of HBM (the bound of the statistics pass);
+//   1. streaming read bandwidth of HBM (the bound of the statistics pass),
+//      with plain and with non-temporal loads;
 //   2. sustained fp32 matrix throughput (v_mfma_f32_32x32x2_f32) for 1, 2 and
 //      4 waves per SIMD and 1, 2 or 4 independent accumulator chains per wave
 //      (the apply kernel runs 4 waves with 2 chains each);
@@ -14,6 +15,7 @@
 #include <cstdio>
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(256) void read_stream(const float4* __restrict__ a, size_t n4, float* __restrict__ out) {
   float acc = 0.f;
@@ -25,6 +27,25 @@ __global__ __launch_bounds__(256) void read_stream(const float4* __restrict__ a,
            ((x2.x + x2.y) + (x2.z + x2.w)) + ((x3.x + x3.y) + (x3.z + x3.w));
   }
   for (; i < n4; i += stride) acc += (a[i].x + a[i].y) + (a[i].z + a[i].w);
+  out[size_t(blockIdx.x) * 256 + threadIdx.x] = acc;
+}
+
+// The same read with the non-temporal hint (how the optimizer's kernels read
+// their per-element streams).
+__global__ __launch_bounds__(256) void read_stream_nt(const f32x4* __restrict__ a, size_t n4, float* __restrict__ out) {
+  float acc = 0.f;
+  size_t i = size_t(blockIdx.x) * 256 + threadIdx.x;
+  const size_t stride = size_t(gridDim.x) * 256;
+  for (; i + 3 * stride < n4; i += 4 * stride) {
+    const f32x4 x0 = __builtin_nontemporal_load(a + i), x1 = __builtin_nontemporal_load(a + i + stride);
+    const f32x4 x2 = __builtin_nontemporal_load(a + i + 2 * stride), x3 = __builtin_nontemporal_load(a + i + 3 * stride);
+    acc += ((x0.x + x0.y) + (x0.z + x0.w)) + ((x1.x + x1.y) + (x1.z + x1.w)) +
+           ((x2.x + x2.y) + (x2.z + x2.w)) + ((x3.x + x3.y) + (x3.z + x3.w));
+  }
+  for (; i < n4; i += stride) {
+    const f32x4 x = __builtin_nontemporal_load(a + i);
+    acc += (x.x + x.y) + (x.z + x.w);
+  }
   out[size_t(blockIdx.x) * 256 + threadIdx.x] = acc;
 }
 
@@ -137,9 +158,24 @@ int main() {
       best_grid = grid;
     }
   }
+  double best_nt = 0.0;
+  int best_nt_grid = 0;
+  for (int grid : {2048, 4096, 8192, 16384, 65536}) {
+    const float ms = time_ms([&] {
+      hipLaunchKernelGGL(read_stream_nt, dim3(grid), dim3(256), 0, 0, reinterpret_cast<const f32x4*>(buf), bytes / 16,
+                         out);
+    });
+    if (ms <= 0.f) return 1;
+    const double bw = bytes / (ms * 1e-3) / 1e12;
+    if (bw > best_nt) {
+      best_nt = bw;
+      best_nt_grid = grid;
+    }
+  }
   CHECK(hipFree(buf));
-  printf("{\"device\": \"%s\", \"cus\": %d, \"read_bw_TBps\": %.3f, \"read_bw_grid\": %d", prop.gcnArchName, cus,
-         best_bw, best_grid);
+  printf("{\"device\": \"%s\", \"cus\": %d, \"read_bw_TBps\": %.3f, \"read_bw_grid\": %d, "
+         "\"read_bw_nontemporal_TBps\": %.3f, \"read_bw_nontemporal_grid\": %d",
+         prop.gcnArchName, cus, best_bw, best_grid, best_nt, best_nt_grid);
 
   // 2. matrix throughput: waves per SIMD x accumulator chains per wave
   const int iters = 4000;

@@ -1,0 +1,22 @@
+"""bench.py's command-line contract on the CPU: a request for more than one GPU
+is refused with a message (this build measures one GPU) before any device work."""
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=60)
+    assert res.returncode != 0
+    assert "one GPU" in res.stderr and res.stdout == ""
+
+
+def test_help_lists_the_options():
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--help"],
+                         capture_output=True, text=True, timeout=60)
+    assert res.returncode == 0
+    for opt in ("--gpus", "--steps", "--warmup", "--workload", "--n-feat", "--impl", "--peaks"):
+        assert opt in res.stdout
