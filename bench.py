@@ -180,7 +180,7 @@ def main():
     step_bytes = 44 * (n - n_vec) + 68 * n_vec
     # algorithmic bytes of the two streaming kernels: g (4 B); g, p, m1..3, v (24 B, 1-D + 12 B)
     stream_bytes = {"k_rowcol_sumsq": 4 * n, "k_stats": 24 * n + 12 * n_vec}
-    apply_ms = float(kern_ms[4])
+    apply_ms = float(kern_ms[L.KERNEL_NAMES.index("k_apply")])
     fpe = flop_per_elem(args.n_feat)
     achieved = fpe * n / (apply_ms * 1e-3) / 1e12
     use_mfma = impl != L.LOPT_MLP_VALU
