@@ -310,16 +310,57 @@ __global__ __launch_bounds__(kBlock) void k_stats(StepCtx c, StepParams hp) {
   }
 }
 
+// Packs the MLP for the apply kernel (one block): W1's feature columns, b1
+// with the step features folded in, W2, b2, W3, b3; advances the step counter.
+__device__ void pack_mlp(const StepCtx& c, const StepParams& hp) {
+  // The step counter lives in device memory so that a captured step, replayed
+  // from a graph, still sees t = 1, 2, 3, ...  Every thread reads it, then
+  // thread 0 advances it after the barrier below.
+  const int64_t step = *c.step + 1;
+  const float tf = float(step);
+  const int nf = hp.n_feat;
+  const int din = nf + hp.n_time;
+  const float* W1 = c.mlp;
+  const float* b1 = W1 + kH * din;
+  const float* W2 = b1 + kH;
+  const float* b2 = W2 + kH * kH;
+  const float* W3 = b2 + kH;
+  const float* b3 = W3 + 2 * kH;
+  float* pk = c.packed;
+  for (int q = threadIdx.x; q < kH * kNF; q += kBlock) {
+    const int o = q / kNF, f = q - o * kNF;
+    pk[kPkW1 + q] = f < nf ? W1[o * din + f] : 0.f;
+  }
+  if (threadIdx.x < kH) {
+    const int o = threadIdx.x;
+    float b = b1[o];
+    for (int s = 0; s < hp.n_time; ++s) b = fmaf(W1[o * din + nf + s], tanhf(tf / hp.timescales[s]), b);
+    pk[kPkB1 + o] = b;
+    pk[kPkB2 + o] = b2[o];
+    pk[kPkW3 + o] = W3[o];
+    pk[kPkW3 + kH + o] = W3[kH + o];
+  }
+  for (int q = threadIdx.x; q < kH * kH; q += kBlock) pk[kPkW2 + q] = W2[q];
+  if (threadIdx.x < 2) pk[kPkB3 + threadIdx.x] = b3[threadIdx.x];
+  __syncthreads();
+  if (threadIdx.x == 0) *c.step = step;
+}
+
 // ---------------------------------------------------------------------------
 // k_finalize: per tensor, S'_d = sum of the chunk partials (chunk order).  The
 // statistics pass leaves sqrt(rbar_k) out of rho_k, so for the rho features
 // S_d = S'_d rbar_k.  Then s_d = (S_d / n + eps_norm)^(-1/2), and the scale
 // stored for the apply kernel (which also leaves sqrt(rbar_k) out) is s_d, or
-// s_d sqrt(rbar_k) for the rho features.  Block 0 packs the MLP for the apply
-// kernel, folding the step features into the first bias:
-// b1' = b1 + W1[:, 28:28+n_time] tanh(t / tau).
+// s_d sqrt(rbar_k) for the rho features.  The last block (index n_tensors)
+// packs the MLP for the apply kernel, folding the step features into the first
+// bias: b1' = b1 + W1[:, 28:28+n_time] tanh(t / tau); it runs beside the
+// per-tensor blocks instead of after tensor 0's.
 __global__ __launch_bounds__(kBlock) void k_finalize(StepCtx c, StepParams hp) {
   const int t = blockIdx.x;
+  if (t == c.n_tensors) {
+    pack_mlp(c, hp);
+    return;
+  }
   const TensorDesc d = c.desc[t];
   __shared__ float lds[4][kNF];
   __shared__ float red[4];
@@ -351,40 +392,6 @@ __global__ __launch_bounds__(kBlock) void k_finalize(StepCtx c, StepParams hp) {
   } else if (threadIdx.x < kNF + 3) {
     const int k = threadIdx.x - kNF;
     sc[kNF + k] = sr[k];
-  }
-
-  if (t == 0) {
-    // The step counter lives in device memory so that a captured step, replayed
-    // from a graph, still sees t = 1, 2, 3, ...  Every thread reads it, then
-    // thread 0 advances it after the barrier below.
-    const int64_t step = *c.step + 1;
-    const float tf = float(step);
-    const int nf = hp.n_feat;
-    const int din = nf + hp.n_time;
-    const float* W1 = c.mlp;
-    const float* b1 = W1 + kH * din;
-    const float* W2 = b1 + kH;
-    const float* b2 = W2 + kH * kH;
-    const float* W3 = b2 + kH;
-    const float* b3 = W3 + 2 * kH;
-    float* pk = c.packed;
-    for (int q = threadIdx.x; q < kH * kNF; q += kBlock) {
-      const int o = q / kNF, f = q - o * kNF;
-      pk[kPkW1 + q] = f < nf ? W1[o * din + f] : 0.f;
-    }
-    if (threadIdx.x < kH) {
-      const int o = threadIdx.x;
-      float b = b1[o];
-      for (int s = 0; s < hp.n_time; ++s) b = fmaf(W1[o * din + nf + s], tanhf(tf / hp.timescales[s]), b);
-      pk[kPkB1 + o] = b;
-      pk[kPkB2 + o] = b2[o];
-      pk[kPkW3 + o] = W3[o];
-      pk[kPkW3 + kH + o] = W3[kH + o];
-    }
-    for (int q = threadIdx.x; q < kH * kH; q += kBlock) pk[kPkW2 + q] = W2[q];
-    if (threadIdx.x < 2) pk[kPkB3 + threadIdx.x] = b3[threadIdx.x];
-    __syncthreads();
-    if (threadIdx.x == 0) *c.step = step;
   }
 }
 
@@ -426,7 +433,7 @@ hipError_t launch_step(const StepCtx& c, const StepParams& p, hipStream_t s, con
   if ((e = mark(2)) != hipSuccess) return e;
   hipLaunchKernelGGL(k_stats, dim3(c.n_chunks), dim3(kBlock), 0, s, c, p);
   if ((e = mark(3)) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_finalize, dim3(c.n_tensors), dim3(kBlock), 0, s, c, p);
+  hipLaunchKernelGGL(k_finalize, dim3(c.n_tensors + 1), dim3(kBlock), 0, s, c, p);
   if ((e = mark(4)) != hipSuccess) return e;
   if ((e = launch_apply(c, p, s)) != hipSuccess) return e;
   if ((e = mark(5)) != hipSuccess) return e;

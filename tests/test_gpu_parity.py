@@ -374,3 +374,40 @@ def test_non_finite_gradient_stays_in_its_tensor(impl, bad):
         if not np.all(np.abs(a[fin] - b[fin]) <= bound):
             errs.append(f"{k}: finite entries out of tolerance")
     check(errs)
+
+
+def random_config(rng):
+    """Hyperparameters drawn across their valid ranges (fp32 values)."""
+    n_time = int(rng.integers(0, 12))
+    kw = dict(beta_m=sorted(rng.uniform(0.0, 0.99, 3).tolist()), beta_v=float(rng.uniform(0.9, 0.9999)),
+              beta_f=sorted(rng.uniform(0.5, 0.999, 3).tolist()), eps_v=float(10 ** rng.uniform(-10, -6)),
+              eps_f=float(10 ** rng.uniform(-24, -16)), eps_norm=float(10 ** rng.uniform(-32, -20)),
+              exp_mult=float(rng.uniform(1e-4, 0.1)), step_mult=float(rng.uniform(1e-4, 1e-2)),
+              lr=float(rng.uniform(0.1, 2.0)), weight_decay=float(rng.uniform(0.0, 0.1)), n_time=n_time,
+              timescales=sorted((10 ** rng.uniform(0, 5, n_time)).tolist()) if n_time else [],
+              n_feat=int(rng.choice([L.LOPT_N_FEATURES, L.LOPT_VELO_FEATURES])))
+    return kw
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_random_shapes_and_hyperparameters(case):
+    # seeded draws of tensor shapes (1-D, thin, square-ish, column counts with
+    # and without 64 | cols) and of every hyperparameter, 3 steps, both MLP paths
+    rng = np.random.default_rng(1000 + case)
+    shapes = []
+    for _ in range(5):
+        k = rng.integers(0, 4)
+        if k == 0:
+            shapes.append((int(rng.integers(1, 5000)),))
+        elif k == 1:
+            shapes.append((int(rng.integers(2, 40)), 64 * int(rng.integers(1, 20))))
+        else:
+            shapes.append((int(rng.integers(2, 300)), int(rng.integers(1, 300))))
+    kw = random_config(rng)
+    if case == 5:
+        kw["eps_v"] = 0.0   # the kernels' general 1/sqrt path (subnormal-safe)
+    w = W.custom_workload(f"rand{case}", shapes, grad_std=float(10 ** rng.uniform(-4, -1)), steps=3,
+                          prewarm_std=1e-3 if case % 2 else None, wid=200 + case)
+    weights = W.mlp_weights(kw["n_time"], seed=(7, case), bias_std=0.1, n_feat=kw["n_feat"])
+    for impl in IMPLS:
+        check(parity(w, weights, L.config_from(mlp_impl=impl, **kw), torch))
