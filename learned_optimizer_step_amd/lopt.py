@@ -342,3 +342,27 @@ class LearnedOptimizer(_torch_optimizer_base()):
             grads.append(p.grad)
         self.lopt.step(grads)
         return loss
+
+    def state_dict(self):
+        """torch's optimizer state (parameter groups) plus what the library keeps:
+        each parameter's accumulator buffer (layout of include/lopt.h) and the
+        step count."""
+        sd = super().state_dict()
+        sd["lopt"] = {"t": self.lopt.t, "n_feat": int(self.lopt.cfg.n_feat),
+                      "states": [s.detach().clone() for s in self.lopt.states]}
+        return sd
+
+    def load_state_dict(self, state_dict):
+        sd = dict(state_dict)
+        lo = sd.pop("lopt", None)
+        if lo is None:
+            raise ValueError("the state dict holds no learned-optimizer state")
+        if int(lo["n_feat"]) != int(self.lopt.cfg.n_feat) or len(lo["states"]) != len(self.lopt.states):
+            raise ValueError("the state dict belongs to another parameter list or learned optimizer")
+        for dst, src in zip(self.lopt.states, lo["states"]):
+            if src.numel() != dst.numel():
+                raise ValueError("accumulator buffer size differs from the parameter's")
+        super().load_state_dict(sd)   # parameter groups: lr and weight decay reach the library at the next step
+        for dst, src in zip(self.lopt.states, lo["states"]):
+            dst.copy_(src.to(device=dst.device, dtype=dst.dtype))
+        self.lopt.t = int(lo["t"])

@@ -411,3 +411,43 @@ def test_random_shapes_and_hyperparameters(case):
     weights = W.mlp_weights(kw["n_time"], seed=(7, case), bias_std=0.1, n_feat=kw["n_feat"])
     for impl in IMPLS:
         check(parity(w, weights, L.config_from(mlp_impl=impl, **kw), torch))
+
+
+def test_optimizer_state_dict_round_trip_continues_bitwise():
+    # checkpoint after 3 of 6 steps through torch.save / torch.load(weights_only=True),
+    # restore into a fresh optimizer over copies of the parameters, finish: the
+    # result equals the uninterrupted 6 steps bit for bit
+    import io
+    w = W.custom_workload("ckpt", [(37, 64), (9,), (5, 300)], grad_std=1e-2, steps=6, wid=140)
+    weights = mlp(bias_std=0.1)
+
+    def params():
+        return [torch.from_numpy(W.param_init(w, i).reshape(t.shape)).cuda() for i, t in enumerate(w.tensors)]
+
+    def run(opt, ps, steps):
+        for t in steps:
+            for i, (p, tt) in enumerate(zip(ps, w.tensors)):
+                p.grad = torch.from_numpy(W.grad_at(w, i, t).reshape(tt.shape)).cuda()
+            opt.step()
+
+    pa = params()
+    a = L.LearnedOptimizer(pa, weights, lr=0.7, weight_decay=0.01)
+    run(a, pa, range(1, 7))
+    pb = params()
+    b = L.LearnedOptimizer(pb, weights, lr=0.7, weight_decay=0.01)
+    run(b, pb, range(1, 4))
+    buf = io.BytesIO()
+    torch.save({"params": [p.detach().cpu() for p in pb], "opt": b.state_dict()}, buf)
+    buf.seek(0)
+    ck = torch.load(buf, weights_only=True)
+    pc = [p.cuda() for p in ck["params"]]
+    c = L.LearnedOptimizer(pc, weights, lr=1.0, weight_decay=0.0)   # restored from the checkpoint
+    c.load_state_dict(ck["opt"])
+    assert c.lopt.t == 3 and c.param_groups[0]["lr"] == 0.7
+    run(c, pc, range(4, 7))
+    torch.cuda.synchronize()
+    for i in range(len(w.tensors)):
+        assert torch.equal(pa[i], pc[i])
+        assert torch.equal(a.lopt.states[i], c.lopt.states[i])
+    for o in (a, b, c):
+        o.lopt.close()
