@@ -142,7 +142,8 @@ lopt_status lopt_workspace_bytes(const lopt_handle* h, const lopt_tensor* ts, in
  * plan upload and the zero fill have been queued and the upload has finished.
  * To start from pre-warmed accumulators, write the state buffers after this
  * call.  Errors: validation -> INVALID_ARGUMENT / UNSUPPORTED / WORKSPACE
- * (nothing is modified); HIP failure -> HIP. */
+ * (nothing is modified); a current device other than the handle's ->
+ * INVALID_ARGUMENT; HIP failure -> HIP. */
 lopt_status lopt_init_state(lopt_handle* h, const lopt_tensor* ts, int32_t n, void* workspace,
                             size_t ws_bytes, void* stream);
 
@@ -153,7 +154,8 @@ lopt_status lopt_init_state(lopt_handle* h, const lopt_tensor* ts, int32_t n, vo
  * lopt_init_state; grad pointers may differ (the plan's copy is refreshed,
  * which synchronises the stream, so it cannot happen while the stream is
  * being captured into a graph).  Errors: a different list -> STATE; bad
- * pointers -> INVALID_ARGUMENT; launch failure -> HIP.  On a validation
+ * pointers, or a current device other than the handle's -> INVALID_ARGUMENT;
+ * launch failure -> HIP.  On a validation
  * error nothing is queued.  Non-finite inputs are not checked (they propagate
  * into the accumulators). */
 lopt_status lopt_step(lopt_handle* h, const lopt_tensor* ts, int32_t n, void* stream);

@@ -372,6 +372,17 @@ void upload(char* ws, size_t off, const std::vector<T>& v, hipStream_t s) {
             "hipMemcpyAsync(plan)");
 }
 
+// The handle's weights and workspace live on the device that was current at
+// lopt_create; launching from another device would hand its kernels foreign
+// pointers.
+void check_device(const lopt_handle* h) {
+  int dev = -1;
+  hip_check(hipGetDevice(&dev), "hipGetDevice");
+  if (dev != h->device)
+    fail(LOPT_ERR_INVALID_ARGUMENT, "current device " + std::to_string(dev) + " is not the handle's device " +
+                                        std::to_string(h->device));
+}
+
 void check_same_list(const lopt_handle* h, const lopt_tensor* ts, int32_t n, bool* grads_changed) {
   if (!h->bound) fail(LOPT_ERR_STATE, "lopt_init_state has not been called");
   const auto& b = h->plan.bound;
@@ -468,6 +479,7 @@ lopt_status lopt_init_state(lopt_handle* h, const lopt_tensor* ts, int32_t n, vo
                             void* stream) {
   return guarded([&] {
     if (!h) fail(LOPT_ERR_INVALID_ARGUMENT, "handle is NULL");
+    check_device(h);
     Plan pl = build_plan(ts, n);
     if (pl.total > 0 && !workspace) fail(LOPT_ERR_WORKSPACE, "workspace is NULL");
     if (reinterpret_cast<uintptr_t>(workspace) & 255u) fail(LOPT_ERR_WORKSPACE, "workspace must be 256-byte aligned");
@@ -495,6 +507,7 @@ lopt_status lopt_step(lopt_handle* h, const lopt_tensor* ts, int32_t n, void* st
     if (!h) fail(LOPT_ERR_INVALID_ARGUMENT, "handle is NULL");
     bool grads_changed = false;
     check_same_list(h, ts, n, &grads_changed);
+    check_device(h);
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (grads_changed) {
       for (int32_t i = 0; i < n; ++i) {
