@@ -66,25 +66,26 @@ __global__ __launch_bounds__(kBlock) void k_apply_valu(StepCtx c, StepParams hp)
 // ---------------------------------------------------------------------------
 // k_apply_mfma: the page's kernel 2 with layers 1 and 2 of the MLP on the fp32
 // matrix cores.  A wave owns 64 elements per iteration, one per lane, for all
-// per-element work (loads, features, update, stores).  The MLP is a pair of
-// 32-element GEMM chains per wave, v_mfma_f32_32x32x2_f32 with the hidden
-// units as M (weights = A operand, register resident), the elements as N and
-// the features as K:
-//   layer 1: 14 K-steps of two features (10 for the 19-feature variant, the
-//     last padded with a zero; one fewer with the row-term slot below).
-//     v_permlane32_swap of the feature pair (2s, 2s+1) gives, in one
-//     instruction, the B operands of both halves: [F_2s of elements 0..31 |
-//     F_2s+1 of elements 0..31] and [F_2s of elements 32..63 | F_2s+1 of
-//     elements 32..63].
-//   layer 2: the layer-1 accumulator register r of a lane holds hidden unit
-//     8(r/4) + 4(lane/32) + r%4 of element lane%32, which is exactly a K-step
-//     B operand if W2's columns are visited in that order (no data movement).
+// per-element work (loads, features, update, stores).  The hidden units are M
+// (weights = A operand, register resident), the elements N, the inputs K:
+//   layer 1: v_mfma_f32_32x32x1_2b_f32, one instruction per feature (28, or
+//     19 for the 19-feature variant; two fewer with the row-term slot below).
+//     Its two blocks take their A and B operands from the two lane halves, so
+//     block b multiplies W1's column (held by both halves) with the feature of
+//     elements 32b..32b+31, each lane feeding its own element: no lane
+//     movement.  Block b's 32x32 result lands in accumulator registers
+//     16b..16b+15 in the usual 32x32 layout.
+//   layer 2: v_mfma_f32_32x32x2_f32, one chain per block.  Layer-1 register r
+//     of a lane holds hidden unit 8(r/4) + 4(lane/32) + r%4 of element
+//     lane%32 (+32 for the second block), which is exactly a K-step B operand
+//     if W2's columns are visited in that order (no data movement).
 //   layer 3 (32 -> 2) on the vector ALU: per-lane partial dot products over
-//     the lane's 16 hidden units, completed with one more swap.
+//     the lane's 16 hidden units, completed with one lane swap.
 // Biases enter as the C operand of the first MFMA of each chain (read from
 // LDS with W3 each iteration, which keeps the kernel within 128 VGPRs); the
 // feature scales s_d are folded into W1's columns once per chunk.
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x32 __attribute__((ext_vector_type(32)));
 
 __device__ __forceinline__ int acc_row(int r, int half) { return 8 * (r >> 2) + 4 * half + (r & 3); }
 
@@ -95,12 +96,11 @@ __device__ __forceinline__ void swap_halves(float x, float y, float& lo, float& 
   hi = __uint_as_float(r[1]);
 }
 
-// Layer-1 K-step slots: two per K-step, slot s on lane half s % 2.  Normally
-// slot s holds feature s.  With RU (a 1-D tensor, or a wave iteration inside
-// one row) the row features F13..F15 are constant over the iteration: their
-// weighted sum, the row term, becomes the A operand of slot 0 (whose B value
-// is 1), and slots 1, 2, ... hold the other features in order.  -1: the
-// constant slot.
+// Layer-1 slots, one per instruction.  Normally slot s holds feature s.
+// With RU (a 1-D tensor, or a wave iteration inside one row) the row features
+// F13..F15 are constant over the iteration: their weighted sum, the row term,
+// becomes the A operand of slot 0 (whose B value is 1), and slots 1, 2, ...
+// hold the other features in order.  -1: the constant slot.
 __device__ constexpr int slot_feature(int s, bool ru) {
   return !ru ? s : s == 0 ? -1 : (s - 1 < 13 ? s - 1 : s + 2);
 }
@@ -116,14 +116,13 @@ __device__ __forceinline__ void apply_mfma_body(const StepCtx& c, const StepPara
   const float* __restrict__ pk = c.packed;
   const float* __restrict__ sc = c.scales + size_t(ch.tensor) * kStatStride;
 
-  constexpr int NS = RU ? NF - 2 : NF;  // used slots (RU: NF - 3 features + the constant)
-  constexpr int KS = (NS + 1) / 2;       // layer-1 K-steps (an odd count pads with a zero)
-  float a1[KS];        // W1[row][f] * s_f for the feature f of slot 2q + half
+  constexpr int NS = RU ? NF - 2 : NF;  // layer-1 slots (RU: NF - 3 features + the constant)
+  float a1[NS];        // W1[row][f] * s_f for the feature f of slot j (the constant slot: unused)
   float a2[kH / 2];    // W2[row][acc_row(s, half)]
 #pragma unroll
-  for (int q = 0; q < KS; ++q) {
-    const int f = slot_feature(2 * q + half, RU);
-    a1[q] = (f >= 0 && f < NF) ? pk[kPkW1 + row * kNF + f] * sc[f] : 0.f;
+  for (int j = 0; j < NS; ++j) {
+    const int f = slot_feature(j, RU);
+    a1[j] = f >= 0 ? pk[kPkW1 + row * kNF + f] * sc[f] : 0.f;
   }
   float arow[3];       // RU: W1[row][13 + k] * s_(13 + k), the row term's weights
 #pragma unroll
@@ -132,12 +131,13 @@ __device__ __forceinline__ void apply_mfma_body(const StepCtx& c, const StepPara
   for (int q = 0; q < 16; ++q) a2[q] = pk[kPkW2 + row * kH + acc_row(q, half)];
 
   // Biases and W3 in accumulator-row order per lane half; read with
-  // ds_read_b128 when needed instead of holding 64 registers.
-  __shared__ float4 tab[4][2][4];   // {b1, b2, W3 dir, W3 mag} x half x 16 floats
-  if (threadIdx.x < 128) {
+  // ds_read_b128 when needed instead of holding 64 registers.  b1 is stored
+  // twice so that each layer-1 block loads its own copy (no register moves).
+  __shared__ float4 tab[5][2][4];   // {b1, b2, W3 dir, W3 mag, b1} x half x 16 floats
+  if (threadIdx.x < 160) {
     const int which = threadIdx.x >> 5, h = (threadIdx.x >> 4) & 1, q = threadIdx.x & 15;
     const int hr = acc_row(q, h);
-    const float v = which == 0 ? pk[kPkB1 + hr] : which == 1 ? pk[kPkB2 + hr]
+    const float v = which == 0 || which == 4 ? pk[kPkB1 + hr] : which == 1 ? pk[kPkB2 + hr]
                     : which == 2 ? pk[kPkW3 + hr] : pk[kPkW3 + kH + hr];
     reinterpret_cast<float*>(&tab[which][h][0])[q] = v;
   }
@@ -150,20 +150,20 @@ __device__ __forceinline__ void apply_mfma_body(const StepCtx& c, const StepPara
     const bool valid = e < ch.e1;
     Elem x;
     load_elem<VEC>(s, valid ? e : ch.e0, x);
-    const float p_decayed = x.p * hp.decay;  // before the swaps below overwrite F1 = p
+    const float p_decayed = x.p * hp.decay;
     float F[kNF], cn[3];
     build_features<VEC, NORMAL, NF>(hp, x, F, cn);
     // the accumulators are final here: storing them now frees their registers
-    // (and the copies the lane swaps below would need) during the MLP
+    // during the MLP
     if (valid) store_state<VEC>(s, e, x, cn);
 
-    f32x16 bias1, bias2;
+    f32x32 acc;  // registers 0..15: elements 0..31, 16..31: elements 32..63
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const float4 v = tab[0][half][q];
-      bias1[4 * q] = v.x; bias1[4 * q + 1] = v.y; bias1[4 * q + 2] = v.z; bias1[4 * q + 3] = v.w;
+      const float4 v = tab[0][half][q], u = tab[4][half][q];
+      acc[4 * q] = v.x; acc[4 * q + 1] = v.y; acc[4 * q + 2] = v.z; acc[4 * q + 3] = v.w;
+      acc[16 + 4 * q] = u.x; acc[16 + 4 * q + 1] = u.y; acc[16 + 4 * q + 2] = u.z; acc[16 + 4 * q + 3] = u.w;
     }
-    f32x16 accA = bias1, accB = bias1;
     float a_first = a1[0];
     if (RU) {
       // the row term of hidden unit `row` for this iteration's row (lane 0's
@@ -171,29 +171,29 @@ __device__ __forceinline__ void apply_mfma_body(const StepCtx& c, const StepPara
       const float r0 = __int_as_float(uni(__float_as_int(x.rq[0])));
       const float r1 = __int_as_float(uni(__float_as_int(x.rq[1])));
       const float r2 = __int_as_float(uni(__float_as_int(x.rq[2])));
-      const float rt = fmaf(arow[2], r2, fmaf(arow[1], r1, arow[0] * r0));
-      a_first = half ? a1[0] : rt;
+      a_first = fmaf(arow[2], r2, fmaf(arow[1], r1, arow[0] * r0));
     }
     // Higher issue priority while this wave runs its matrix-core chains: the
     // chains then issue back to back ahead of the other waves' vector work
     // (measured: 5 % fewer cycles than without).
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int q = 0; q < KS; ++q) {
-      const int f0 = slot_feature(2 * q, RU), f1 = slot_feature(2 * q + 1, RU);
-      const float x0 = f0 < 0 ? 1.f : f0 < NF ? F[f0] : 0.f;
-      const float x1 = f1 < 0 ? 1.f : f1 < NF ? F[f1] : 0.f;
-      float bA, bB;
-      swap_halves(x0, x1, bA, bB);
-      const float aq = q == 0 ? a_first : a1[q];
-      accA = __builtin_amdgcn_mfma_f32_32x32x2f32(aq, bA, accA, 0, 0, 0);
-      accB = __builtin_amdgcn_mfma_f32_32x32x2f32(aq, bB, accB, 0, 0, 0);
+    for (int j = 0; j < NS; ++j) {
+      const int f = slot_feature(j, RU);
+      acc = __builtin_amdgcn_mfma_f32_32x32x1f32(j == 0 ? a_first : a1[j], f < 0 ? 1.f : F[f], acc, 0, 0, 0);
+    }
+    f32x16 accA, accB;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      accA[q] = acc[q];
+      accB[q] = acc[16 + q];
     }
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       accA[q] = fmaxf(accA[q], 0.f);
       accB[q] = fmaxf(accB[q], 0.f);
     }
+    f32x16 bias2;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const float4 v = tab[1][half][q];
