@@ -31,6 +31,11 @@ EDGE_SHAPES = [(1,), (2,), (3,), (15,), (16,), (17,), (63,), (65,), (40000,),
 # features enter through the row-term slot
 ROW_UNIFORM_SHAPES = [(2, 64), (3, 128), (5, 192), (64, 64), (100, 320), (7, 4096), (300, 256)]
 
+# 2-D shapes whose column count is above 64 and not a multiple of it: the row
+# features enter as three slots, some wave iterations lie inside one row and
+# the others span two rows
+MIXED_ROW_SHAPES = [(9, 65), (40, 100), (17, 127), (12, 200), (6, 1000), (3, 4097), (70, 96), (2, 1025)]
+
 
 def mlp(n_time=11, bias_std=0.0):
     return W.mlp_weights(n_time, bias_std=bias_std)
@@ -55,6 +60,13 @@ def test_edge_shapes_ten_steps(impl):
 @pytest.mark.parametrize("n_feat", [L.LOPT_N_FEATURES, L.LOPT_VELO_FEATURES])
 def test_row_uniform_shapes_ten_steps(n_feat):
     w = W.custom_workload("rowuni", ROW_UNIFORM_SHAPES, grad_std=1e-2, steps=10, wid=104)
+    weights = W.mlp_weights(11, bias_std=0.1, n_feat=n_feat)
+    check(parity(w, weights, L.config_from(mlp_impl=L.LOPT_MLP_MFMA, n_feat=n_feat), torch))
+
+
+@pytest.mark.parametrize("n_feat", [L.LOPT_N_FEATURES, L.LOPT_VELO_FEATURES])
+def test_mixed_row_shapes_ten_steps(n_feat):
+    w = W.custom_workload("mixrow", MIXED_ROW_SHAPES, grad_std=1e-2, steps=10, wid=150)
     weights = W.mlp_weights(11, bias_std=0.1, n_feat=n_feat)
     check(parity(w, weights, L.config_from(mlp_impl=L.LOPT_MLP_MFMA, n_feat=n_feat), torch))
 
