@@ -27,6 +27,9 @@
  * All arithmetic on the device is fp32.  Every call returns an lopt_status;
  * no C++ exception crosses this boundary.  lopt_last_error() gives a
  * thread-local message for the last failing call on the calling thread.
+ * A handle is not thread-safe, and the calls on one handle must be ordered on
+ * the device: each step reads and writes the handle's workspace, so issue them
+ * on one stream (or order the streams yourself).
  */
 #ifndef LOPT_H
 #define LOPT_H
@@ -56,7 +59,8 @@ typedef enum lopt_status {
 typedef enum lopt_mlp_impl {
   LOPT_MLP_AUTO = 0, /* currently the matrix-core path */
   LOPT_MLP_VALU = 1, /* vector FMA, weights broadcast from scalar registers */
-  LOPT_MLP_MFMA = 2  /* fp32 matrix-core (v_mfma_f32_32x32x2_f32) path */
+  LOPT_MLP_MFMA = 2  /* fp32 matrix-core path (v_mfma_f32_32x32x1_2b_f32 and
+                        v_mfma_f32_32x32x2_f32) */
 } lopt_mlp_impl;
 
 /* Hyperparameters.  lopt_default_config() fills the defaults shown. */
@@ -119,8 +123,9 @@ size_t lopt_mlp_floats(int32_t n_feat, int32_t n_time);
  * allocation/copy failure -> HIP.  *out is set only on success. */
 lopt_status lopt_create(const lopt_config* cfg, const float* mlp_host, lopt_handle** out);
 
-/* Frees the handle and its device memory (not the caller's buffers).  The
- * caller must make sure no step using the handle is still running. */
+/* Frees the handle, its device memory and its pinned host buffer (not the
+ * caller's buffers).  The caller must make sure no step using the handle is
+ * still running. */
 void lopt_destroy(lopt_handle* h);
 
 /* Floats in one tensor's state buffer: 4*rows*cols + 3*(rows + cols);
@@ -140,6 +145,9 @@ lopt_status lopt_workspace_bytes(const lopt_handle* h, const lopt_tensor* ts, in
  * caller, which must keep it alive and untouched until the last lopt_step.
  * stream: a hipStream_t (NULL = default stream); the call returns after the
  * plan upload and the zero fill have been queued and the upload has finished.
+ * The first binding (and one with more tensors than any before) allocates a
+ * pinned host buffer of 2 n pointers, owned by the handle, through which
+ * lopt_step passes changed gradient pointers.
  * To start from pre-warmed accumulators, write the state buffers after this
  * call.  Errors: validation -> INVALID_ARGUMENT / UNSUPPORTED / WORKSPACE
  * (nothing is modified); a current device other than the handle's ->
@@ -151,10 +159,14 @@ lopt_status lopt_init_state(lopt_handle* h, const lopt_tensor* ts, int32_t n, vo
  * the step on `stream` and returns (asynchronous); the step's finalize kernel
  * advances t.  An empty list queues nothing and leaves t unchanged.  ts must
  * list the same tensors (param, state, rows, cols) in the same order as
- * lopt_init_state; grad pointers may differ (the plan's copy is refreshed,
- * which synchronises the stream, so it cannot happen while the stream is
- * being captured into a graph).  Errors: a different list -> STATE; bad
- * pointers, or a current device other than the handle's -> INVALID_ARGUMENT;
+ * lopt_init_state; grad pointers may differ from the previous call's: the new
+ * pointers are copied to the device on `stream` from the handle's pinned
+ * buffer (two slots used in turn; the host waits only for the copy queued two
+ * changes earlier, which has normally finished).  Such a change cannot be
+ * captured into a graph (INVALID_ARGUMENT while `stream` is capturing): call
+ * lopt_step once with the new gradients before capturing.  Errors: a
+ * different list -> STATE; bad pointers, or a current device other than the
+ * handle's -> INVALID_ARGUMENT;
  * launch failure -> HIP.  On a validation
  * error nothing is queued.  Non-finite inputs are not checked (they propagate
  * into the accumulators). */

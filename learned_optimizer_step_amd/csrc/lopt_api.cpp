@@ -306,6 +306,12 @@ struct lopt_handle {
   char* ws = nullptr;
   size_t ws_bytes = 0;
   std::vector<hipEvent_t> events;  // optional timing events (kNumKernels + 1)
+  // Gradient-pointer uploads: two slots of pinned host memory, used in turn;
+  // slot_done[k] is recorded after the copy that last read slot k.
+  const float** gp_pinned = nullptr;
+  size_t gp_cap = 0;               // pointers per slot
+  hipEvent_t slot_done[2] = {nullptr, nullptr};
+  int next_slot = 0;
 };
 
 namespace {
@@ -381,6 +387,45 @@ void check_device(const lopt_handle* h) {
   if (dev != h->device)
     fail(LOPT_ERR_INVALID_ARGUMENT, "current device " + std::to_string(dev) + " is not the handle's device " +
                                         std::to_string(h->device));
+}
+
+// Waits until no queued copy reads the pinned gradient-pointer slots.
+void drain_slots(lopt_handle* h) {
+  for (hipEvent_t e : h->slot_done)
+    if (e) hip_check(hipEventSynchronize(e), "hipEventSynchronize(gradient slot)");
+}
+
+// Pinned slots for n gradient pointers, and their events (created once).
+void reserve_slots(lopt_handle* h, size_t n) {
+  for (hipEvent_t& e : h->slot_done)
+    if (!e) hip_check(hipEventCreateWithFlags(&e, hipEventDisableTiming), "hipEventCreate");
+  if (n <= h->gp_cap && h->gp_pinned) return;
+  // allocate first: on failure the handle keeps its old slots
+  void* p = nullptr;
+  hip_check(hipHostMalloc(&p, 2 * std::max<size_t>(n, 1) * sizeof(const float*), hipHostMallocDefault),
+            "hipHostMalloc(gradient slots)");
+  drain_slots(h);
+  if (h->gp_pinned) (void)hipHostFree(h->gp_pinned);
+  h->gp_pinned = static_cast<const float**>(p);
+  h->gp_cap = std::max<size_t>(n, 1);
+}
+
+// Queues the copy of the gradient pointers of ts into the plan's table on s.
+// The source is a pinned slot that no queued copy still reads, so the host
+// does not wait for the stream.
+void upload_grads(lopt_handle* h, const lopt_tensor* ts, int32_t n, hipStream_t s) {
+  const int k = h->next_slot;
+  hip_check(hipEventSynchronize(h->slot_done[k]), "hipEventSynchronize(gradient slot)");
+  const float** slot = h->gp_pinned + size_t(k) * h->gp_cap;
+  for (int32_t i = 0; i < n; ++i) slot[i] = ts[i].grad;
+  hip_check(hipMemcpyAsync(h->ws + h->plan.off_grads, slot, sizeof(const float*) * size_t(n), hipMemcpyHostToDevice, s),
+            "hipMemcpyAsync(gradient pointers)");
+  hip_check(hipEventRecord(h->slot_done[k], s), "hipEventRecord(gradient slot)");
+  h->next_slot = k ^ 1;
+  for (int32_t i = 0; i < n; ++i) {
+    h->plan.grads[i] = ts[i].grad;
+    h->plan.bound[i].grad = ts[i].grad;
+  }
 }
 
 void check_same_list(const lopt_handle* h, const lopt_tensor* ts, int32_t n, bool* grads_changed) {
@@ -462,6 +507,12 @@ lopt_status lopt_create(const lopt_config* cfg, const float* mlp_host, lopt_hand
 
 void lopt_destroy(lopt_handle* h) {
   if (!h) return;
+  for (hipEvent_t e : h->slot_done)
+    if (e) {
+      (void)hipEventSynchronize(e);
+      (void)hipEventDestroy(e);
+    }
+  if (h->gp_pinned) (void)hipHostFree(h->gp_pinned);
   if (h->d_mlp) (void)hipFree(h->d_mlp);
   delete h;
 }
@@ -486,13 +537,16 @@ lopt_status lopt_init_state(lopt_handle* h, const lopt_tensor* ts, int32_t n, vo
     if (ws_bytes < pl.total)
       fail(LOPT_ERR_WORKSPACE, "workspace too small: need " + std::to_string(pl.total) + " bytes");
     hipStream_t s = static_cast<hipStream_t>(stream);
+    reserve_slots(h, size_t(n));
+    drain_slots(h);  // a queued gradient-pointer copy of the previous binding may still target the old workspace
     char* ws = static_cast<char*>(workspace);
+    const std::vector<int64_t> step0{0};
     upload(ws, pl.off_desc, pl.desc, s);
     upload(ws, pl.off_grads, pl.grads, s);
     upload(ws, pl.off_tiles0, pl.tiles0, s);
     upload(ws, pl.off_segs1, pl.segs1, s);
     upload(ws, pl.off_chunks, pl.chunks, s);
-    upload(ws, pl.off_step, std::vector<int64_t>{0}, s);
+    upload(ws, pl.off_step, step0, s);
     hip_check(hipStreamSynchronize(s), "hipStreamSynchronize(plan upload)");
     h->plan = std::move(pl);
     h->ws = ws;
@@ -510,12 +564,12 @@ lopt_status lopt_step(lopt_handle* h, const lopt_tensor* ts, int32_t n, void* st
     check_device(h);
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (grads_changed) {
-      for (int32_t i = 0; i < n; ++i) {
-        h->plan.grads[i] = ts[i].grad;
-        h->plan.bound[i].grad = ts[i].grad;
-      }
-      upload(h->ws, h->plan.off_grads, h->plan.grads, s);
-      hip_check(hipStreamSynchronize(s), "hipStreamSynchronize(grad pointer upload)");
+      hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+      hip_check(hipStreamIsCapturing(s, &cs), "hipStreamIsCapturing");
+      if (cs != hipStreamCaptureStatusNone)
+        fail(LOPT_ERR_INVALID_ARGUMENT,
+             "gradient pointers changed while the stream is being captured: step once with them before capturing");
+      upload_grads(h, ts, n, s);
     }
     const StepParams p = make_params(h);
     hip_check(launch_step(make_ctx(h), p, s, h->events.empty() ? nullptr : h->events.data()), "launch(step)");

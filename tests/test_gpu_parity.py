@@ -196,6 +196,45 @@ def test_resume_equals_uninterrupted_and_grad_pointers_may_change():
     run2.close()
 
 
+def test_grad_pointer_changes_queued_without_waiting():
+    # gradients of steps 1..8 staged on the device first, then eight steps
+    # queued back to back, each with a different gradient tensor: every step
+    # must read its own pointers (the pinned slots are reused from step 3 on)
+    shapes = [(48, 80), (1, 300), (7, 129)]
+    m = mlp(bias_std=0.1)
+    w = W.custom_workload("gptr", shapes, grad_std=1e-2, steps=8, wid=160)
+    # reference: one gradient buffer per tensor for all steps (pointers never change)
+    ref_params = [torch.from_numpy(W.param_init(w, i).reshape(t.shape)).cuda() for i, t in enumerate(w.tensors)]
+    fixed = [torch.empty(t.shape, device="cuda") for t in w.tensors]
+    ref_opt = L.LOpt(ref_params, m, L.config_from())
+    for t in range(1, 9):
+        for i, tt in enumerate(w.tensors):
+            fixed[i].copy_(torch.from_numpy(W.grad_at(w, i, t).reshape(tt.shape)))
+        ref_opt.step(fixed)
+    torch.cuda.synchronize()
+    ref = []
+    for i, tt in enumerate(w.tensors):
+        v = ref_opt.state_views(i)
+        ref.append({k: v[k].cpu().numpy() for k in ("m", "v", "r", "c")})
+        ref[-1]["p"] = ref_params[i].cpu().numpy().reshape(tt.rows, tt.cols)
+    ref_opt.close()
+    params = [torch.from_numpy(W.param_init(w, i).reshape(t.shape)).cuda() for i, t in enumerate(w.tensors)]
+    staged = [[torch.from_numpy(W.grad_at(w, i, t).reshape(tt.shape)).cuda() for i, tt in enumerate(w.tensors)]
+              for t in range(1, 9)]
+    opt = L.LOpt(params, m, L.config_from())
+    torch.cuda.synchronize()
+    for t in range(8):
+        opt.step(staged[t])
+    torch.cuda.synchronize()
+    assert opt.t == 8
+    for i, tt in enumerate(w.tensors):
+        v = opt.state_views(i)
+        assert np.array_equal(params[i].cpu().numpy().reshape(tt.rows, tt.cols), ref[i]["p"]), i
+        for k in ("m", "v", "r", "c"):
+            assert np.array_equal(v[k].cpu().numpy(), ref[i][k]), (i, k)
+    opt.close()
+
+
 def test_step_rejects_a_different_list():
     p = torch.zeros(4, 4, device="cuda")
     q = torch.zeros(4, 4, device="cuda")
