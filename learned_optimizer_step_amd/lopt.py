@@ -239,15 +239,17 @@ class LOpt:
             self._table["rows"][:n] = [r for r, _ in self.shapes]
             self._table["cols"][:n] = [c for _, c in self.shapes]
         self._table_ptr = self._table.ctypes.data_as(ctypes.POINTER(lopt_tensor))
-        self.handle = lopt_create(self.cfg, mlp)
         lib = load_library()
-        ws = ctypes.c_size_t()
-        # gradients are first needed by lopt_step: NULL grad pointers here
-        _check(lib.lopt_workspace_bytes(self.handle, self._table_ptr, n, ctypes.byref(ws)))
-        self.ws_bytes = int(ws.value)
-        self.workspace = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)
-        _check(lib.lopt_init_state(self.handle, self._table_ptr, n, ctypes.c_void_p(self.workspace.data_ptr()),
-                                   self.ws_bytes, ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)))
+        # the handle belongs to the device that is current at lopt_create: the parameters'
+        with torch.cuda.device(dev):
+            self.handle = lopt_create(self.cfg, mlp)
+            ws = ctypes.c_size_t()
+            # gradients are first needed by lopt_step: NULL grad pointers here
+            _check(lib.lopt_workspace_bytes(self.handle, self._table_ptr, n, ctypes.byref(ws)))
+            self.ws_bytes = int(ws.value)
+            self.workspace = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)
+            _check(lib.lopt_init_state(self.handle, self._table_ptr, n, ctypes.c_void_p(self.workspace.data_ptr()),
+                                       self.ws_bytes, ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)))
 
     def step(self, grads) -> None:
         grads = list(grads)
@@ -261,8 +263,9 @@ class LOpt:
                                  "on the parameters' device")
         if n:
             self._table["grad"][:n] = [g.data_ptr() for g in grads]
-        _check(load_library().lopt_step(self.handle, self._table_ptr, n,
-                                        ctypes.c_void_p(self.torch.cuda.current_stream(dev).cuda_stream)))
+        with self.torch.cuda.device(dev):
+            _check(load_library().lopt_step(self.handle, self._table_ptr, n,
+                                            ctypes.c_void_p(self.torch.cuda.current_stream(dev).cuda_stream)))
 
     @property
     def t(self) -> int:
