@@ -149,7 +149,9 @@ __device__ __forceinline__ void apply_mfma_body(const StepCtx& c, const StepPara
     const uint32_t e = base + lane;
     const bool valid = e < ch.e1;
     Elem x;
-    load_elem<VEC>(s, valid ? e : ch.e0, x);
+    // an invalid lane loads the wave's first element instead (inside the
+    // chunk, and in the same row when the iteration lies in one row)
+    load_elem<VEC, RU && !VEC>(s, valid ? e : base, x, base);
     const float p_decayed = x.p * hp.decay;
     float F[kNF], cn[3];
     build_features<VEC, NORMAL, NF>(hp, x, F, cn);

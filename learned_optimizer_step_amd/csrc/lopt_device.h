@@ -251,8 +251,11 @@ __device__ __forceinline__ void build_features(const StepParams& hp, Elem& x, fl
 // Loads the inputs of element e of the chunk.  All byte offsets fit in 32
 // bits: a chunk spans at most kChunkElems elements (and rows), and the host
 // rejects 2-D tensors with 2^28 or more columns (16-byte column records).
-template <bool VEC>
-__device__ __forceinline__ void load_elem(const Streams& s, uint32_t e, Elem& x) {
+// ROW (2-D only): the caller guarantees that e lies in the same row as the
+// wave-uniform element `row_elem`; the row index is then divided once for the
+// wave (scalar unit) and the row record read with one uniform load.
+template <bool VEC, bool ROW = false>
+__device__ __forceinline__ void load_elem(const Streams& s, uint32_t e, Elem& x, uint32_t row_elem = 0) {
   const uint32_t off = (e - s.e0) * 4u;
   x.g = ldb_stream(s.g, off);
   x.p = ldb_stream(s.p, off);
@@ -266,7 +269,7 @@ __device__ __forceinline__ void load_elem(const Streams& s, uint32_t e, Elem& x)
       x.rq[k] = s.rq[k];
     }
   } else {
-    const uint32_t i = div_c(e, s.cmagic, s.cshift);
+    const uint32_t i = ROW ? div_c(row_elem, s.cmagic, s.cshift) : div_c(e, s.cmagic, s.cshift);
     const uint32_t j = e - i * s.C;
     const f32x4 r4 = ldb4(s.rq, (i - s.i0) * 16u);
     const f32x4 c4 = ldb4(s.cq, j * 16u);
