@@ -127,6 +127,7 @@ __device__ __forceinline__ void apply_mfma_body(const StepCtx& c, const StepPara
   float arow[3];       // RU: W1[row][13 + k] * s_(13 + k), the row term's weights
 #pragma unroll
   for (int k = 0; k < 3; ++k) arow[k] = RU ? pk[kPkW1 + row * kNF + 13 + k] * sc[13 + k] : 0.f;
+  const float b1row = RU ? pk[kPkB1 + row] : 0.f;  // RU: b1 rides in the row-term slot
 #pragma unroll
   for (int q = 0; q < 16; ++q) a2[q] = pk[kPkW2 + row * kH + acc_row(q, half)];
 
@@ -160,20 +161,25 @@ __device__ __forceinline__ void apply_mfma_body(const StepCtx& c, const StepPara
     if (valid) store_state<VEC>(s, e, x, cn);
 
     f32x32 acc;  // registers 0..15: elements 0..31, 16..31: elements 32..63
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float4 v = tab[0][half][q], u = tab[4][half][q];
-      acc[4 * q] = v.x; acc[4 * q + 1] = v.y; acc[4 * q + 2] = v.z; acc[4 * q + 3] = v.w;
-      acc[16 + 4 * q] = u.x; acc[16 + 4 * q + 1] = u.y; acc[16 + 4 * q + 2] = u.z; acc[16 + 4 * q + 3] = u.w;
-    }
     float a_first = a1[0];
     if (RU) {
-      // the row term of hidden unit `row` for this iteration's row (lane 0's
-      // element is always inside the chunk)
+      // The constant slot (B = 1) adds its A value to every element's hidden
+      // unit, as a bias does: it carries b1 plus the row term of hidden unit
+      // `row` for this iteration's row (lane 0's element is always inside the
+      // chunk), and the chain starts from zero.
       const float r0 = __int_as_float(uni(__float_as_int(x.rq[0])));
       const float r1 = __int_as_float(uni(__float_as_int(x.rq[1])));
       const float r2 = __int_as_float(uni(__float_as_int(x.rq[2])));
-      a_first = fmaf(arow[2], r2, fmaf(arow[1], r1, arow[0] * r0));
+      a_first = fmaf(arow[2], r2, fmaf(arow[1], r1, fmaf(arow[0], r0, b1row)));
+#pragma unroll
+      for (int q = 0; q < 32; ++q) acc[q] = 0.f;
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 v = tab[0][half][q], u = tab[4][half][q];
+        acc[4 * q] = v.x; acc[4 * q + 1] = v.y; acc[4 * q + 2] = v.z; acc[4 * q + 3] = v.w;
+        acc[16 + 4 * q] = u.x; acc[16 + 4 * q + 1] = u.y; acc[16 + 4 * q + 2] = u.z; acc[16 + 4 * q + 3] = u.w;
+      }
     }
     // Higher issue priority while this wave runs its matrix-core chains: the
     // chains then issue back to back ahead of the other waves' vector work
