@@ -38,17 +38,25 @@ def log(msg):
 
 
 # Sources of the apply kernel; the committed HBM-traffic figure is only valid
-# for the exact sources it was measured on.
+# for the code it was measured on (comments and blank lines do not count).
 APPLY_SOURCES = ("learned_optimizer_step_amd/csrc/lopt_apply.hip", "learned_optimizer_step_amd/csrc/lopt_device.h",
                  "learned_optimizer_step_amd/csrc/lopt_internal.h")
+
+
+def code_text(src: str) -> str:
+    """C++ source without comments, trailing blanks and empty lines."""
+    import re
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    lines = (re.sub(r"//.*$", "", line).rstrip() for line in src.splitlines())
+    return "\n".join(line for line in lines if line.strip())
 
 
 def apply_sources_sha() -> str:
     import hashlib
     h = hashlib.sha256()
     for p in APPLY_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p)) as f:
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -80,10 +80,12 @@ __global__ __launch_bounds__(kBlock) void k_apply_valu(StepCtx c, StepParams hp)
 //     lane%32 (+32 for the second block), which is exactly a K-step B operand
 //     if W2's columns are visited in that order (no data movement).
 //   layer 3 (32 -> 2) on the vector ALU: per-lane partial dot products over
-//     the lane's 16 hidden units, completed with one lane swap.
-// Biases enter as the C operand of the first MFMA of each chain (read from
-// LDS with W3 each iteration, which keeps the kernel within 128 VGPRs); the
-// feature scales s_d are folded into W1's columns once per chunk.
+//     the lane's 16 hidden units, completed with one lane swap per output.
+// b1 rides in the row-term slot where there is one (the layer-1 chain then
+// starts from zero); otherwise, and for b2, a bias is the C operand of the
+// first MFMA of its chain.  Biases and W3 are read from LDS each iteration,
+// which keeps the kernel within 128 VGPRs; the feature scales s_d are folded
+// into W1's columns once per chunk.
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x32 __attribute__((ext_vector_type(32)));
 
@@ -99,8 +101,8 @@ __device__ __forceinline__ void swap_halves(float x, float y, float& lo, float& 
 // Layer-1 slots, one per instruction.  Normally slot s holds feature s.
 // With RU (a 1-D tensor, or a wave iteration inside one row) the row features
 // F13..F15 are constant over the iteration: their weighted sum, the row term,
-// becomes the A operand of slot 0 (whose B value is 1), and slots 1, 2, ...
-// hold the other features in order.  -1: the constant slot.
+// plus b1 becomes the A operand of slot 0 (whose B value is 1), and slots 1,
+// 2, ... hold the other features in order.  -1: the constant slot.
 __device__ constexpr int slot_feature(int s, bool ru) {
   return !ru ? s : s == 0 ? -1 : (s - 1 < 13 ? s - 1 : s + 2);
 }
