@@ -119,7 +119,7 @@ def main():
                     help="after the timed steps, run one plain 1 GiB device copy (reference for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the library has no "
               f"multi-GPU path", file=sys.stderr)
         sys.exit(2)
 
