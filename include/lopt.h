@@ -146,8 +146,8 @@ lopt_status lopt_workspace_bytes(const lopt_handle* h, const lopt_tensor* ts, in
  * stream: a hipStream_t (NULL = default stream); the call returns after the
  * plan upload and the zero fill have been queued and the upload has finished.
  * The first binding (and one with more tensors than any before) allocates a
- * pinned host buffer of 2 n pointers, owned by the handle, through which
- * lopt_step passes changed gradient pointers.
+ * pinned host buffer of 32 bytes per tensor, owned by the handle, through which
+ * lopt_step passes changed gradient pointers and per-tensor values.
  * To start from pre-warmed accumulators, write the state buffers after this
  * call.  Errors: validation -> INVALID_ARGUMENT / UNSUPPORTED / WORKSPACE
  * (nothing is modified); a current device other than the handle's ->
@@ -162,9 +162,10 @@ lopt_status lopt_init_state(lopt_handle* h, const lopt_tensor* ts, int32_t n, vo
  * lopt_init_state; grad pointers may differ from the previous call's: the new
  * pointers are copied to the device on `stream` from the handle's pinned
  * buffer (two slots used in turn; the host waits only for the copy queued two
- * changes earlier, which has normally finished).  Such a change cannot be
- * captured into a graph (INVALID_ARGUMENT while `stream` is capturing): call
- * lopt_step once with the new gradients before capturing.  Errors: a
+ * changes earlier, which has normally finished), as are per-tensor values set
+ * since the last step.  Such a change cannot be captured into a graph
+ * (INVALID_ARGUMENT while `stream` is capturing): call lopt_step once with
+ * the new gradients before capturing.  Errors: a
  * different list -> STATE; bad pointers, or a current device other than the
  * handle's -> INVALID_ARGUMENT;
  * launch failure -> HIP.  On a validation
@@ -192,6 +193,21 @@ lopt_status lopt_set_step(lopt_handle* h, int64_t t);
  * Errors: invalid config, or n_feat or n_time different from lopt_create's
  * -> INVALID_ARGUMENT (the handle keeps its previous config). */
 lopt_status lopt_set_config(lopt_handle* h, const lopt_config* cfg);
+
+/* Per-tensor learning rate and weight decay, as torch's parameter groups give
+ * them (the PyLO page, "Library design": the optimizer is a torch optimizer;
+ * decoupled weight decay as in lopt_config).  lr[i] and weight_decay[i]
+ * replace the config's lr and weight_decay for tensor i of the bound list in
+ * the following lopt_step calls; tensor i then gets
+ *   p <- p - lr[i] u - lr[i] weight_decay[i] p.
+ * Both NULL: back to the config's values for every tensor.  n: the bound
+ * list's length.  The arrays are copied on the host; the next lopt_step queues
+ * the device copy on its stream through the handle's pinned buffer (no wait),
+ * so such a step cannot be captured into a graph (INVALID_ARGUMENT while its
+ * stream is capturing).  lopt_init_state forgets the values.  Errors: no bound
+ * list or n different from its length -> STATE; exactly one NULL array or a
+ * non-finite value -> INVALID_ARGUMENT (nothing changes). */
+lopt_status lopt_set_tensor_hyper(lopt_handle* h, const float* lr, const float* weight_decay, int32_t n);
 
 /* Kernels of one step, in launch order. */
 #define LOPT_N_KERNELS 5 /* row/col sums, moving averages, statistics, finalize, apply */

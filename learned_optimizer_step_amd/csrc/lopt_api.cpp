@@ -78,7 +78,7 @@ struct Plan {
   uint32_t chunk_elems = 0;
   // byte offsets inside the workspace
   size_t off_desc = 0, off_grads = 0, off_tiles0 = 0, off_segs1 = 0, off_chunks = 0;
-  size_t off_rbar = 0, off_stats = 0, off_scales = 0, off_packed = 0, off_step = 0, off_floats = 0;
+  size_t off_rbar = 0, off_stats = 0, off_scales = 0, off_packed = 0, off_step = 0, off_th = 0, off_floats = 0;
   size_t floats = 0;  // per-tensor float arrays (row/col partials, rq, cq)
   size_t total = 0;
   std::vector<lopt_tensor> bound;
@@ -282,6 +282,7 @@ Plan build_plan(const lopt_tensor* ts, int32_t n) {
   pl.off_scales = take(sizeof(float) * kStatStride * pl.desc.size());
   pl.off_packed = take(sizeof(float) * kPkFloats);
   pl.off_step = take(sizeof(int64_t));
+  pl.off_th = take(sizeof(float) * 2 * pl.desc.size());
   pl.off_floats = take(sizeof(float) * pl.floats);
   pl.total = off;
   // per-tensor float offsets are relative to the workspace base
@@ -306,10 +307,15 @@ struct lopt_handle {
   char* ws = nullptr;
   size_t ws_bytes = 0;
   std::vector<hipEvent_t> events;  // optional timing events (kNumKernels + 1)
-  // Gradient-pointer uploads: two slots of pinned host memory, used in turn;
-  // slot_done[k] is recorded after the copy that last read slot k.
-  const float** gp_pinned = nullptr;
-  size_t gp_cap = 0;               // pointers per slot
+  // Per-tensor learning rates and weight decays (lopt_set_tensor_hyper).
+  bool th_active = false;          // the step uses them instead of cfg.lr / cfg.weight_decay
+  bool th_dirty = false;           // the device copy is out of date
+  std::vector<float> th_lr, th_wd;
+  // Uploads between steps (gradient pointers, per-tensor pairs): two slots of
+  // pinned host memory used in turn, each [cap pointers][cap x 2 floats];
+  // slot_done[k] is recorded after the copies that last read slot k.
+  char* staging = nullptr;
+  size_t staging_cap = 0;          // tensors per slot
   hipEvent_t slot_done[2] = {nullptr, nullptr};
   int next_slot = 0;
 };
@@ -330,6 +336,7 @@ StepCtx make_ctx(const lopt_handle* h) {
   c.scales = reinterpret_cast<float*>(h->ws + pl.off_scales);
   c.packed = reinterpret_cast<float*>(h->ws + pl.off_packed);
   c.step = reinterpret_cast<int64_t*>(h->ws + pl.off_step);
+  c.tensor_hyper = reinterpret_cast<const float*>(h->ws + pl.off_th);
   c.mlp = h->d_mlp;
   c.n_tensors = int32_t(pl.desc.size());
   c.n_tiles0 = int32_t(pl.tiles0.size());
@@ -365,6 +372,7 @@ StepParams make_params(const lopt_handle* h) {
   bool normal = c.eps_v >= 2.0f * FLT_MIN;
   for (int k = 0; k < 3; ++k) normal = normal && p.omb_f[k] * c.eps_f >= 2.0f * FLT_MIN;
   p.rsq_normal = normal ? 1 : 0;
+  p.per_tensor = h->th_active ? 1 : 0;
   p.n_time = c.n_time;
   p.n_feat = c.n_feat;
   for (int q = 0; q < kMaxTime; ++q) p.timescales[q] = q < c.n_time ? c.timescales[q] : 1.f;
@@ -389,43 +397,61 @@ void check_device(const lopt_handle* h) {
                                         std::to_string(h->device));
 }
 
-// Waits until no queued copy reads the pinned gradient-pointer slots.
+// Waits until no queued copy reads the pinned staging slots.
 void drain_slots(lopt_handle* h) {
   for (hipEvent_t e : h->slot_done)
-    if (e) hip_check(hipEventSynchronize(e), "hipEventSynchronize(gradient slot)");
+    if (e) hip_check(hipEventSynchronize(e), "hipEventSynchronize(staging slot)");
 }
 
-// Pinned slots for n gradient pointers, and their events (created once).
+size_t slot_bytes(size_t cap) { return cap * (sizeof(const float*) + 2 * sizeof(float)); }
+
+// Pinned staging slots for n tensors, and their events (created once).
 void reserve_slots(lopt_handle* h, size_t n) {
   for (hipEvent_t& e : h->slot_done)
     if (!e) hip_check(hipEventCreateWithFlags(&e, hipEventDisableTiming), "hipEventCreate");
-  if (n <= h->gp_cap && h->gp_pinned) return;
+  if (n <= h->staging_cap && h->staging) return;
   // allocate first: on failure the handle keeps its old slots
+  const size_t cap = std::max<size_t>(n, 1);
   void* p = nullptr;
-  hip_check(hipHostMalloc(&p, 2 * std::max<size_t>(n, 1) * sizeof(const float*), hipHostMallocDefault),
-            "hipHostMalloc(gradient slots)");
+  hip_check(hipHostMalloc(&p, 2 * slot_bytes(cap), hipHostMallocDefault), "hipHostMalloc(staging slots)");
   drain_slots(h);
-  if (h->gp_pinned) (void)hipHostFree(h->gp_pinned);
-  h->gp_pinned = static_cast<const float**>(p);
-  h->gp_cap = std::max<size_t>(n, 1);
+  if (h->staging) (void)hipHostFree(h->staging);
+  h->staging = static_cast<char*>(p);
+  h->staging_cap = cap;
 }
 
-// Queues the copy of the gradient pointers of ts into the plan's table on s.
-// The source is a pinned slot that no queued copy still reads, so the host
-// does not wait for the stream.
-void upload_grads(lopt_handle* h, const lopt_tensor* ts, int32_t n, hipStream_t s) {
+// Queues, on s, the copies of whatever changed since the last step into the
+// plan's tables: the gradient pointers of ts and/or the per-tensor (decay,
+// lr_step) pairs.  The source is a pinned slot that no queued copy still
+// reads, so the host does not wait for the stream.
+void upload_changes(lopt_handle* h, const lopt_tensor* ts, int32_t n, bool grads, bool pairs, hipStream_t s) {
   const int k = h->next_slot;
-  hip_check(hipEventSynchronize(h->slot_done[k]), "hipEventSynchronize(gradient slot)");
-  const float** slot = h->gp_pinned + size_t(k) * h->gp_cap;
-  for (int32_t i = 0; i < n; ++i) slot[i] = ts[i].grad;
-  hip_check(hipMemcpyAsync(h->ws + h->plan.off_grads, slot, sizeof(const float*) * size_t(n), hipMemcpyHostToDevice, s),
-            "hipMemcpyAsync(gradient pointers)");
-  hip_check(hipEventRecord(h->slot_done[k], s), "hipEventRecord(gradient slot)");
-  h->next_slot = k ^ 1;
-  for (int32_t i = 0; i < n; ++i) {
-    h->plan.grads[i] = ts[i].grad;
-    h->plan.bound[i].grad = ts[i].grad;
+  hip_check(hipEventSynchronize(h->slot_done[k]), "hipEventSynchronize(staging slot)");
+  char* slot = h->staging + size_t(k) * slot_bytes(h->staging_cap);
+  if (grads) {
+    const float** gp = reinterpret_cast<const float**>(slot);
+    for (int32_t i = 0; i < n; ++i) gp[i] = ts[i].grad;
+    hip_check(hipMemcpyAsync(h->ws + h->plan.off_grads, gp, sizeof(const float*) * size_t(n), hipMemcpyHostToDevice, s),
+              "hipMemcpyAsync(gradient pointers)");
   }
+  if (pairs) {
+    float* th = reinterpret_cast<float*>(slot + sizeof(const float*) * h->staging_cap);
+    for (int32_t i = 0; i < n; ++i) {
+      // the same fp32 expressions as the whole-list values in make_params
+      th[2 * i] = 1.0f - h->th_lr[i] * h->th_wd[i];
+      th[2 * i + 1] = h->th_lr[i] * h->cfg.step_mult;
+    }
+    hip_check(hipMemcpyAsync(h->ws + h->plan.off_th, th, 2 * sizeof(float) * size_t(n), hipMemcpyHostToDevice, s),
+              "hipMemcpyAsync(per-tensor hyperparameters)");
+  }
+  hip_check(hipEventRecord(h->slot_done[k], s), "hipEventRecord(staging slot)");
+  h->next_slot = k ^ 1;
+  if (grads)
+    for (int32_t i = 0; i < n; ++i) {
+      h->plan.grads[i] = ts[i].grad;
+      h->plan.bound[i].grad = ts[i].grad;
+    }
+  if (pairs) h->th_dirty = false;
 }
 
 void check_same_list(const lopt_handle* h, const lopt_tensor* ts, int32_t n, bool* grads_changed) {
@@ -512,7 +538,7 @@ void lopt_destroy(lopt_handle* h) {
       (void)hipEventSynchronize(e);
       (void)hipEventDestroy(e);
     }
-  if (h->gp_pinned) (void)hipHostFree(h->gp_pinned);
+  if (h->staging) (void)hipHostFree(h->staging);
   if (h->d_mlp) (void)hipFree(h->d_mlp);
   delete h;
 }
@@ -538,7 +564,7 @@ lopt_status lopt_init_state(lopt_handle* h, const lopt_tensor* ts, int32_t n, vo
       fail(LOPT_ERR_WORKSPACE, "workspace too small: need " + std::to_string(pl.total) + " bytes");
     hipStream_t s = static_cast<hipStream_t>(stream);
     reserve_slots(h, size_t(n));
-    drain_slots(h);  // a queued gradient-pointer copy of the previous binding may still target the old workspace
+    drain_slots(h);  // a queued copy of the previous binding may still target the old workspace
     char* ws = static_cast<char*>(workspace);
     const std::vector<int64_t> step0{0};
     upload(ws, pl.off_desc, pl.desc, s);
@@ -552,6 +578,9 @@ lopt_status lopt_init_state(lopt_handle* h, const lopt_tensor* ts, int32_t n, vo
     h->ws = ws;
     h->ws_bytes = ws_bytes;
     h->bound = true;
+    h->th_active = h->th_dirty = false;  // per-tensor values belong to the previous list
+    h->th_lr.clear();
+    h->th_wd.clear();
     hip_check(launch_zero_state(make_ctx(h), s), "launch(zero state)");
   });
 }
@@ -563,13 +592,15 @@ lopt_status lopt_step(lopt_handle* h, const lopt_tensor* ts, int32_t n, void* st
     check_same_list(h, ts, n, &grads_changed);
     check_device(h);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (grads_changed) {
+    const bool pairs_changed = h->th_active && h->th_dirty;
+    if (grads_changed || pairs_changed) {
       hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
       hip_check(hipStreamIsCapturing(s, &cs), "hipStreamIsCapturing");
       if (cs != hipStreamCaptureStatusNone)
         fail(LOPT_ERR_INVALID_ARGUMENT,
-             "gradient pointers changed while the stream is being captured: step once with them before capturing");
-      upload_grads(h, ts, n, s);
+             "gradient pointers or per-tensor hyperparameters changed while the stream is being captured: "
+             "step once with them before capturing");
+      upload_changes(h, ts, n, grads_changed, pairs_changed, s);
     }
     const StepParams p = make_params(h);
     hip_check(launch_step(make_ctx(h), p, s, h->events.empty() ? nullptr : h->events.data()), "launch(step)");
@@ -605,6 +636,29 @@ lopt_status lopt_set_config(lopt_handle* h, const lopt_config* cfg) {
     if (cfg->n_time != h->cfg.n_time || cfg->n_feat != h->cfg.n_feat)
       fail(LOPT_ERR_INVALID_ARGUMENT, "n_feat and n_time are fixed by the MLP weights given to lopt_create");
     h->cfg = *cfg;
+    if (h->th_active) h->th_dirty = true;  // lr_step depends on step_mult
+  });
+}
+
+lopt_status lopt_set_tensor_hyper(lopt_handle* h, const float* lr, const float* weight_decay, int32_t n) {
+  return guarded([&] {
+    if (!h) fail(LOPT_ERR_INVALID_ARGUMENT, "handle is NULL");
+    if (!h->bound) fail(LOPT_ERR_STATE, "lopt_init_state has not been called");
+    if (n != int32_t(h->plan.bound.size())) fail(LOPT_ERR_STATE, "n differs from the bound tensor count");
+    if (!lr && !weight_decay) {
+      h->th_active = h->th_dirty = false;
+      h->th_lr.clear();
+      h->th_wd.clear();
+      return;
+    }
+    if (!lr || !weight_decay) fail(LOPT_ERR_INVALID_ARGUMENT, "lr and weight_decay must both be given or both be NULL");
+    for (int32_t i = 0; i < n; ++i)
+      if (!std::isfinite(lr[i]) || !std::isfinite(weight_decay[i]))
+        fail(LOPT_ERR_INVALID_ARGUMENT, "tensor " + std::to_string(i) + ": lr and weight_decay must be finite");
+    h->th_lr.assign(lr, lr + n);
+    h->th_wd.assign(weight_decay, weight_decay + n);
+    h->th_active = n > 0;
+    h->th_dirty = h->th_active;
   });
 }
 

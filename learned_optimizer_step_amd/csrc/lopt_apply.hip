@@ -21,6 +21,8 @@ __device__ __forceinline__ void apply_valu_body(const StepCtx& c, const StepPara
   const Streams s = make_streams(d, g, c.ws, ch);
   const float* __restrict__ pk = c.packed;
   const float* __restrict__ sc = c.scales + size_t(ch.tensor) * kStatStride;
+  float decay, lr_step;
+  update_constants(c, hp, ch, decay, lr_step);
   for (uint32_t e = ch.e0 + threadIdx.x; e < ch.e1; e += kBlock) {
     Elem x;
     load_elem<VEC>(s, e, x);
@@ -48,7 +50,7 @@ __device__ __forceinline__ void apply_valu_body(const StepCtx& c, const StepPara
       dir = fmaf(pk[kPkW3 + o], a, dir);
       mag = fmaf(pk[kPkW3 + kH + o], a, mag);
     }
-    store_param(s, e, fmaf(-hp.lr_step, dir * __builtin_amdgcn_exp2f(mag * hp.exp2_mult), p_old * hp.decay));
+    store_param(s, e, fmaf(-lr_step, dir * __builtin_amdgcn_exp2f(mag * hp.exp2_mult), p_old * decay));
   }
 }
 
@@ -146,6 +148,8 @@ __device__ __forceinline__ void apply_mfma_body(const StepCtx& c, const StepPara
   }
   __syncthreads();
   const float b3d = pk[kPkB3], b3m = pk[kPkB3 + 1];
+  float decay, lr_step;
+  update_constants(c, hp, ch, decay, lr_step);
   uint32_t base = ch.e0 + wave * 64;
   if (base >= ch.e1) return;  // this wave has no elements in the chunk
   for (; base < ch.e1; base += kBlock) {
@@ -155,7 +159,7 @@ __device__ __forceinline__ void apply_mfma_body(const StepCtx& c, const StepPara
     // an invalid lane loads the wave's first element instead (inside the
     // chunk, and in the same row when the iteration lies in one row)
     load_elem<VEC, RU && !VEC>(s, valid ? e : base, x, base);
-    const float p_decayed = x.p * hp.decay;
+    const float p_decayed = x.p * decay;
     float F[kNF], cn[3];
     build_features<VEC, NORMAL, NF>(hp, x, F, cn);
     // the accumulators are final here: storing them now frees their registers
@@ -242,7 +246,7 @@ __device__ __forceinline__ void apply_mfma_body(const StepCtx& c, const StepPara
     swap_halves(mA, mB, m0, m1);
     const float dir = d0 + d1;
     const float mag = m0 + m1;
-    if (valid) store_param(s, e, fmaf(-hp.lr_step, dir * __builtin_amdgcn_exp2f(mag * hp.exp2_mult), p_decayed));
+    if (valid) store_param(s, e, fmaf(-lr_step, dir * __builtin_amdgcn_exp2f(mag * hp.exp2_mult), p_decayed));
   }
 }
 

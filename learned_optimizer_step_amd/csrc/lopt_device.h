@@ -291,6 +291,18 @@ __device__ __forceinline__ void store_state(const Streams& s, uint32_t e, const 
   }
 }
 
+// The update constants of the chunk's tensor: (decay, lr_step) = (1 - lr wd,
+// lr step_mult) from the step, or the tensor's own pair (wave-uniform).
+__device__ __forceinline__ void update_constants(const StepCtx& c, const StepParams& hp, const Chunk& ch,
+                                                 float& decay, float& lr_step) {
+  decay = hp.decay;
+  lr_step = hp.lr_step;
+  if (hp.per_tensor) {
+    decay = __int_as_float(uni(__float_as_int(c.tensor_hyper[2 * ch.tensor])));
+    lr_step = __int_as_float(uni(__float_as_int(c.tensor_hyper[2 * ch.tensor + 1])));
+  }
+}
+
 // Stores the updated parameter of element e.
 __device__ __forceinline__ void store_param(const Streams& s, uint32_t e, float p_new) {
   stb(s.p, (e - s.e0) * 4u, p_new);

@@ -108,6 +108,9 @@ struct StepParams {
   // the bare hardware reciprocal square root, which only differs from rsqrtf
   // on subnormal arguments.
   int32_t rsq_normal;
+  // 1: decay and lr_step come per tensor from StepCtx::tensor_hyper (the
+  // caller's per-tensor learning rates and weight decays) instead of above
+  int32_t per_tensor;
   int32_t n_feat;            // kNF or kVeloNF
   int32_t n_time;
   float timescales[kMaxTime];
@@ -126,6 +129,7 @@ struct StepCtx {
   float* scales;                     // [n_tensors][32]: s_0..s_27, sqrt(rbar_k) at 28..30
   float* packed;                     // kPkFloats
   int64_t* step;                     // steps taken; advanced by k_finalize (graph-replay safe)
+  const float* tensor_hyper;         // [n_tensors][2]: decay, lr_step (StepParams::per_tensor)
   const float* mlp;                  // raw weights (handle-owned)
   int32_t n_tensors, n_tiles0, n_segs1, n_chunks;
   int32_t mlp_impl;                  // 1 = VALU, 2 = MFMA

@@ -88,6 +88,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "lopt_set_step": (st, [ctypes.c_void_p, ctypes.c_int64]),
         "lopt_set_timing_events": (st, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32]),
         "lopt_set_config": (st, [ctypes.c_void_p, ctypes.POINTER(lopt_config)]),
+        "lopt_set_tensor_hyper": (st, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32]),
         "lopt_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -170,6 +171,24 @@ def lopt_set_step(h, t: int) -> None:
 
 def lopt_set_config(h, cfg: lopt_config) -> None:
     _check(load_library().lopt_set_config(h, ctypes.byref(cfg)))
+
+
+def lopt_set_tensor_hyper(h, lr: Optional[Sequence[float]], weight_decay: Optional[Sequence[float]],
+                          n: Optional[int] = None) -> None:
+    """Per-tensor lr and weight decay for the bound list; (None, None) goes back to the config's."""
+    if lr is None and weight_decay is None:
+        _check(load_library().lopt_set_tensor_hyper(h, None, None, 0 if n is None else n))
+        return
+    if lr is None or weight_decay is None:
+        raise ValueError("give both lr and weight_decay, or neither")
+    a = np.ascontiguousarray(lr, dtype=np.float32)
+    b = np.ascontiguousarray(weight_decay, dtype=np.float32)
+    if a.shape != b.shape or a.ndim != 1:
+        raise ValueError("lr and weight_decay must be 1-D sequences of the same length")
+    if n is not None and a.size != n:
+        raise ValueError(f"expected {n} values, got {a.size}")
+    _check(load_library().lopt_set_tensor_hyper(h, a.ctypes.data_as(ctypes.c_void_p), b.ctypes.data_as(ctypes.c_void_p),
+                                                 a.size if n is None else n))
 
 
 LOPT_N_KERNELS = 5
@@ -275,6 +294,10 @@ class LOpt:
     def t(self, value: int) -> None:
         lopt_set_step(self.handle, value)
 
+    def set_tensor_hyper(self, lr: Optional[Sequence[float]], weight_decay: Optional[Sequence[float]]) -> None:
+        """Per-parameter lr and weight decay (None, None: the config's for all)."""
+        lopt_set_tensor_hyper(self.handle, lr, weight_decay, len(self.params))
+
     def state_views(self, i: int) -> dict:
         """Views of tensor i's state: m (3,R,C), v (R,C), r (3,R), c (3,C)."""
         R, C = self.shapes[i]
@@ -306,9 +329,11 @@ class LearnedOptimizer(_torch_optimizer_base()):
 
     Each ``step()`` is one ``lopt_step`` over every parameter, with the
     gradients in ``p.grad``.  ``lr`` and ``weight_decay`` are read from the
-    (single) parameter group, so ``torch.optim.lr_scheduler`` schedules drive
-    them; a change is passed to the library with ``lopt_set_config``.  The
-    accumulators live in ``self.lopt.states`` (layout of ``include/lopt.h``).
+    parameter groups at every step, so ``torch.optim.lr_scheduler`` schedules
+    drive them; groups may differ (say, no weight decay on biases and norms).
+    One setting for all groups goes to the library with ``lopt_set_config``,
+    several with ``lopt_set_tensor_hyper``.  The accumulators live in
+    ``self.lopt.states`` (layout of ``include/lopt.h``).
     """
 
     def __init__(self, params, mlp: np.ndarray, lr: float = 1.0, weight_decay: float = 0.0,
@@ -319,12 +344,25 @@ class LearnedOptimizer(_torch_optimizer_base()):
         cfg.lr, cfg.weight_decay = lr, weight_decay
         self.lopt = LOpt(plist, mlp, cfg)
         self._applied = (float(cfg.lr), float(cfg.weight_decay))
+        self._applied_per_tensor = None
 
-    def _hyper(self):
-        hv = {(float(g["lr"]), float(g["weight_decay"])) for g in self.param_groups}
-        if len(hv) != 1:
-            raise ValueError("all parameter groups must share lr and weight_decay")
-        return hv.pop()
+    def _sync_hyper(self):
+        """Hands the groups' lr / weight_decay to the library when they changed."""
+        pairs = [(float(g["lr"]), float(g["weight_decay"])) for g in self.param_groups for _ in g["params"]]
+        distinct = set(pairs)
+        if len(distinct) <= 1:
+            lr, wd = distinct.pop() if distinct else self._applied
+            if self._applied_per_tensor is not None:
+                self.lopt.set_tensor_hyper(None, None)
+                self._applied_per_tensor = None
+            if (lr, wd) != self._applied:
+                cfg = self.lopt.cfg
+                cfg.lr, cfg.weight_decay = lr, wd
+                lopt_set_config(self.lopt.handle, cfg)
+                self._applied = (float(cfg.lr), float(cfg.weight_decay))
+        elif pairs != self._applied_per_tensor:
+            self.lopt.set_tensor_hyper([a for a, _ in pairs], [b for _, b in pairs])
+            self._applied_per_tensor = pairs
 
     def step(self, closure=None):
         import torch
@@ -332,12 +370,7 @@ class LearnedOptimizer(_torch_optimizer_base()):
         if closure is not None:
             with torch.enable_grad():
                 loss = closure()
-        lr, wd = self._hyper()
-        if (lr, wd) != self._applied:
-            cfg = self.lopt.cfg
-            cfg.lr, cfg.weight_decay = lr, wd
-            lopt_set_config(self.lopt.handle, cfg)
-            self._applied = (float(cfg.lr), float(cfg.weight_decay))
+        self._sync_hyper()
         grads = []
         for p in self.lopt.params:
             if p.grad is None:

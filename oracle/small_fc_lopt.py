@@ -64,7 +64,7 @@ computes in fp64 and rounds the returned state and parameters to fp32 once.
 """
 from __future__ import annotations
 
-from dataclasses import dataclass, field
+from dataclasses import dataclass, field, replace
 from typing import List, Optional, Sequence, Tuple
 
 import numpy as np
@@ -350,18 +350,27 @@ def step_tensor_rows(p, g, state: dict, t: int, mlp: Mlp, hp: Hyper, rows: Seque
 
 
 def step(params: Sequence[np.ndarray], grads: Sequence[np.ndarray], states: Sequence[dict],
-         t: int, mlp_flat: np.ndarray, hp: Hyper = Hyper(), **kw):
+         t: int, mlp_flat: np.ndarray, hp: Hyper = Hyper(),
+         tensor_hyper: Optional[Sequence[Tuple[float, float]]] = None, **kw):
     """One optimizer step over a list of tensors (tensors are independent; t is shared).
 
-    ``t`` is the 1-based index of this step.  Returns (new params, new states).
+    ``t`` is the 1-based index of this step.  ``tensor_hyper``: optional
+    (lr, weight_decay) per tensor, replacing hp's for that tensor (R16; torch's
+    parameter groups).  Returns (new params, new states).
     """
     hp32 = hp.as_f32()
     if hp32.n_feat not in FEATURE_SETS:
         raise ValueError(f"n_feat must be one of {FEATURE_SETS}")
+    if tensor_hyper is not None and len(tensor_hyper) != len(params):
+        raise ValueError("tensor_hyper needs one (lr, weight_decay) pair per tensor")
     mlp = unpack_mlp(mlp_flat, hp32.n_time, hp32.n_feat)
     outs_p, outs_s = [], []
-    for p, g, s in zip(params, grads, states):
-        pn, sn, _ = step_tensor(p, g, s, t, mlp, hp32, **kw)
+    for i, (p, g, s) in enumerate(zip(params, grads, states)):
+        hpi = hp32
+        if tensor_hyper is not None:
+            lr, wd = tensor_hyper[i]
+            hpi = replace(hp32, lr=_f32(lr), weight_decay=_f32(wd))
+        pn, sn, _ = step_tensor(p, g, s, t, mlp, hpi, **kw)
         outs_p.append(pn)
         outs_s.append(sn)
     return outs_p, outs_s

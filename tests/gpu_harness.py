@@ -69,14 +69,16 @@ class GpuRun:
 
 
 def oracle_run(w: W.Workload, mlp: np.ndarray, hp: oracle.Hyper, steps: int,
-               subset: Optional[Sequence[int]] = None) -> Dict[int, dict]:
-    """Oracle trajectory of the tensors in ``subset`` (tensors are independent)."""
+               subset: Optional[Sequence[int]] = None, tensor_hyper=None) -> Dict[int, dict]:
+    """Oracle trajectory of the tensors in ``subset`` (tensors are independent);
+    tensor_hyper: optional (lr, weight_decay) for every tensor of the workload."""
     idx = list(range(len(w.tensors))) if subset is None else list(subset)
+    th = None if tensor_hyper is None else [tensor_hyper[i] for i in idx]
     ps = [W.param_init(w, i) for i in idx]
     sts = [W.state_init(w, i) for i in idx]
     for t in range(1, steps + 1):
         gs = [W.grad_at(w, i, t) for i in idx]
-        ps, sts = oracle.step(ps, gs, sts, t, mlp, hp)
+        ps, sts = oracle.step(ps, gs, sts, t, mlp, hp, tensor_hyper=th)
     return {i: dict(p=p, **s) for i, p, s in zip(idx, ps, sts)}
 
 
@@ -97,16 +99,21 @@ def compare(got: dict, want: dict, label: str, rtol=RTOL, atol=ATOL) -> List[str
 
 
 def parity(w: W.Workload, mlp: np.ndarray, cfg, torch, steps: Optional[int] = None,
-           subset: Optional[Sequence[int]] = None) -> List[str]:
+           subset: Optional[Sequence[int]] = None, tensor_hyper=None) -> List[str]:
+    """GPU steps through the C ABI against the oracle, element by element;
+    tensor_hyper: optional (lr, weight_decay) per tensor (lopt_set_tensor_hyper)."""
     steps = w.steps if steps is None else steps
-    say(f"[parity] {w.key}: {len(w.tensors)} tensors, {w.n_params} params, {steps} steps, impl={cfg.mlp_impl}")
+    say(f"[parity] {w.key}: {len(w.tensors)} tensors, {w.n_params} params, {steps} steps, impl={cfg.mlp_impl}"
+        + (", per-tensor lr/wd" if tensor_hyper is not None else ""))
     run = GpuRun(w, mlp, cfg, torch)
+    if tensor_hyper is not None:
+        run.opt.set_tensor_hyper([a for a, _ in tensor_hyper], [b for _, b in tensor_hyper])
     for t in range(1, steps + 1):
         run.step(t)
     idx = list(range(len(w.tensors))) if subset is None else list(subset)
     got = {i: run.fetch(i) for i in idx}
     run.close()
-    want = oracle_run(w, mlp, hyper_from_cfg(cfg), steps, idx)
+    want = oracle_run(w, mlp, hyper_from_cfg(cfg), steps, idx, tensor_hyper)
     errs = []
     for i in idx:
         errs += compare(got[i], want[i], f"{w.key}[{i}:{w.tensors[i].name} {w.tensors[i].rows}x{w.tensors[i].cols}]")

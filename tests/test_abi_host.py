@@ -154,6 +154,7 @@ def test_null_handle_calls(lib):
     assert lib.lopt_set_step(None, 3) == L.LOPT_ERR_INVALID_ARGUMENT
     assert lib.lopt_step(None, None, 0, None) == L.LOPT_ERR_INVALID_ARGUMENT
     assert lib.lopt_init_state(None, None, 0, None, 0, None) == L.LOPT_ERR_INVALID_ARGUMENT
+    assert lib.lopt_set_tensor_hyper(None, None, None, 0) == L.LOPT_ERR_INVALID_ARGUMENT
     lib.lopt_destroy(None)  # no-op
 
 

@@ -276,6 +276,85 @@ def test_lr_schedule_and_weight_decay_through_torch_optimizer():
     check(errs)
 
 
+@pytest.mark.parametrize("impl", IMPLS)
+def test_per_tensor_lr_and_weight_decay(impl):
+    # every tensor its own (lr, wd), through lopt_set_tensor_hyper, 5 steps
+    shapes = [(40, 64), (1, 300), (33, 17), (7,), (5, 129)]
+    w = W.custom_workload("th", shapes, grad_std=1e-2, steps=5, wid=170)
+    th = [(0.8, 0.05), (1.5, 0.0), (0.3, 0.2), (1.0, 0.01), (2.0, 0.1)]
+    check(parity(w, mlp(bias_std=0.1), L.config_from(mlp_impl=impl, lr=0.5, weight_decay=0.3), torch,
+                 tensor_hyper=th))
+
+
+def test_per_tensor_values_equal_to_the_config_are_bitwise_the_config():
+    # per-tensor pairs built from the same fp32 expressions as the list-wide ones;
+    # clearing them goes back to the config's values
+    shapes = [(48, 64), (1, 200), (9, 31)]
+    w = W.custom_workload("th_eq", shapes, grad_std=1e-2, steps=3, wid=171)
+    m = mlp(bias_std=0.1)
+    cfg = L.config_from(lr=0.7, weight_decay=0.05)
+    a = GpuRun(w, m, cfg, torch)
+    b = GpuRun(w, m, cfg, torch)
+    b.opt.set_tensor_hyper([0.7] * 3, [0.05] * 3)
+    for t in (1, 2):
+        a.step(t)
+        b.step(t)
+    b.opt.set_tensor_hyper(None, None)
+    a.step(3)
+    b.step(3)
+    for i in range(len(shapes)):
+        x, y = a.fetch(i), b.fetch(i)
+        for k in x:
+            assert np.array_equal(x[k], y[k]), (i, k)
+    with pytest.raises(ValueError):
+        b.opt.set_tensor_hyper([0.1, 0.2], [0.0, 0.0])          # the binding checks the count
+    with pytest.raises(ValueError):
+        b.opt.set_tensor_hyper([0.1] * 3, None)
+    with pytest.raises(L.LoptError) as e:                       # so does the library
+        L.lopt_set_tensor_hyper(b.opt.handle, [0.1, 0.2], [0.0, 0.0])
+    assert e.value.status == L.LOPT_ERR_STATE
+    with pytest.raises(L.LoptError) as e:
+        b.opt.set_tensor_hyper([float("nan")] * 3, [0.0] * 3)
+    assert e.value.status == L.LOPT_ERR_INVALID_ARGUMENT
+    a.close()
+    b.close()
+
+
+def test_parameter_groups_with_a_schedule_through_torch_optimizer():
+    # two groups, as a training script makes them: weights with weight decay,
+    # biases and norms without; a cosine schedule changes both groups' lr every
+    # step, so the per-tensor values are sent at every step
+    shapes = [(48, 40), (40,), (1, 100), (64, 32)]
+    m = mlp(bias_std=0.1)
+    w = W.custom_workload("groups", shapes, steps=6, wid=172)
+    params = [torch.from_numpy(W.param_init(w, i).reshape(t.shape)).cuda() for i, t in enumerate(w.tensors)]
+    decay, no_decay = [params[0], params[3]], [params[1], params[2]]
+    opt = L.LearnedOptimizer([{"params": decay, "weight_decay": 0.05}, {"params": no_decay, "weight_decay": 0.0}],
+                             m, lr=0.8)
+    sched = torch.optim.lr_scheduler.CosineAnnealingLR(opt, T_max=6)
+    order = decay + no_decay           # the library's tensor order: group by group
+    idx = [next(i for i, p in enumerate(params) if p is q) for q in order]
+    ps = [W.param_init(w, i) for i in idx]
+    sts = [W.state_init(w, i) for i in idx]
+    for t in range(1, 7):
+        th = [(g["lr"], g["weight_decay"]) for g in opt.param_groups for _ in g["params"]]
+        gs = [W.grad_at(w, i, t) for i in idx]
+        for q, g, i in zip(order, gs, idx):
+            q.grad = torch.from_numpy(g.reshape(w.tensors[i].shape)).cuda()
+        opt.step()
+        ps, sts = oracle.step(ps, gs, sts, t, m, oracle.Hyper(), tensor_hyper=th)
+        sched.step()
+    torch.cuda.synchronize()
+    errs = []
+    for j, i in enumerate(idx):
+        tt = w.tensors[i]
+        v = opt.lopt.state_views(j)
+        got = {"p": params[i].cpu().numpy().reshape(tt.rows, tt.cols)}
+        got.update({k: v[k].cpu().numpy() for k in ("m", "v", "r", "c")})
+        errs += compare(got, dict(p=ps[j], **sts[j]), f"groups[{i}]")
+    check(errs)
+
+
 def test_graph_replay_matches_eager_steps():
     shapes = [(64, 96), (1, 500), (300, 7)]
     m = mlp(bias_std=0.1)

@@ -83,6 +83,24 @@ def test_p3b_lr_and_decoupled_weight_decay():
     np.testing.assert_allclose(p_new, p.astype(F64) * (1 - 0.05) - 0.5 * 0.005, rtol=1e-14)
 
 
+def test_p3c_per_tensor_lr_and_weight_decay():
+    # constant output dir = 0.5, mag = 0: u = 0.5 step_mult everywhere; with
+    # per-tensor (lr_i, wd_i) tensor i gets exactly p (1 - lr_i wd_i) - lr_i u,
+    # whatever the list-wide lr and wd say (all values exact in fp32)
+    cases = [random_case(3, 4, seed=40), random_case(1, 6, seed=41), random_case(5, 1, seed=42)]
+    m = random_mlp(4)
+    mc = Mlp(m.W1, m.b1, m.W2, m.b2, np.zeros((2, 32)), np.array([0.5, 0.0]))
+    hp = Hyper(step_mult=2.0 ** -7, lr=8.0, weight_decay=4.0)
+    th = [(0.5, 0.125), (2.0, 0.0), (0.25, 0.375)]
+    ps, _ = step([c[0] for c in cases], [c[1] for c in cases], [c[2] for c in cases], 1, pack_mlp(mc), hp,
+                 tensor_hyper=th, store_dtype=F64)
+    for (p, _, _), (lr, wd), p_new in zip(cases, th, ps):
+        np.testing.assert_allclose(p_new, p.astype(F64) * (1 - lr * wd) - lr * 0.5 * 2.0 ** -7, rtol=1e-14)
+    with pytest.raises(ValueError):
+        step([c[0] for c in cases], [c[1] for c in cases], [c[2] for c in cases], 1, pack_mlp(mc), hp,
+             tensor_hyper=th[:2])
+
+
 # --------------------------------------------------------------- P4 features via selectors
 def rank1_expected_inputs(alpha, beta, p_last, t, hp):
     """Closed-form MLP inputs after t steps of the constant rank-1 gradient alpha beta^T
