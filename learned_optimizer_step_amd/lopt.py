@@ -215,12 +215,19 @@ def config_from(**overrides) -> lopt_config:
 
 
 def matrix_shape(shape) -> tuple:
-    """(rows, cols) view of a 1-D or 2-D tensor: length n -> (1, n)."""
-    if len(shape) == 1:
-        return 1, int(shape[0])
-    if len(shape) == 2:
-        return int(shape[0]), int(shape[1])
-    raise ValueError("parameters must be 1-D or 2-D")
+    """(rows, cols) view of a contiguous tensor: a scalar is 1 x 1, length n is
+    1 x n, a matrix stays as given, and a tensor of more dimensions is its first
+    dimension by the product of the others (a convolution weight: output
+    channels x fan-in)."""
+    dims = [int(d) for d in shape]
+    if len(dims) == 0:
+        return 1, 1
+    if len(dims) == 1:
+        return 1, dims[0]
+    cols = 1
+    for d in dims[1:]:
+        cols *= d
+    return dims[0], cols
 
 
 # numpy view of an array of lopt_tensor (three pointers and two int64 per entry)
@@ -230,7 +237,8 @@ _TENSOR_DTYPE = np.dtype([("param", "<u8"), ("grad", "<u8"), ("state", "<u8"), (
 class LOpt:
     """The optimizer over a list of fp32 CUDA (HIP) tensors.
 
-    params: torch tensors (1-D or 2-D, contiguous, float32, all on one device).
+    params: torch tensors (contiguous, float32, all on one device; viewed as
+    matrices by ``matrix_shape``).
     mlp: packed fp32 MLP weights (numpy).  cfg: lopt_config.
     The tensor table handed to lopt_step is kept between steps; each step only
     writes the gradient addresses into it.

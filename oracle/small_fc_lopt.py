@@ -34,7 +34,8 @@ them as follows (each choice is one "reading"):
   R9  step features tanh(t / tau_q) for 11 timescales, not normalised.
   R10 population mean (divide by n).
   R11 a 1-D tensor of length n is viewed as 1 x n.
-  R12 a matrix is viewed as given: first dimension = rows, row-major.
+  R12 a matrix is viewed as given: first dimension = rows, row-major (a
+      tensor of more dimensions: first dimension x the product of the others).
   R13 ReLU on both hidden layers, linear output.
   R14 three weight matrices d_in -> 32 -> 32 -> 2.
   R16 learning-rate multiplier lr (default 1) and decoupled weight decay wd

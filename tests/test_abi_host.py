@@ -178,3 +178,12 @@ def test_numpy_tensor_table_matches_the_struct_layout(lib):
     tab[1]["rows"] = 0    # the library reads the rows field where the struct has it
     st = lib.lopt_workspace_bytes(None, tab.ctypes.data_as(ctypes.POINTER(L.lopt_tensor)), 3, ctypes.byref(out))
     assert st == L.LOPT_ERR_INVALID_ARGUMENT
+
+
+def test_matrix_view_of_parameter_shapes():
+    # scalar 1 x 1, vector 1 x n, matrix as given, more dimensions: first x product of the rest
+    assert L.matrix_shape(()) == (1, 1)
+    assert L.matrix_shape((5,)) == (1, 5)
+    assert L.matrix_shape((3, 4)) == (3, 4)
+    assert L.matrix_shape((8, 3, 5, 5)) == (8, 75)
+    assert L.matrix_shape((2, 1, 1)) == (2, 1)

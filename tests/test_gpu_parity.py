@@ -355,6 +355,33 @@ def test_parameter_groups_with_a_schedule_through_torch_optimizer():
     check(errs)
 
 
+def test_nd_and_scalar_parameters_through_torch_optimizer():
+    # a convolution weight, a scalar, a vector and a matrix, as a model's
+    # parameters() gives them; the library sees each as its matrix view
+    nd = [(8, 3, 5, 5), (), (7,), (6, 10)]
+    mats = [L.matrix_shape(x) for x in nd]
+    w = W.custom_workload("nd", [m if m[0] > 1 else (m[1],) for m in mats], grad_std=1e-2, steps=4, wid=173)
+    m = mlp(bias_std=0.1)
+    params = [torch.from_numpy(W.param_init(w, i).reshape(x)).cuda() for i, x in enumerate(nd)]
+    opt = L.LearnedOptimizer(params, m, lr=0.9, weight_decay=0.02)
+    ps = [W.param_init(w, i) for i in range(len(nd))]
+    sts = [W.state_init(w, i) for i in range(len(nd))]
+    for t in range(1, 5):
+        gs = [W.grad_at(w, i, t) for i in range(len(nd))]
+        for p, g, x in zip(params, gs, nd):
+            p.grad = torch.from_numpy(g.reshape(x)).cuda()
+        opt.step()
+        ps, sts = oracle.step(ps, gs, sts, t, m, oracle.Hyper(lr=0.9, weight_decay=0.02))
+    torch.cuda.synchronize()
+    errs = []
+    for i, (r, c) in enumerate(mats):
+        v = opt.lopt.state_views(i)
+        got = {"p": params[i].cpu().numpy().reshape(r, c)}
+        got.update({k: v[k].cpu().numpy() for k in ("m", "v", "r", "c")})
+        errs += compare(got, dict(p=ps[i], **sts[i]), f"nd[{i}:{nd[i]}]")
+    check(errs)
+
+
 def test_graph_replay_matches_eager_steps():
     shapes = [(64, 96), (1, 500), (300, 7)]
     m = mlp(bias_std=0.1)
