@@ -86,7 +86,10 @@ typedef struct lopt_config {
  * fp32, contiguous, 4-byte aligned.
  *   param: rows*cols values, row-major; updated in place by lopt_step.
  *   grad:  rows*cols values; read only.  Its address may change between steps.
- *          May be NULL in lopt_workspace_bytes and lopt_init_state.
+ *          NULL: in lopt_step, the tensor is skipped for that step (its
+ *          parameters and state stay as they are, as torch optimizers skip a
+ *          parameter without a gradient; t still advances).  lopt_workspace_bytes
+ *          and lopt_init_state ignore it.
  *   state: lopt_state_floats(rows, cols) values, owned by the caller and
  *          updated in place.  Layout (each block contiguous):
  *            m1 | m2 | m3 | v      (rows*cols each, row-major)

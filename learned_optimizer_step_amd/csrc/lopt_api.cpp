@@ -111,9 +111,8 @@ struct Range {
   int tensor;
 };
 
-// require_grads: gradients are first needed by lopt_step; lopt_init_state and
-// lopt_workspace_bytes accept NULL gradient pointers.
-void validate_tensors(const lopt_tensor* ts, int32_t n, bool require_grads) {
+// Gradient pointers may be NULL everywhere: lopt_step skips such a tensor.
+void validate_tensors(const lopt_tensor* ts, int32_t n) {
   if (n < 0) fail(LOPT_ERR_INVALID_ARGUMENT, "negative tensor count");
   if (n > 0 && !ts) fail(LOPT_ERR_INVALID_ARGUMENT, "tensor list is NULL");
   std::vector<Range> written;
@@ -122,7 +121,6 @@ void validate_tensors(const lopt_tensor* ts, int32_t n, bool require_grads) {
     const lopt_tensor& t = ts[i];
     const std::string at = "tensor " + std::to_string(i) + ": ";
     if (!t.param || !t.state) fail(LOPT_ERR_INVALID_ARGUMENT, at + "NULL param or state");
-    if (require_grads && !t.grad) fail(LOPT_ERR_INVALID_ARGUMENT, at + "NULL grad");
     if (t.rows < 1 || t.cols < 1) fail(LOPT_ERR_INVALID_ARGUMENT, at + "rows and cols must be >= 1");
     if (t.rows > INT32_MAX || t.cols > INT32_MAX || t.rows * t.cols >= (int64_t(1) << 31))
       fail(LOPT_ERR_UNSUPPORTED, at + "tensors must have fewer than 2^31 elements");
@@ -160,7 +158,7 @@ void validate_tensors(const lopt_tensor* ts, int32_t n, bool require_grads) {
 }
 
 Plan build_plan(const lopt_tensor* ts, int32_t n) {
-  validate_tensors(ts, n, false);
+  validate_tensors(ts, n);
   Plan pl;
   pl.bound.assign(ts, ts + n);
   pl.desc.resize(n);
@@ -466,7 +464,7 @@ void check_same_list(const lopt_handle* h, const lopt_tensor* ts, int32_t n, boo
       fail(LOPT_ERR_STATE, "tensor " + std::to_string(i) + " differs from lopt_init_state");
     if (ts[i].grad != b[i].grad) *grads_changed = true;
   }
-  if (*grads_changed) validate_tensors(ts, n, true);
+  if (*grads_changed) validate_tensors(ts, n);
 }
 
 }  // namespace

@@ -59,6 +59,7 @@ __global__ __launch_bounds__(kBlock) void k_apply_valu(StepCtx c, StepParams hp)
   TensorDesc d;
   const float* g;
   load_chunk(c, blockIdx.x, ch, d, g);
+  if (!g) return;  // no gradient this step: the tensor is skipped
   dispatch_variant<false>(d, hp, [&](auto v) {
     using V = decltype(v);
     apply_valu_body<V::vec, V::normal, V::nf>(c, hp, ch, d, g);
@@ -255,6 +256,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   TensorDesc d;
   const float* g;
   load_chunk(c, blockIdx.x, ch, d, g);
+  if (!g) return;  // no gradient this step: the tensor is skipped
   dispatch_variant<true>(d, hp, [&](auto v) {
     using V = decltype(v);
     apply_mfma_body<V::vec, V::normal, V::nf, V::rowuni>(c, hp, ch, d, g);

@@ -35,8 +35,9 @@ namespace lopt {
 //   Flat tile (1-D tensors): one partial of sum g^2 over [c0, c1).
 __global__ __launch_bounds__(kBlock) void k_rowcol_sumsq(StepCtx c) {
   const Tile0 tl = c.tiles0[blockIdx.x];
+  const float* __restrict__ g = uni(c.grads[tl.tensor]);
+  if (!g) return;  // no gradient this step: the tensor is skipped
   const TensorDesc d = c.desc[tl.tensor];
-  const float* __restrict__ g = c.grads[tl.tensor];
   float* __restrict__ ws = c.ws;
   const int tid = threadIdx.x;
   __shared__ float lds_rows[4 * kTile0Iters];
@@ -181,6 +182,7 @@ struct KahanSum {
 // inverse square roots (workspace) and per-segment partial sums of r_k.
 __global__ __launch_bounds__(kBlock) void k_moving_avg(StepCtx c, StepParams hp) {
   const Seg1 sg = c.segs1[blockIdx.x];
+  if (!uni(c.grads[sg.tensor])) return;  // no gradient this step: the tensor is skipped
   const TensorDesc d = c.desc[sg.tensor];
   float* __restrict__ ws = c.ws;
   const int tid = threadIdx.x;
@@ -289,6 +291,7 @@ __global__ __launch_bounds__(kBlock) void k_stats(StepCtx c, StepParams hp) {
   TensorDesc d;
   const float* g;
   load_chunk(c, blockIdx.x, ch, d, g);
+  if (!g) return;  // no gradient this step: the tensor is skipped
   __shared__ float lds[4][kNF];
   float acc[kNF];
 #pragma unroll
@@ -361,6 +364,7 @@ __global__ __launch_bounds__(kBlock) void k_finalize(StepCtx c, StepParams hp) {
     pack_mlp(c, hp);
     return;
   }
+  if (!uni(c.grads[t])) return;  // no gradient this step: the tensor is skipped
   const TensorDesc d = c.desc[t];
   __shared__ float lds[4][kNF];
   __shared__ float red[4];

@@ -279,17 +279,19 @@ class LOpt:
                                        self.ws_bytes, ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)))
 
     def step(self, grads) -> None:
+        """One step; grads[i] None skips parameter i (it and its state stay as they are)."""
         grads = list(grads)
         n = len(self.params)
         if len(grads) != n:
             raise ValueError(f"expected {n} gradients, got {len(grads)}")
         f32, dev = self.torch.float32, self.device
         for g, p in zip(grads, self.params):
-            if g.dtype != f32 or not g.is_contiguous() or g.numel() != p.numel() or g.device != dev:
+            if g is not None and (g.dtype != f32 or not g.is_contiguous() or g.numel() != p.numel()
+                                  or g.device != dev):
                 raise ValueError("gradients must be contiguous float32 tensors shaped like the parameters, "
-                                 "on the parameters' device")
+                                 "on the parameters' device (or None)")
         if n:
-            self._table["grad"][:n] = [g.data_ptr() for g in grads]
+            self._table["grad"][:n] = [0 if g is None else g.data_ptr() for g in grads]
         with self.torch.cuda.device(dev):
             _check(load_library().lopt_step(self.handle, self._table_ptr, n,
                                             ctypes.c_void_p(self.torch.cuda.current_stream(dev).cuda_stream)))
@@ -336,7 +338,7 @@ class LearnedOptimizer(_torch_optimizer_base()):
     """small_fc_lopt as a ``torch.optim.Optimizer`` over fp32 device parameters.
 
     Each ``step()`` is one ``lopt_step`` over every parameter, with the
-    gradients in ``p.grad``.  ``lr`` and ``weight_decay`` are read from the
+    gradients in ``p.grad``; a parameter whose ``grad`` is None is skipped.  ``lr`` and ``weight_decay`` are read from the
     parameter groups at every step, so ``torch.optim.lr_scheduler`` schedules
     drive them; groups may differ (say, no weight decay on biases and norms).
     One setting for all groups goes to the library with ``lopt_set_config``,
@@ -379,12 +381,8 @@ class LearnedOptimizer(_torch_optimizer_base()):
             with torch.enable_grad():
                 loss = closure()
         self._sync_hyper()
-        grads = []
-        for p in self.lopt.params:
-            if p.grad is None:
-                raise ValueError("every parameter needs a gradient (the tensor list is fixed)")
-            grads.append(p.grad)
-        self.lopt.step(grads)
+        # a parameter without a gradient is skipped, as torch optimizers do
+        self.lopt.step([p.grad for p in self.lopt.params])
         return loss
 
     def state_dict(self):

@@ -40,6 +40,9 @@ them as follows (each choice is one "reading"):
   R14 three weight matrices d_in -> 32 -> 32 -> 2.
   R16 learning-rate multiplier lr (default 1) and decoupled weight decay wd
       (default 0): p <- p - lr*u - lr*wd*p.
+  R28 a tensor without a gradient in a step is left as it is (parameters and
+      accumulators), as torch optimizers skip such parameters; t is the
+      optimizer's and advances with every step.
   R18 hyperparameters are fp32 numbers (they are passed as fp32).
   R24 no bias correction of the moving averages.
   R26 the VeLO-shaped variant (n_feat = 19): the same page gives VeLO's feature
@@ -357,7 +360,8 @@ def step(params: Sequence[np.ndarray], grads: Sequence[np.ndarray], states: Sequ
 
     ``t`` is the 1-based index of this step.  ``tensor_hyper``: optional
     (lr, weight_decay) per tensor, replacing hp's for that tensor (R16; torch's
-    parameter groups).  Returns (new params, new states).
+    parameter groups).  A gradient of None leaves its tensor and state as they
+    are (R28).  Returns (new params, new states).
     """
     hp32 = hp.as_f32()
     if hp32.n_feat not in FEATURE_SETS:
@@ -367,6 +371,10 @@ def step(params: Sequence[np.ndarray], grads: Sequence[np.ndarray], states: Sequ
     mlp = unpack_mlp(mlp_flat, hp32.n_time, hp32.n_feat)
     outs_p, outs_s = [], []
     for i, (p, g, s) in enumerate(zip(params, grads, states)):
+        if g is None:
+            outs_p.append(p)
+            outs_s.append(s)
+            continue
         hpi = hp32
         if tensor_hyper is not None:
             lr, wd = tensor_hyper[i]

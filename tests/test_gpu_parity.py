@@ -382,6 +382,36 @@ def test_nd_and_scalar_parameters_through_torch_optimizer():
     check(errs)
 
 
+@pytest.mark.parametrize("impl", IMPLS)
+def test_tensors_without_gradient_are_skipped(impl):
+    # some tensors have no gradient in some steps (None, as torch gives a
+    # parameter that took no part in the loss): they stay as they are, the
+    # others step as usual; step 4 has no gradient at all
+    shapes = [(40, 64), (1, 300), (33, 17), (7,)]
+    w = W.custom_workload("skip", shapes, grad_std=1e-2, steps=5, wid=174)
+    m = mlp(bias_std=0.1)
+    missing = {1: {1}, 2: {0, 3}, 3: {2}, 4: {0, 1, 2, 3}, 5: set()}
+    params = [torch.from_numpy(W.param_init(w, i).reshape(t.shape)).cuda() for i, t in enumerate(w.tensors)]
+    opt = L.LOpt(params, m, L.config_from(mlp_impl=impl))
+    ps = [W.param_init(w, i) for i in range(len(shapes))]
+    sts = [W.state_init(w, i) for i in range(len(shapes))]
+    for t in range(1, 6):
+        gs = [None if i in missing[t] else W.grad_at(w, i, t) for i in range(len(shapes))]
+        opt.step([None if g is None else torch.from_numpy(g.reshape(tt.shape)).cuda()
+                  for g, tt in zip(gs, w.tensors)])
+        ps, sts = oracle.step(ps, gs, sts, t, m, hyper_from_cfg(opt.cfg))
+    torch.cuda.synchronize()
+    assert opt.t == 5
+    errs = []
+    for i, tt in enumerate(w.tensors):
+        v = opt.state_views(i)
+        got = {"p": params[i].cpu().numpy().reshape(tt.rows, tt.cols)}
+        got.update({k: v[k].cpu().numpy() for k in ("m", "v", "r", "c")})
+        errs += compare(got, dict(p=ps[i], **sts[i]), f"skip[{i}]")
+    check(errs)
+    opt.close()
+
+
 def test_graph_replay_matches_eager_steps():
     shapes = [(64, 96), (1, 500), (300, 7)]
     m = mlp(bias_std=0.1)

@@ -101,6 +101,21 @@ def test_p3c_per_tensor_lr_and_weight_decay():
              tensor_hyper=th[:2])
 
 
+def test_p3d_tensor_without_gradient_is_left_as_is():
+    # R28: a None gradient leaves its tensor and state untouched, and the other
+    # tensors step exactly as they would without it in the list
+    cases = [random_case(4, 6, seed=43), random_case(1, 9, seed=44), random_case(3, 3, seed=45)]
+    w = pack_mlp(random_mlp(5))
+    ps, sts = step([c[0] for c in cases], [cases[0][1], None, cases[2][1]], [c[2] for c in cases], 2, w, Hyper())
+    assert ps[1] is cases[1][0] and sts[1] is cases[1][2]
+    ref_p, ref_s = step([cases[0][0], cases[2][0]], [cases[0][1], cases[2][1]], [cases[0][2], cases[2][2]], 2, w,
+                        Hyper())
+    for a, b in ((0, 0), (2, 1)):
+        assert np.array_equal(ps[a], ref_p[b])
+        for k in ("m", "v", "r", "c"):
+            assert np.array_equal(sts[a][k], ref_s[b][k])
+
+
 # --------------------------------------------------------------- P4 features via selectors
 def rank1_expected_inputs(alpha, beta, p_last, t, hp):
     """Closed-form MLP inputs after t steps of the constant rank-1 gradient alpha beta^T
