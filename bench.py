@@ -109,7 +109,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="vit_b16")
-    ap.add_argument("--impl", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--impl", default="auto", choices=["auto", "valu", "mfma", "bf16x6"])
     ap.add_argument("--n-feat", type=int, default=28, choices=(28, 19),
                     help="per-element features: 28 (small_fc_lopt) or 19 (the VeLO-shaped variant)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -129,7 +129,8 @@ def main():
     from learned_optimizer_step_amd import lopt as L
     from learned_optimizer_step_amd import workloads as W
 
-    impl = {"auto": L.LOPT_MLP_AUTO, "valu": L.LOPT_MLP_VALU, "mfma": L.LOPT_MLP_MFMA}[args.impl]
+    impl = {"auto": L.LOPT_MLP_AUTO, "valu": L.LOPT_MLP_VALU, "mfma": L.LOPT_MLP_MFMA,
+            "bf16x6": L.LOPT_MLP_BF16X6}[args.impl]
     w = W.get_workload(args.workload)
     log(f"[bench] {w.key}: {len(w.tensors)} tensors, {w.n_params} params; generating inputs")
     dev = torch.device("cuda:0")
@@ -208,7 +209,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"{w.key}: {w.description}", "n_params": n, "n_tensors": len(w.tensors),
-                   "mlp_impl": "mfma" if use_mfma else "valu", "state": "zero-init, gradients fixed",
+                   "mlp_impl": {L.LOPT_MLP_VALU: "valu", L.LOPT_MLP_BF16X6: "bf16x6"}.get(impl, "mfma"),
+                   "state": "zero-init, gradients fixed",
                    "variant": "small_fc_lopt" if args.n_feat == 28 else "VeLO-shaped (19 features, 30 inputs)"},
         "roofline": {"bound": "mfma" if use_mfma else "alu", "kernel": "k_apply",
                      "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",

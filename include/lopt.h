@@ -59,8 +59,13 @@ typedef enum lopt_status {
 typedef enum lopt_mlp_impl {
   LOPT_MLP_AUTO = 0, /* currently the matrix-core path */
   LOPT_MLP_VALU = 1, /* vector FMA, weights broadcast from scalar registers */
-  LOPT_MLP_MFMA = 2  /* fp32 matrix-core path (v_mfma_f32_32x32x1_2b_f32 and
+  LOPT_MLP_MFMA = 2, /* fp32 matrix-core path (v_mfma_f32_32x32x1_2b_f32 and
                         v_mfma_f32_32x32x2_f32) */
+  LOPT_MLP_BF16X6 = 3 /* bf16 matrix-core path with every fp32 operand split
+                         exactly into three bf16 pieces and the six largest
+                         piece products accumulated in fp32
+                         (v_mfma_f32_32x32x16_bf16); the dropped products are
+                         below one fp32 rounding of each term */
 } lopt_mlp_impl;
 
 /* Hyperparameters.  lopt_default_config() fills the defaults shown. */

@@ -100,7 +100,7 @@ void validate_config(const lopt_config* c) {
   for (int q = 0; q < c->n_time; ++q)
     if (!(c->timescales[q] > 0.f) || !finite(c->timescales[q]))
       fail(LOPT_ERR_INVALID_ARGUMENT, "timescales must be finite and > 0");
-  if (c->mlp_impl < LOPT_MLP_AUTO || c->mlp_impl > LOPT_MLP_MFMA)
+  if (c->mlp_impl < LOPT_MLP_AUTO || c->mlp_impl > LOPT_MLP_BF16X6)
     fail(LOPT_ERR_INVALID_ARGUMENT, "unknown mlp_impl");
   if (c->n_feat != LOPT_N_FEATURES && c->n_feat != LOPT_VELO_FEATURES)
     fail(LOPT_ERR_INVALID_ARGUMENT, "n_feat must be 28 or 19");
@@ -340,7 +340,7 @@ StepCtx make_ctx(const lopt_handle* h) {
   c.n_tiles0 = int32_t(pl.tiles0.size());
   c.n_segs1 = int32_t(pl.segs1.size());
   c.n_chunks = int32_t(pl.chunks.size());
-  c.mlp_impl = h->cfg.mlp_impl == LOPT_MLP_VALU ? LOPT_MLP_VALU : LOPT_MLP_MFMA;
+  c.mlp_impl = h->cfg.mlp_impl == LOPT_MLP_AUTO ? LOPT_MLP_MFMA : h->cfg.mlp_impl;
   return c;
 }
 

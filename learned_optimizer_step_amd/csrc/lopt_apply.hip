@@ -263,9 +263,280 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   });
 }
 
+// ---------------------------------------------------------------------------
+// k_apply_bf16x6: layers 1 and 2 on the bf16 matrix cores with fp32 accuracy.
+// Every fp32 operand x is split into three bf16 pieces, x = h + m + l exactly:
+// h is x with its low 16 bits cleared, m the same of r = x - h (exact), and
+// l = r - m, which has at most 8 significant bits (truncation split of the
+// 24-bit significand into 8-bit parts).  A product a.b is then the sum of the
+// six piece products whose orders add up to at most 2 (hh, hm, mh, hl, lh,
+// mm); the three dropped ones (ml, lm, ll) are below 2^-24 |a b| together,
+// the size of one fp32 rounding, and each piece product is exact in the
+// fp32 accumulation.  This is the piece-wise emulation of an fp32 GEMM on
+// reduced-precision matrix units (published as bf16x6 / bf16x9 splitting).
+// On gfx950 a v_mfma_f32_32x32x16_bf16 does 16x the FLOP of the fp32 form in
+// half its cycles, and vector instructions of the other waves issue beside
+// it (the fp32 form shares their issue cycles), so the six products cost
+// less than one fp32 product and the split's vector work overlaps the matrix
+// work.
+//
+// Layout (one wave, 64 elements, lane l owns element l; M = hidden unit
+// l%32, K = inputs, N = elements, two 32-element blocks):
+//   layer 1: 32 K entries in two K-steps of 16; entry q < NL holds the q-th
+//     feature of the variant's list (RU: without the row features), the
+//     entries of position (1, 7) in both lane halves hold half of the
+//     constant term (b1, plus the row term with RU) against a B value of 1,
+//     the rest are zero.  A K-step's B operand takes entries 0..7 from lane
+//     half 0 and 8..15 from half 1 for the block's 32 elements, so each pair
+//     of entries (one per half, same position) is exchanged between the lane
+//     halves once in fp32 (v_permlane32_swap) before the split.
+//   layer 2: the layer-1 accumulator register r of lane half h holds hidden
+//     unit 8(r/4) + 4h + r%4, which is a B operand entry as it stands (W2's
+//     columns are visited in that order, as in the fp32 matrix path).
+//   layer 3 on the vector ALU, as in the fp32 matrix path.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// The values whose upper halves are the pieces h, m, l of x.
+struct Pieces {
+  float h, m, l;
+};
+__device__ __forceinline__ Pieces split3(float x) {
+  const float r = x - __uint_as_float(__float_as_uint(x) & 0xffff0000u);
+  return {x, r, r - __uint_as_float(__float_as_uint(r) & 0xffff0000u)};
+}
+__device__ __forceinline__ float piece(const Pieces& p, int k) { return k == 0 ? p.h : k == 1 ? p.m : p.l; }
+// bf16 pair: the upper half of a (low) and of b (high).
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+}
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Layer-1 entries: feature of entry q (q < 30), -1 = zero.
+__device__ constexpr int x6_feature(int q, int nf, bool ru) {
+  for (int f = 0; f < nf; ++f) {
+    if (ru && f >= 13 && f < 16) continue;
+    if (q == 0) return f;
+    --q;
+  }
+  return -1;
+}
+// entry q sits at K-step (q/2)/8, position (q/2)%8, lane half q%2
+static_assert(x6_feature(24, kNF, true) == 27 && x6_feature(25, kNF, true) == -1 && x6_feature(27, kNF, false) == 27 &&
+                  x6_feature(13, kNF, true) == 16 && x6_feature(16, kVeloNF, true) == -1,
+              "bf16x6 layer-1 entries");
+
+// (A piece, B piece) of product t of the six, smallest terms first:
+// hl, lh, mm, hm, mh, hh.
+__device__ constexpr int x6_a(int t) { return t == 1 ? 2 : (t == 2 || t == 4) ? 1 : 0; }
+__device__ constexpr int x6_b(int t) { return t == 0 ? 2 : (t == 2 || t == 3) ? 1 : 0; }
+
+// LDS of the kernel (one copy for every variant the body is instantiated for).
+struct X6Lds {
+  u32x4 a1[2][3][64];   // layer-1 A operands: K-step, piece, lane
+  u32x4 a2[2][3][64];   // layer-2 A operands
+  float4 tab[3][2][4];  // {b2, W3 dir, W3 mag} x half x 16 floats
+};
+
+template <bool VEC, bool NORMAL, int NF, bool RU>
+__device__ __forceinline__ void apply_x6_body(const StepCtx& c, const StepParams& hp, const Chunk& ch,
+                                              const TensorDesc& d, const float* g, X6Lds& L) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = lane >> 5;
+  const int row = lane & 31;
+  const Streams s = make_streams(d, g, c.ws, ch);
+  const float* __restrict__ pk = c.packed;
+  const float* __restrict__ sc = c.scales + size_t(ch.tensor) * kStatStride;
+
+  // A operands, built once per chunk by the first wave and read from LDS
+  // (16 bytes per lane per K-step and piece) where needed.  Layer 1: K-step
+  // k, piece p: entries of positions 0..7 of the lane's half.  The constant
+  // entries (1, 7) are set per iteration with RU; otherwise they hold b1 / 2
+  // (two entries, one per half, against B = 1).  Layer 2: W2's columns in
+  // accumulator-row order.
+  if (threadIdx.x < 64) {
+    const float b1half = 0.5f * pk[kPkB1 + row];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int q = 2 * (8 * k + i);
+        const int f0 = x6_feature(q, NF, RU), f1 = x6_feature(q + 1, NF, RU);
+        const float w0 = f0 >= 0 ? pk[kPkW1 + row * kNF + f0] * sc[f0] : 0.f;
+        const float w1 = f1 >= 0 ? pk[kPkW1 + row * kNF + f1] * sc[f1] : 0.f;
+        v[i] = (k == 1 && i == 7) ? (RU ? 0.f : b1half) : half ? w1 : w0;
+      }
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+        u32x4 t;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) t[j] = pack2(piece(split3(v[2 * j]), p), piece(split3(v[2 * j + 1]), p));
+        L.a1[k][p][lane] = t;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+        u32x4 t;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float w0 = pk[kPkW2 + row * kH + acc_row(8 * k + 2 * j, half)];
+          const float w1 = pk[kPkW2 + row * kH + acc_row(8 * k + 2 * j + 1, half)];
+          t[j] = pack2(piece(split3(w0), p), piece(split3(w1), p));
+        }
+        L.a2[k][p][lane] = t;
+      }
+  }
+  float arow[3];       // RU: W1[row][13 + k] * s_(13 + k), the row term's weights
+#pragma unroll
+  for (int k = 0; k < 3; ++k) arow[k] = RU ? pk[kPkW1 + row * kNF + 13 + k] * sc[13 + k] : 0.f;
+  const float b1row = RU ? pk[kPkB1 + row] : 0.f;
+
+  if (threadIdx.x < 96) {
+    const int which = threadIdx.x >> 5, h = (threadIdx.x >> 4) & 1, q = threadIdx.x & 15;
+    const int hr = acc_row(q, h);
+    const float v = which == 0 ? pk[kPkB2 + hr] : which == 1 ? pk[kPkW3 + hr] : pk[kPkW3 + kH + hr];
+    reinterpret_cast<float*>(&L.tab[which][h][0])[q] = v;
+  }
+  __syncthreads();
+  const float b3d = pk[kPkB3], b3m = pk[kPkB3 + 1];
+  float decay, lr_step;
+  update_constants(c, hp, ch, decay, lr_step);
+  uint32_t base = ch.e0 + wave * 64;
+  if (base >= ch.e1) return;
+  for (; base < ch.e1; base += kBlock) {
+    const uint32_t e = base + lane;
+    const bool valid = e < ch.e1;
+    Elem x;
+    load_elem<VEC, RU && !VEC>(s, valid ? e : base, x, base);
+    const float p_decayed = x.p * decay;
+    float F[kNF], cn[3];
+    build_features<VEC, NORMAL, NF>(hp, x, F, cn);
+    if (valid) store_state<VEC>(s, e, x, cn);
+
+    Pieces ct = {0.f, 0.f, 0.f};
+    if (RU) {
+      // constant entries: (b1 + row term) / 2 in both lane halves
+      const float r0 = __int_as_float(uni(__float_as_int(x.rq[0])));
+      const float r1 = __int_as_float(uni(__float_as_int(x.rq[1])));
+      const float r2 = __int_as_float(uni(__float_as_int(x.rq[2])));
+      ct = split3(0.5f * fmaf(arow[2], r2, fmaf(arow[1], r1, fmaf(arow[0], r0, b1row))));
+    }
+    // The A operands are read from LDS where they are used: an offset the
+    // compiler cannot see through keeps the reads in the loop (hoisted, the
+    // 48 registers they need would be spilled to scratch).
+    int li = lane;
+    asm volatile("" : "+v"(li));
+    // Layer-1 B values: entry pairs exchanged between the lane halves, so
+    // that v[b][k][i] holds position i of K-step k for block b's element.
+    float v[2][2][8];
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int q = 2 * (8 * k + i);
+        const int f0 = x6_feature(q, NF, RU), f1 = x6_feature(q + 1, NF, RU);
+        if (k == 1 && i == 7) {
+          v[0][k][i] = v[1][k][i] = 1.f;
+        } else if (f0 < 0 && f1 < 0) {
+          v[0][k][i] = v[1][k][i] = 0.f;
+        } else {
+          swap_halves(f0 >= 0 ? F[f0] : 0.f, f1 >= 0 ? F[f1] : 0.f, v[0][k][i], v[1][k][i]);
+        }
+      }
+    // One block at a time through the three layers (keeps one block's
+    // accumulators live): lane half 0's layer-3 partial sums start at b3.
+    float dpart[2], mpart[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      f32x16 acc1;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc1[q] = 0.f;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        u32x4 a[3], bt[3];
+#pragma unroll
+        for (int p = 0; p < 3; ++p) {
+          a[p] = L.a1[k][p][li];
+          if (RU && k == 1) a[p][3] = __builtin_amdgcn_perm(__float_as_uint(piece(ct, p)), a[p][3], 0x07060100u);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const Pieces u0 = split3(v[b][k][2 * j]), u1 = split3(v[b][k][2 * j + 1]);
+#pragma unroll
+          for (int p = 0; p < 3; ++p) bt[p][j] = pack2(piece(u0, p), piece(u1, p));
+        }
+#pragma unroll
+        for (int t = 0; t < 6; ++t)
+          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[x6_a(t)]), as_bf16x8(bt[x6_b(t)]), acc1, 0, 0, 0);
+      }
+      f32x16 acc2;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 w = L.tab[0][half][q];
+        acc2[4 * q] = w.x; acc2[4 * q + 1] = w.y; acc2[4 * q + 2] = w.z; acc2[4 * q + 3] = w.w;
+      }
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        u32x4 a[3], bt[3];
+#pragma unroll
+        for (int p = 0; p < 3; ++p) a[p] = L.a2[k][p][li];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const Pieces u0 = split3(fmaxf(acc1[8 * k + 2 * j], 0.f));
+          const Pieces u1 = split3(fmaxf(acc1[8 * k + 2 * j + 1], 0.f));
+#pragma unroll
+          for (int p = 0; p < 3; ++p) bt[p][j] = pack2(piece(u0, p), piece(u1, p));
+        }
+#pragma unroll
+        for (int t = 0; t < 6; ++t)
+          acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[x6_a(t)]), as_bf16x8(bt[x6_b(t)]), acc2, 0, 0, 0);
+      }
+      float dsum = half ? 0.f : b3d, msum = half ? 0.f : b3m;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 wd = L.tab[1][half][q], wm = L.tab[2][half][q];
+        const float hq[4] = {fmaxf(acc2[4 * q], 0.f), fmaxf(acc2[4 * q + 1], 0.f), fmaxf(acc2[4 * q + 2], 0.f),
+                             fmaxf(acc2[4 * q + 3], 0.f)};
+        dsum = fmaf(wd.x, hq[0], dsum); msum = fmaf(wm.x, hq[0], msum);
+        dsum = fmaf(wd.y, hq[1], dsum); msum = fmaf(wm.y, hq[1], msum);
+        dsum = fmaf(wd.z, hq[2], dsum); msum = fmaf(wm.z, hq[2], msum);
+        dsum = fmaf(wd.w, hq[3], dsum); msum = fmaf(wm.w, hq[3], msum);
+      }
+      dpart[b] = dsum;
+      mpart[b] = msum;
+    }
+    const float dA = dpart[0], dB = dpart[1], mA = mpart[0], mB = mpart[1];
+    float d0, d1, m0, m1;
+    swap_halves(dA, dB, d0, d1);
+    swap_halves(mA, mB, m0, m1);
+    const float dir = d0 + d1;
+    const float mag = m0 + m1;
+    if (valid) store_param(s, e, fmaf(-lr_step, dir * __builtin_amdgcn_exp2f(mag * hp.exp2_mult), p_decayed));
+  }
+}
+
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void k_apply_bf16x6(StepCtx c, StepParams hp) {
+  Chunk ch;
+  TensorDesc d;
+  const float* g;
+  load_chunk(c, blockIdx.x, ch, d, g);
+  if (!g) return;  // no gradient this step: the tensor is skipped
+  __shared__ X6Lds lds;
+  dispatch_variant<true>(d, hp, [&](auto v) {
+    using V = decltype(v);
+    apply_x6_body<V::vec, V::normal, V::nf, V::rowuni>(c, hp, ch, d, g, lds);
+  });
+}
+
 hipError_t launch_apply(const StepCtx& c, const StepParams& p, hipStream_t s) {
   if (c.mlp_impl == 1)
     hipLaunchKernelGGL(k_apply_valu, dim3(c.n_chunks), dim3(kBlock), 0, s, c, p);
+  else if (c.mlp_impl == 3)
+    hipLaunchKernelGGL(k_apply_bf16x6, dim3(c.n_chunks), dim3(kBlock), 0, s, c, p);
   else
     hipLaunchKernelGGL(k_apply_mfma, dim3(c.n_chunks), dim3(kBlock), 0, s, c, p);
   return hipGetLastError();

@@ -19,7 +19,7 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU container
 from learned_optimizer_step_amd import lopt as L  # noqa: E402
 from learned_optimizer_step_amd import workloads as W  # noqa: E402
 
-IMPLS = [L.LOPT_MLP_VALU, L.LOPT_MLP_MFMA]
+IMPLS = [L.LOPT_MLP_VALU, L.LOPT_MLP_MFMA, L.LOPT_MLP_BF16X6]
 
 EDGE_SHAPES = [(1,), (2,), (3,), (15,), (16,), (17,), (63,), (65,), (40000,),
                (1, 1), (2, 3), (3, 1), (7, 1), (17, 33), (65, 3), (4, 513), (300, 2),
@@ -57,18 +57,23 @@ def test_edge_shapes_ten_steps(impl):
     check(parity(w, mlp(bias_std=0.1), L.config_from(mlp_impl=impl), torch))
 
 
+MATRIX_IMPLS = [L.LOPT_MLP_MFMA, L.LOPT_MLP_BF16X6]
+
+
+@pytest.mark.parametrize("impl", MATRIX_IMPLS)
 @pytest.mark.parametrize("n_feat", [L.LOPT_N_FEATURES, L.LOPT_VELO_FEATURES])
-def test_row_uniform_shapes_ten_steps(n_feat):
+def test_row_uniform_shapes_ten_steps(n_feat, impl):
     w = W.custom_workload("rowuni", ROW_UNIFORM_SHAPES, grad_std=1e-2, steps=10, wid=104)
     weights = W.mlp_weights(11, bias_std=0.1, n_feat=n_feat)
-    check(parity(w, weights, L.config_from(mlp_impl=L.LOPT_MLP_MFMA, n_feat=n_feat), torch))
+    check(parity(w, weights, L.config_from(mlp_impl=impl, n_feat=n_feat), torch))
 
 
+@pytest.mark.parametrize("impl", MATRIX_IMPLS)
 @pytest.mark.parametrize("n_feat", [L.LOPT_N_FEATURES, L.LOPT_VELO_FEATURES])
-def test_mixed_row_shapes_ten_steps(n_feat):
+def test_mixed_row_shapes_ten_steps(n_feat, impl):
     w = W.custom_workload("mixrow", MIXED_ROW_SHAPES, grad_std=1e-2, steps=10, wid=150)
     weights = W.mlp_weights(11, bias_std=0.1, n_feat=n_feat)
-    check(parity(w, weights, L.config_from(mlp_impl=L.LOPT_MLP_MFMA, n_feat=n_feat), torch))
+    check(parity(w, weights, L.config_from(mlp_impl=impl, n_feat=n_feat), torch))
 
 
 @pytest.mark.parametrize("impl", IMPLS)
