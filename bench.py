@@ -27,6 +27,8 @@ def flop_per_elem(n_feat: int = 28) -> int:
 
 PEAK_FP32_MFMA_TFLOPS = 157.3                      # MI355X dense fp32 matrix
 PEAK_FP32_VALU_TFLOPS = 78.6                       # 256 CU x 4 SIMD x 16 lanes x 2 x 2.4 GHz (no packed fp32)
+PEAK_BF16_MFMA_TFLOPS = 2500.0                     # MI355X dense bf16 matrix
+X6_PRODUCTS = 6                                    # bf16 piece products per fp32 product (bf16x6 path)
 PEAK_HBM_GBS = 8000.0
 # ViT-B/16 step of small_fc_lopt with the fused CUDA kernels on the PyLO page
 # ("Benchmark results" > step-time table): 99.59 ms for 86,563,584 parameters.
@@ -191,9 +193,18 @@ def main():
     stream_bytes = {"k_rowcol_sumsq": 4 * n, "k_stats": 24 * n + 12 * n_vec}
     apply_ms = float(kern_ms[L.KERNEL_NAMES.index("k_apply")])
     fpe = flop_per_elem(args.n_feat)
-    achieved = fpe * n / (apply_ms * 1e-3) / 1e12
+    fp32_equiv = fpe * n / (apply_ms * 1e-3) / 1e12  # the MLP's fp32 FLOP per second
     use_mfma = impl != L.LOPT_MLP_VALU
-    peak = PEAK_FP32_MFMA_TFLOPS if use_mfma else PEAK_FP32_VALU_TFLOPS
+    x6 = impl in (L.LOPT_MLP_AUTO, L.LOPT_MLP_BF16X6)
+    # The roofline of the apply kernel is that of the unit its contraction runs
+    # on: fp32 matrix cores, the vector ALU, or (bf16x6) the bf16 matrix cores,
+    # which execute six bf16 piece products per fp32 product.
+    if x6:
+        achieved, peak, apply_kernel = X6_PRODUCTS * fp32_equiv, PEAK_BF16_MFMA_TFLOPS, "k_apply_bf16x6"
+    elif use_mfma:
+        achieved, peak, apply_kernel = fp32_equiv, PEAK_FP32_MFMA_TFLOPS, "k_apply_mfma"
+    else:
+        achieved, peak, apply_kernel = fp32_equiv, PEAK_FP32_VALU_TFLOPS, "k_apply_valu"
     out = {
         "metric": "G params updated/sec per optimizer step; % of HBM / FP32 roofline",
         "value": round(value, 4),
@@ -209,14 +220,16 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"{w.key}: {w.description}", "n_params": n, "n_tensors": len(w.tensors),
-                   "mlp_impl": {L.LOPT_MLP_VALU: "valu", L.LOPT_MLP_BF16X6: "bf16x6"}.get(impl, "mfma"),
+                   "mlp_impl": "bf16x6" if x6 else "mfma" if use_mfma else "valu",
                    "state": "zero-init, gradients fixed",
                    "variant": "small_fc_lopt" if args.n_feat == 28 else "VeLO-shaped (19 features, 30 inputs)"},
-        "roofline": {"bound": "mfma" if use_mfma else "alu", "kernel": "k_apply",
+        "roofline": {"bound": "mfma" if use_mfma else "alu", "kernel": apply_kernel,
                      "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4),
-                     "traffic": committed_traffic(w.key) if use_mfma and args.n_feat == 28 else None,
-                     "flop_per_elem": fpe, "elems_per_launch": n},
+                     "traffic": committed_traffic(w.key, apply_kernel) if use_mfma and args.n_feat == 28 else None,
+                     "flop_per_elem": fpe * (X6_PRODUCTS if x6 else 1), "elems_per_launch": n,
+                     "fp32_equivalent": {"achieved": round(fp32_equiv, 3), "peak": PEAK_FP32_MFMA_TFLOPS,
+                                         "unit": "TFLOP/s", "frac": round(fp32_equiv / PEAK_FP32_MFMA_TFLOPS, 4)}},
         "step_frac_fp32_peak": round(fpe * n / (ms * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4),
         "kernels_ms": {name: round(float(t), 4) for name, t in zip(L.KERNEL_NAMES, kern_ms)},
         "step_ms_median": round(float(np.median(per_step)), 4),
@@ -240,7 +253,7 @@ def main():
             # the same kernels against what the microbenchmark sustains on this GPU
             out["frac_of_measured"] = {
                 "k_apply_vs_mfma_4waves_2chains": round(achieved / mp["mfma_4waves_2chains_tflops"], 4)
-                if use_mfma else None,
+                if use_mfma and not x6 else None,
                 "k_stats_vs_read_bw": round(out["hbm_kernels"]["k_stats"]["achieved"] /
                                             (max(mp["read_bw_TBps"], mp["read_bw_nontemporal_TBps"]) * 1e3), 4),
             }

@@ -57,7 +57,7 @@ typedef enum lopt_status {
 
 /* Implementation of the per-element MLP in the apply kernel. */
 typedef enum lopt_mlp_impl {
-  LOPT_MLP_AUTO = 0, /* currently the matrix-core path */
+  LOPT_MLP_AUTO = 0, /* currently LOPT_MLP_BF16X6 (the fastest on gfx950) */
   LOPT_MLP_VALU = 1, /* vector FMA, weights broadcast from scalar registers */
   LOPT_MLP_MFMA = 2, /* fp32 matrix-core path (v_mfma_f32_32x32x1_2b_f32 and
                         v_mfma_f32_32x32x2_f32) */

@@ -340,7 +340,7 @@ StepCtx make_ctx(const lopt_handle* h) {
   c.n_tiles0 = int32_t(pl.tiles0.size());
   c.n_segs1 = int32_t(pl.segs1.size());
   c.n_chunks = int32_t(pl.chunks.size());
-  c.mlp_impl = h->cfg.mlp_impl == LOPT_MLP_AUTO ? LOPT_MLP_MFMA : h->cfg.mlp_impl;
+  c.mlp_impl = h->cfg.mlp_impl == LOPT_MLP_AUTO ? LOPT_MLP_BF16X6 : h->cfg.mlp_impl;
   return c;
 }
 

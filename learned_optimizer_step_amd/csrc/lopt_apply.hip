@@ -447,22 +447,22 @@ __device__ __forceinline__ void apply_x6_body(const StepCtx& c, const StepParams
           swap_halves(f0 >= 0 ? F[f0] : 0.f, f1 >= 0 ? F[f1] : 0.f, v[0][k][i], v[1][k][i]);
         }
       }
-    // One block at a time through the three layers (keeps one block's
-    // accumulators live): lane half 0's layer-3 partial sums start at b3.
-    float dpart[2], mpart[2];
+    f32x16 acc1s[2];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      f32x16 acc1;
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) acc1[q] = 0.f;
+      for (int q = 0; q < 16; ++q) acc1s[b][q] = 0.f;
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        u32x4 a[3], bt[3];
+    for (int k = 0; k < 2; ++k) {
+      u32x4 a[3];
 #pragma unroll
-        for (int p = 0; p < 3; ++p) {
-          a[p] = L.a1[k][p][li];
-          if (RU && k == 1) a[p][3] = __builtin_amdgcn_perm(__float_as_uint(piece(ct, p)), a[p][3], 0x07060100u);
-        }
+      for (int p = 0; p < 3; ++p) {
+        a[p] = L.a1[k][p][li];
+        if (RU && k == 1) a[p][3] = __builtin_amdgcn_perm(__float_as_uint(piece(ct, p)), a[p][3], 0x07060100u);
+      }
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        u32x4 bt[3];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const Pieces u0 = split3(v[b][k][2 * j]), u1 = split3(v[b][k][2 * j + 1]);
@@ -471,8 +471,13 @@ __device__ __forceinline__ void apply_x6_body(const StepCtx& c, const StepParams
         }
 #pragma unroll
         for (int t = 0; t < 6; ++t)
-          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[x6_a(t)]), as_bf16x8(bt[x6_b(t)]), acc1, 0, 0, 0);
+          acc1s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[x6_a(t)]), as_bf16x8(bt[x6_b(t)]), acc1s[b], 0, 0, 0);
       }
+    }
+    float dpart[2], mpart[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const f32x16 acc1 = acc1s[b];
       f32x16 acc2;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {

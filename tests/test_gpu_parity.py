@@ -76,6 +76,53 @@ def test_mixed_row_shapes_ten_steps(n_feat, impl):
     check(parity(w, weights, L.config_from(mlp_impl=impl, n_feat=n_feat), torch))
 
 
+def test_update_accuracy_of_each_mlp_path():
+    """The MLP's accuracy, seen through the update: with p = 0 (so no decay
+    term), one step leaves p = -lr step_mult dir exp(exp_mult mag), the MLP
+    output rounded once to fp32.  Over the elements whose update is not tiny
+    (>= 1e-3 of the largest; smaller ones come from cancellation in the last
+    layer):
+      * against the fp64 oracle, every path shows the same error, which comes
+        from the fp32 inputs of the MLP rather than from its evaluation; the
+        bf16x6 path stays within 1.5x of the fp32 paths (rms) and 4x (max);
+      * against the fp32 matrix path on identical inputs (evaluation only),
+        the bf16x6 path differs no more than the vector-ALU path does, which
+        computes the same fp32 products in another summation order."""
+    shapes = [(256, 256), (4096,), (100, 300), (64, 128), (33, 65)]
+    w = W.custom_workload("updacc", shapes, param_std=0.0, grad_std=1e-2, steps=1, wid=176)
+    weights = W.mlp_weights(11, bias_std=0.1)
+    want = oracle_run(w, weights, hyper_from_cfg(L.config_from()), 1)
+    ref = np.concatenate([np.asarray(want[i]["p"], np.float64).ravel() for i in range(len(shapes))])
+    keep = np.zeros(ref.size, bool)
+    off = 0
+    for i in range(len(shapes)):
+        r = np.asarray(want[i]["p"], np.float64).ravel()
+        keep[off:off + r.size] = np.abs(r) >= 1e-3 * np.abs(r).max()
+        off += r.size
+    got = {}
+    for impl in IMPLS:
+        run = GpuRun(w, weights, L.config_from(mlp_impl=impl), torch)
+        run.step(1)
+        got[impl] = np.concatenate([np.asarray(run.fetch(i)["p"], np.float64).ravel() for i in range(len(shapes))])
+        run.close()
+
+    def rel(a, b):
+        e = np.abs(a[keep] - b[keep]) / np.abs(b[keep])
+        return float(np.sqrt(np.mean(e ** 2))), float(e.max())
+
+    vs_oracle = {impl: rel(got[impl], ref) for impl in IMPLS}
+    vs_mfma = {impl: rel(got[impl], got[L.LOPT_MLP_MFMA]) for impl in (L.LOPT_MLP_VALU, L.LOPT_MLP_BF16X6)}
+    for impl in IMPLS:
+        say(f"[update accuracy] impl {impl} vs oracle: rms {vs_oracle[impl][0]:.3e}, max {vs_oracle[impl][1]:.3e}"
+            + (f"; vs fp32 matrix path: rms {vs_mfma[impl][0]:.3e}, max {vs_mfma[impl][1]:.3e}" if impl in vs_mfma
+               else "") + f" ({int(keep.sum())} elements)")
+    x6 = L.LOPT_MLP_BF16X6
+    rms32 = max(vs_oracle[L.LOPT_MLP_MFMA][0], vs_oracle[L.LOPT_MLP_VALU][0])
+    max32 = max(vs_oracle[L.LOPT_MLP_MFMA][1], vs_oracle[L.LOPT_MLP_VALU][1])
+    assert vs_oracle[x6][0] <= 1.5 * rms32 and vs_oracle[x6][1] <= 4.0 * max32, vs_oracle
+    assert vs_mfma[x6][0] <= 2.0 * vs_mfma[L.LOPT_MLP_VALU][0], vs_mfma
+
+
 @pytest.mark.parametrize("impl", IMPLS)
 def test_no_time_features_lr_wd_prewarmed(impl):
     w = W.custom_workload("nt0", [(37, 41), (1, 77), (9,)], grad_std=1e-3, steps=4,
