@@ -65,7 +65,8 @@ typedef enum lopt_mlp_impl {
                          exactly into three bf16 pieces and the six largest
                          piece products accumulated in fp32
                          (v_mfma_f32_32x32x16_bf16); the dropped products are
-                         below 2^-23 of each product (two fp32 roundings) */
+                         below 2^-21 of each product (median below one fp32
+                         rounding) */
 } lopt_mlp_impl;
 
 /* Hyperparameters.  lopt_default_config() fills the defaults shown. */

@@ -265,20 +265,23 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
 
 // ---------------------------------------------------------------------------
 // k_apply_bf16x6: layers 1 and 2 on the bf16 matrix cores.  Every fp32
-// operand x is split into three bf16 pieces, x = h + m + l exactly: h = x
-// rounded to bf16 (nearest), m = r rounded to bf16 with r = x - h (exact in
-// fp32), l = r - m, which has at most 8 significant bits and so is a bf16
-// value itself; |m| <= 2^-8 |x| and |l| <= 2^-16 |x|.  A product a.b is the
-// sum of its nine piece products; the kernel keeps the six whose orders add
-// up to at most 2 (hh, hm, mh, hl, lh, mm), each exact in the fp32
-// accumulation, and leaves out ml, lm, ll, together below 2^-23 |a b| (about
-// two fp32 roundings of the product).  This is the piece-wise emulation of an
-// fp32 GEMM on reduced-precision matrix units known as bf16x6 (bf16x9 keeps
-// all nine).  On gfx950 a v_mfma_f32_32x32x16_bf16 does 16x the FLOP of the
-// fp32 form in half its cycles, and vector instructions of the other waves
-// issue beside it (the fp32 form shares their issue cycles), so the six
-// products cost less than one fp32 product and the split's vector work
-// overlaps the matrix work.
+// operand x is split into three bf16 pieces, x = h + m + l exactly: h is x
+// with its low 16 bits cleared, m the same of r = x - h (exact), and
+// l = r - m, which has at most 8 significant bits (truncation split of the
+// 24-bit significand into 8-bit parts; |m| < 2^-7 |x|, |l| < 2^-15 |x|).  A
+// product a.b is then the sum of the six piece products whose orders add up
+// to at most 2 (hh, hm, mh, hl, lh, mm), each exact in the fp32
+// accumulation; the three dropped ones (ml, lm, ll) stay below 2^-21 |a b|,
+// with a median below one fp32 rounding.  (Rounding the pieces to nearest
+// with v_cvt_pk_bf16_f32 bounds them by 2^-23 at the same instruction count
+// but measured 4.6 % slower.)  This is the piece-wise emulation of an fp32
+// GEMM on reduced-precision matrix units known as bf16x6 (bf16x9 keeps all
+// nine).
+// On gfx950 a v_mfma_f32_32x32x16_bf16 does 16x the FLOP of the fp32 form in
+// half its cycles, and vector instructions of the other waves issue beside
+// it (the fp32 form shares their issue cycles), so the six products cost
+// less than one fp32 product and the split's vector work overlaps the matrix
+// work.
 //
 // Layout (one wave, 64 elements, lane l owns element l; M = hidden unit
 // l%32, K = inputs, N = elements, two 32-element blocks):
@@ -295,26 +298,20 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
 //     columns are visited in that order, as in the fp32 matrix path).
 //   layer 3 on the vector ALU, as in the fp32 matrix path.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// bf16 pair (x0 low, x1 high), each rounded to nearest (v_cvt_pk_bf16_f32).
-__device__ __forceinline__ uint32_t cvt_bf16x2(float x0, float x1) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, bf16x2));
-}
-// The three pieces of x0 and x1 as bf16 pairs: h, m, l (index 0, 1, 2).
-struct Pieces2 {
-  uint32_t p[3];
+// The values whose upper halves are the pieces h, m, l of x.
+struct Pieces {
+  float h, m, l;
 };
-__device__ __forceinline__ Pieces2 split3x2(float x0, float x1) {
-  Pieces2 s;
-  s.p[0] = cvt_bf16x2(x0, x1);
-  const float r0 = x0 - __uint_as_float(s.p[0] << 16), r1 = x1 - __uint_as_float(s.p[0] & 0xffff0000u);
-  s.p[1] = cvt_bf16x2(r0, r1);
-  const float l0 = r0 - __uint_as_float(s.p[1] << 16), l1 = r1 - __uint_as_float(s.p[1] & 0xffff0000u);
-  s.p[2] = cvt_bf16x2(l0, l1);  // exact
-  return s;
+__device__ __forceinline__ Pieces split3(float x) {
+  const float r = x - __uint_as_float(__float_as_uint(x) & 0xffff0000u);
+  return {x, r, r - __uint_as_float(__float_as_uint(r) & 0xffff0000u)};
+}
+__device__ __forceinline__ float piece(const Pieces& p, int k) { return k == 0 ? p.h : k == 1 ? p.m : p.l; }
+// bf16 pair: the upper half of a (low) and of b (high).
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
 }
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -374,22 +371,27 @@ __device__ __forceinline__ void apply_x6_body(const StepCtx& c, const StepParams
         const float w1 = f1 >= 0 ? pk[kPkW1 + row * kNF + f1] * sc[f1] : 0.f;
         v[i] = (k == 1 && i == 7) ? (RU ? 0.f : b1half) : half ? w1 : w0;
       }
-      Pieces2 pc[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) pc[j] = split3x2(v[2 * j], v[2 * j + 1]);
+      for (int p = 0; p < 3; ++p) {
+        u32x4 t;
 #pragma unroll
-      for (int p = 0; p < 3; ++p) L.a1[k][p][lane] = u32x4{pc[0].p[p], pc[1].p[p], pc[2].p[p], pc[3].p[p]};
+        for (int j = 0; j < 4; ++j) t[j] = pack2(piece(split3(v[2 * j]), p), piece(split3(v[2 * j + 1]), p));
+        L.a1[k][p][lane] = t;
+      }
     }
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      Pieces2 pc[4];
+    for (int k = 0; k < 2; ++k)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        pc[j] = split3x2(pk[kPkW2 + row * kH + acc_row(8 * k + 2 * j, half)],
-                         pk[kPkW2 + row * kH + acc_row(8 * k + 2 * j + 1, half)]);
+      for (int p = 0; p < 3; ++p) {
+        u32x4 t;
 #pragma unroll
-      for (int p = 0; p < 3; ++p) L.a2[k][p][lane] = u32x4{pc[0].p[p], pc[1].p[p], pc[2].p[p], pc[3].p[p]};
-    }
+        for (int j = 0; j < 4; ++j) {
+          const float w0 = pk[kPkW2 + row * kH + acc_row(8 * k + 2 * j, half)];
+          const float w1 = pk[kPkW2 + row * kH + acc_row(8 * k + 2 * j + 1, half)];
+          t[j] = pack2(piece(split3(w0), p), piece(split3(w1), p));
+        }
+        L.a2[k][p][lane] = t;
+      }
   }
   float arow[3];       // RU: W1[row][13 + k] * s_(13 + k), the row term's weights
 #pragma unroll
@@ -418,14 +420,13 @@ __device__ __forceinline__ void apply_x6_body(const StepCtx& c, const StepParams
     build_features<VEC, NORMAL, NF>(hp, x, F, cn);
     if (valid) store_state<VEC>(s, e, x, cn);
 
-    Pieces2 ct = {{0u, 0u, 0u}};
+    Pieces ct = {0.f, 0.f, 0.f};
     if (RU) {
       // constant entries: (b1 + row term) / 2 in both lane halves
       const float r0 = __int_as_float(uni(__float_as_int(x.rq[0])));
       const float r1 = __int_as_float(uni(__float_as_int(x.rq[1])));
       const float r2 = __int_as_float(uni(__float_as_int(x.rq[2])));
-      const float c = 0.5f * fmaf(arow[2], r2, fmaf(arow[1], r1, fmaf(arow[0], r0, b1row)));
-      ct = split3x2(c, c);  // the upper halves are used
+      ct = split3(0.5f * fmaf(arow[2], r2, fmaf(arow[1], r1, fmaf(arow[0], r0, b1row))));
     }
     // The A operands are read from LDS where they are used: an offset the
     // compiler cannot see through keeps the reads in the loop (hoisted, the
@@ -460,16 +461,16 @@ __device__ __forceinline__ void apply_x6_body(const StepCtx& c, const StepParams
 #pragma unroll
       for (int p = 0; p < 3; ++p) {
         a[p] = L.a1[k][p][li];
-        if (RU && k == 1) a[p][3] = __builtin_amdgcn_perm(ct.p[p], a[p][3], 0x07060100u);
+        if (RU && k == 1) a[p][3] = __builtin_amdgcn_perm(__float_as_uint(piece(ct, p)), a[p][3], 0x07060100u);
       }
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         u32x4 bt[3];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const Pieces2 u = split3x2(v[b][k][2 * j], v[b][k][2 * j + 1]);
+          const Pieces u0 = split3(v[b][k][2 * j]), u1 = split3(v[b][k][2 * j + 1]);
 #pragma unroll
-          for (int p = 0; p < 3; ++p) bt[p][j] = u.p[p];
+          for (int p = 0; p < 3; ++p) bt[p][j] = pack2(piece(u0, p), piece(u1, p));
         }
 #pragma unroll
         for (int t = 0; t < 6; ++t)
@@ -493,9 +494,10 @@ __device__ __forceinline__ void apply_x6_body(const StepCtx& c, const StepParams
         for (int p = 0; p < 3; ++p) a[p] = L.a2[k][p][li];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const Pieces2 u = split3x2(fmaxf(acc1[8 * k + 2 * j], 0.f), fmaxf(acc1[8 * k + 2 * j + 1], 0.f));
+          const Pieces u0 = split3(fmaxf(acc1[8 * k + 2 * j], 0.f));
+          const Pieces u1 = split3(fmaxf(acc1[8 * k + 2 * j + 1], 0.f));
 #pragma unroll
-          for (int p = 0; p < 3; ++p) bt[p][j] = u.p[p];
+          for (int p = 0; p < 3; ++p) bt[p][j] = pack2(piece(u0, p), piece(u1, p));
         }
 #pragma unroll
         for (int t = 0; t < 6; ++t)
