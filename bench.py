@@ -254,6 +254,8 @@ def main():
             out["frac_of_measured"] = {
                 "k_apply_vs_mfma_4waves_2chains": round(achieved / mp["mfma_4waves_2chains_tflops"], 4)
                 if use_mfma and not x6 else None,
+                "k_apply_vs_bf16_mfma_4waves_2chains": round(achieved / mp["bf16_mfma_4waves_2chains_tflops"], 4)
+                if x6 else None,
                 "k_stats_vs_read_bw": round(out["hbm_kernels"]["k_stats"]["achieved"] /
                                             (max(mp["read_bw_TBps"], mp["read_bw_nontemporal_TBps"]) * 1e3), 4),
             }

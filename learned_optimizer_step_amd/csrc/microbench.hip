@@ -7,7 +7,10 @@
 //   3. what one vector instruction of a given kind adds to a stream of
 //      matrix instructions (4 waves x 2 chains): on gfx950 the fp32 matrix
 //      instructions and the vector ALU share the SIMD's issue, so vector work
-//      adds to the matrix time instead of hiding under it.
+//      adds to the matrix time instead of hiding under it;
+//   4. the same two figures for the bf16 matrix instruction
+//      v_mfma_f32_32x32x16_bf16 (the default apply path), beside which
+//      vector instructions of the other waves do issue.
 // Prints one JSON object.  Every kernel writes only out[block * 64 + lane],
 // and out is sized for the largest grid launched.
 #include <hip/hip_runtime.h>
@@ -16,6 +19,7 @@
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 __global__ __launch_bounds__(256) void read_stream(const float4* __restrict__ a, size_t n4, float* __restrict__ out) {
   float acc = 0.f;
@@ -101,6 +105,56 @@ __global__ __launch_bounds__(64) void mfma_plus(float* out, int iters, float s) 
   }
   float acc = 0.f;
   for (int i = 0; i < 16; ++i) acc += a0[i] + a1[i] + v[i] + float(u[i]);
+  out[size_t(blockIdx.x) * 64 + threadIdx.x] = acc;
+}
+
+// bf16 operands (8 per lane) from two floats.
+__device__ __forceinline__ bf16x8 bf16_operand(float a, float b) {
+  bf16x8 v;
+  for (int i = 0; i < 8; ++i) v[i] = (__bf16)(i & 1 ? b : a);
+  return v;
+}
+
+// 16 bf16 matrix instructions per iteration over NACC independent accumulators.
+template <int NACC>
+__global__ __launch_bounds__(64) void mfma_bf16_chains(float* out, int iters, float s) {
+  f32x16 a[NACC];
+#pragma unroll
+  for (int k = 0; k < NACC; ++k) a[k] = f32x16{0};
+  const bf16x8 x = bf16_operand(s * threadIdx.x * 1e-3f, s), y = bf16_operand(s + 1e-3f, s * 0.5f);
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int r = 0; r < 16 / NACC; ++r)
+#pragma unroll
+      for (int k = 0; k < NACC; ++k) a[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, y, a[k], 0, 0, 0);
+  }
+  float acc = 0.f;
+#pragma unroll
+  for (int k = 0; k < NACC; ++k)
+    for (int i = 0; i < 16; ++i) acc += a[k][i];
+  out[size_t(blockIdx.x) * 64 + threadIdx.x] = acc;
+}
+
+// 4 bf16 matrix instructions (2 chains) plus 16 independent v_fma_f32 (OP 1)
+// or none (OP 0) per iteration.
+template <int OP>
+__global__ __launch_bounds__(64) void mfma_bf16_plus(float* out, int iters, float s) {
+  f32x16 a0 = {0}, a1 = {0};
+  float v[16];
+  for (int i = 0; i < 16; ++i) v[i] = threadIdx.x * 0.001f + i;
+  const bf16x8 x = bf16_operand(s * threadIdx.x * 1e-3f, s), y = bf16_operand(s + 1e-3f, s * 0.5f);
+  const float xf = s * threadIdx.x;
+  for (int it = 0; it < iters; ++it) {
+    a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, y, a0, 0, 0, 0);
+    a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, y, a1, 0, 0, 0);
+    a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, y, a0, 0, 0, 0);
+    a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, y, a1, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (OP == 1) v[i] = fmaf(v[i], s, xf);
+  }
+  float acc = 0.f;
+  for (int i = 0; i < 16; ++i) acc += a0[i] + a1[i] + v[i];
   out[size_t(blockIdx.x) * 64 + threadIdx.x] = acc;
 }
 
@@ -220,6 +274,26 @@ int main() {
     for (int op = 1; op < 5; ++op)
       printf("%s\"%s\": %.2f", op == 1 ? "" : ", ", names[op], (ms[op] - ms[0]) / ms[0] * 256.0 / count[op]);
     printf("}");
+  }
+  // 4. bf16 matrix instruction: throughput (4 waves x 2 chains; 32768 FLOP
+  // each) and the added cycles per v_fma_f32 beside it (alone, the 4 matrix
+  // instructions of an iteration take 4 x 32 = 128 SIMD cycles)
+  {
+    const int blocks = cus * 4 * 4;
+    const float ms = time_ms([&] {
+      hipLaunchKernelGGL(mfma_bf16_chains<2>, dim3(blocks), dim3(64), 0, 0, out, iters, 1.0001f);
+    });
+    if (ms <= 0.f) return 1;
+    printf(", \"bf16_mfma_4waves_2chains_tflops\": %.1f", double(blocks) * iters * 16 * 32768 / (ms * 1e-3) / 1e12);
+    const int it2 = 8000;
+    const float m0 = time_ms([&] {
+      hipLaunchKernelGGL(mfma_bf16_plus<0>, dim3(blocks), dim3(64), 0, 0, out, it2, 1.0001f);
+    });
+    const float m1 = time_ms([&] {
+      hipLaunchKernelGGL(mfma_bf16_plus<1>, dim3(blocks), dim3(64), 0, 0, out, it2, 1.0001f);
+    });
+    if (m0 <= 0.f || m1 <= 0.f) return 1;
+    printf(", \"added_cycles_per_v_fma_f32_beside_bf16_mfma\": %.2f", (m1 - m0) / m0 * 128.0 / 16);
   }
   printf("}\n");
   CHECK(hipFree(out));
