@@ -124,6 +124,21 @@ def test_update_accuracy_of_each_mlp_path():
 
 
 @pytest.mark.parametrize("impl", IMPLS)
+@pytest.mark.parametrize("scale", ["large", "small"])
+def test_magnitudes_far_from_one(impl, scale):
+    """Parameters many orders of magnitude from 1 (1e6 or 1e-8) and gradients
+    of 1e-2 or 1e-12: one element's features then span a wide range of
+    exponents, which the bf16x6 path's pieces must follow exactly.  (The
+    gradients stay small: an EMA of 1e3-sized gradients that cancels towards
+    zero carries an fp32 error of ~1e-5 absolute, above the parity bar's
+    absolute term, on every path and whatever the MLP does.)"""
+    p_std, g_std = (1e6, 1e-2) if scale == "large" else (1e-8, 1e-12)
+    w = W.custom_workload(f"mag_{scale}", [(64, 64), (300,), (40, 100), (3, 257)], param_std=p_std,
+                          grad_std=g_std, steps=5, wid=177)
+    check(parity(w, mlp(bias_std=0.1), L.config_from(mlp_impl=impl), torch))
+
+
+@pytest.mark.parametrize("impl", IMPLS)
 def test_no_time_features_lr_wd_prewarmed(impl):
     w = W.custom_workload("nt0", [(37, 41), (1, 77), (9,)], grad_std=1e-3, steps=4,
                           prewarm_std=1e-3, wid=102)
