@@ -18,7 +18,7 @@ def test_help_lists_the_options():
     res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--help"],
                          capture_output=True, text=True, timeout=60)
     assert res.returncode == 0
-    for opt in ("--gpus", "--steps", "--warmup", "--workload", "--n-feat", "--impl", "--peaks"):
+    for opt in ("--gpus", "--steps", "--warmup", "--workload", "--n-feat", "--impl", "--peaks", "--no-fp32-compare"):
         assert opt in res.stdout
 
 
