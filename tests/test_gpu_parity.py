@@ -139,6 +139,16 @@ def test_magnitudes_far_from_one(impl, scale):
 
 
 @pytest.mark.parametrize("impl", IMPLS)
+def test_mlp_weights_four_times_larger(impl):
+    """The test MLP's weights and biases scaled by 4: hidden activations and
+    every operand the matrix paths split move further from 1 (and layer 3's
+    output into the range where exp(mag exp_mult) matters more)."""
+    w = W.custom_workload("bigw", [(64, 128), (3000,), (33, 65), (200, 7)], grad_std=1e-2, steps=5, wid=178)
+    weights = (4.0 * mlp(bias_std=0.2)).astype(np.float32)
+    check(parity(w, weights, L.config_from(mlp_impl=impl), torch))
+
+
+@pytest.mark.parametrize("impl", IMPLS)
 def test_no_time_features_lr_wd_prewarmed(impl):
     w = W.custom_workload("nt0", [(37, 41), (1, 77), (9,)], grad_std=1e-3, steps=4,
                           prewarm_std=1e-3, wid=102)
