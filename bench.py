@@ -28,7 +28,9 @@ def flop_per_elem(n_feat: int = 28) -> int:
 PEAK_FP32_MFMA_TFLOPS = 157.3                      # MI355X dense fp32 matrix
 PEAK_FP32_VALU_TFLOPS = 78.6                       # 256 CU x 4 SIMD x 16 lanes x 2 x 2.4 GHz (no packed fp32)
 PEAK_BF16_MFMA_TFLOPS = 2500.0                     # MI355X dense bf16 matrix
+PEAK_FP16_MFMA_TFLOPS = 2500.0                     # MI355X dense fp16 matrix
 X6_PRODUCTS = 6                                    # bf16 piece products per fp32 product (bf16x6 path)
+X3_PRODUCTS = 3                                    # fp16 piece products per fp32 product (fp16x3 path)
 PEAK_HBM_GBS = 8000.0
 # ViT-B/16 step of small_fc_lopt with the fused CUDA kernels on the PyLO page
 # ("Benchmark results" > step-time table): 99.59 ms for 86,563,584 parameters.
@@ -111,7 +113,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="vit_b16")
-    ap.add_argument("--impl", default="auto", choices=["auto", "valu", "mfma", "bf16x6"])
+    ap.add_argument("--impl", default="auto", choices=["auto", "valu", "mfma", "bf16x6", "fp16x3"])
     ap.add_argument("--n-feat", type=int, default=28, choices=(28, 19),
                     help="per-element features: 28 (small_fc_lopt) or 19 (the VeLO-shaped variant)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -134,7 +136,7 @@ def main():
     from learned_optimizer_step_amd import workloads as W
 
     impl = {"auto": L.LOPT_MLP_AUTO, "valu": L.LOPT_MLP_VALU, "mfma": L.LOPT_MLP_MFMA,
-            "bf16x6": L.LOPT_MLP_BF16X6}[args.impl]
+            "bf16x6": L.LOPT_MLP_BF16X6, "fp16x3": L.LOPT_MLP_FP16X3}[args.impl]
     w = W.get_workload(args.workload)
     log(f"[bench] {w.key}: {len(w.tensors)} tensors, {w.n_params} params; generating inputs")
     dev = torch.device("cuda:0")
@@ -222,11 +224,14 @@ def main():
     fp32_equiv = fpe * n / (apply_ms * 1e-3) / 1e12  # the MLP's fp32 FLOP per second
     use_mfma = impl != L.LOPT_MLP_VALU
     x6 = impl in (L.LOPT_MLP_AUTO, L.LOPT_MLP_BF16X6)
+    x3 = impl == L.LOPT_MLP_FP16X3
     # The roofline of the apply kernel is that of the unit its contraction runs
     # on: fp32 matrix cores, the vector ALU, or (bf16x6) the bf16 matrix cores,
     # which execute six bf16 piece products per fp32 product.
     if x6:
         achieved, peak, apply_kernel = X6_PRODUCTS * fp32_equiv, PEAK_BF16_MFMA_TFLOPS, "k_apply_bf16x6"
+    elif x3:
+        achieved, peak, apply_kernel = X3_PRODUCTS * fp32_equiv, PEAK_FP16_MFMA_TFLOPS, "k_apply_fp16x3"
     elif use_mfma:
         achieved, peak, apply_kernel = fp32_equiv, PEAK_FP32_MFMA_TFLOPS, "k_apply_mfma"
     else:
@@ -246,14 +251,14 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"{w.key}: {w.description}", "n_params": n, "n_tensors": len(w.tensors),
-                   "mlp_impl": "bf16x6" if x6 else "mfma" if use_mfma else "valu",
+                   "mlp_impl": "bf16x6" if x6 else "fp16x3" if x3 else "mfma" if use_mfma else "valu",
                    "state": "zero-init, gradients fixed",
                    "variant": "small_fc_lopt" if args.n_feat == 28 else "VeLO-shaped (19 features, 30 inputs)"},
         "roofline": {"bound": "mfma" if use_mfma else "alu", "kernel": apply_kernel,
                      "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4),
                      "traffic": committed_traffic(w.key, apply_kernel) if use_mfma and args.n_feat == 28 else None,
-                     "flop_per_elem": fpe * (X6_PRODUCTS if x6 else 1), "elems_per_launch": n,
+                     "flop_per_elem": fpe * (X6_PRODUCTS if x6 else X3_PRODUCTS if x3 else 1), "elems_per_launch": n,
                      "fp32_equivalent": {"achieved": round(fp32_equiv, 3), "peak": PEAK_FP32_MFMA_TFLOPS,
                                          "unit": "TFLOP/s", "frac": round(fp32_equiv / PEAK_FP32_MFMA_TFLOPS, 4)}},
         "step_frac_fp32_peak": round(fpe * n / (ms * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4),
@@ -280,7 +285,7 @@ def main():
             # the same kernels against what the microbenchmark sustains on this GPU
             out["frac_of_measured"] = {
                 "k_apply_vs_mfma_4waves_2chains": round(achieved / mp["mfma_4waves_2chains_tflops"], 4)
-                if use_mfma and not x6 else None,
+                if use_mfma and not (x6 or x3) else None,
                 "k_apply_vs_bf16_mfma_4waves_2chains": round(achieved / mp["bf16_mfma_4waves_2chains_tflops"], 4)
                 if x6 else None,
                 "k_stats_vs_read_bw": round(out["hbm_kernels"]["k_stats"]["achieved"] /

@@ -61,12 +61,23 @@ typedef enum lopt_mlp_impl {
   LOPT_MLP_VALU = 1, /* vector FMA, weights broadcast from scalar registers */
   LOPT_MLP_MFMA = 2, /* fp32 matrix-core path (v_mfma_f32_32x32x1_2b_f32 and
                         v_mfma_f32_32x32x2_f32) */
-  LOPT_MLP_BF16X6 = 3 /* bf16 matrix-core path with every fp32 operand split
-                         exactly into three bf16 pieces and the six largest
-                         piece products accumulated in fp32
-                         (v_mfma_f32_32x32x16_bf16); the dropped products are
-                         below 2^-21 of each product (median below one fp32
-                         rounding) */
+  LOPT_MLP_BF16X6 = 3, /* bf16 matrix-core path with every fp32 operand split
+                          exactly into three bf16 pieces and the six largest
+                          piece products accumulated in fp32
+                          (v_mfma_f32_32x32x16_bf16); the dropped products are
+                          below 2^-21 of each product (median below one fp32
+                          rounding) */
+  LOPT_MLP_FP16X3 = 4  /* fp16 matrix-core path (v_mfma_f32_32x32x16_f16): the
+                          features normalised first, every operand split into
+                          two fp16 pieces (22 significant bits) and the three
+                          largest piece products accumulated in fp32; a wave
+                          whose layer-2 inputs leave fp16's range is rescaled
+                          by a power of two.  Faster than LOPT_MLP_BF16X6,
+                          slightly less accurate for values far below 1.
+                          lopt_create / lopt_set_config refuse it
+                          (LOPT_ERR_UNSUPPORTED) for weights of magnitude
+                          2^15 or more, or whose first-layer row-feature
+                          weights are too large for its constant term. */
 } lopt_mlp_impl;
 
 /* Hyperparameters.  lopt_default_config() fills the defaults shown. */

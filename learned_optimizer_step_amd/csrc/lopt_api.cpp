@@ -100,7 +100,7 @@ void validate_config(const lopt_config* c) {
   for (int q = 0; q < c->n_time; ++q)
     if (!(c->timescales[q] > 0.f) || !finite(c->timescales[q]))
       fail(LOPT_ERR_INVALID_ARGUMENT, "timescales must be finite and > 0");
-  if (c->mlp_impl < LOPT_MLP_AUTO || c->mlp_impl > LOPT_MLP_BF16X6)
+  if (c->mlp_impl < LOPT_MLP_AUTO || c->mlp_impl > LOPT_MLP_FP16X3)
     fail(LOPT_ERR_INVALID_ARGUMENT, "unknown mlp_impl");
   if (c->n_feat != LOPT_N_FEATURES && c->n_feat != LOPT_VELO_FEATURES)
     fail(LOPT_ERR_INVALID_ARGUMENT, "n_feat must be 28 or 19");
@@ -300,6 +300,8 @@ struct lopt_handle {
   lopt_config cfg{};
   int device = 0;
   float* d_mlp = nullptr;
+  // fp16x3 path: the constant-entry shift, or -1 when the weights do not fit
+  int32_t x3_shift = -1;
   bool bound = false;
   Plan plan;
   char* ws = nullptr;
@@ -373,6 +375,7 @@ StepParams make_params(const lopt_handle* h) {
   p.per_tensor = h->th_active ? 1 : 0;
   p.n_time = c.n_time;
   p.n_feat = c.n_feat;
+  p.x3_shift = h->x3_shift > 0 ? h->x3_shift : 0;
   for (int q = 0; q < kMaxTime; ++q) p.timescales[q] = q < c.n_time ? c.timescales[q] : 1.f;
   return p;
 }
@@ -467,6 +470,35 @@ void check_same_list(const lopt_handle* h, const lopt_tensor* ts, int32_t n, boo
   if (*grads_changed) validate_tensors(ts, n);
 }
 
+// The fp16x3 path's bound on its constant layer-1 entries, (b1' + row term) / 2
+// with b1' = b1 plus the step features (|tanh| <= 1) and the row term the
+// three normalised row features (each at most sqrt(n) < 46341 for n < 2^31)
+// times their weights: the smallest shift k with bound * 2^-k < 2^15, or -1
+// when k would exceed 14 or a weight has magnitude 2^15 or more (fp16 pieces).
+int32_t fp16x3_shift(const float* mlp, int32_t n_feat, int32_t n_time) {
+  const int din = n_feat + n_time;
+  const size_t nw = lopt_mlp_floats(n_feat, n_time);
+  for (size_t i = 0; i < nw; ++i)
+    if (!(std::fabs(mlp[i]) < 32768.f)) return -1;
+  const float* W1 = mlp;
+  const float* b1 = W1 + kH * din;
+  double bound = 0.0;
+  for (int u = 0; u < kH; ++u) {
+    double c = std::fabs(double(b1[u]));
+    for (int s = 0; s < n_time; ++s) c += std::fabs(double(W1[u * din + n_feat + s]));
+    for (int k = 0; k < 3; ++k) c += 46341.0 * std::fabs(double(W1[u * din + 13 + k]));
+    bound = std::max(bound, 0.5 * c * 1.001);
+  }
+  int32_t k = 0;
+  while (bound * std::ldexp(1.0, -k) >= 32768.0) ++k;
+  return k <= 14 ? k : -1;
+}
+
+void check_fp16x3(const lopt_handle* h, const lopt_config* cfg) {
+  if (cfg->mlp_impl == LOPT_MLP_FP16X3 && h->x3_shift < 0)
+    fail(LOPT_ERR_UNSUPPORTED, "the MLP weights are too large for mlp_impl = LOPT_MLP_FP16X3");
+}
+
 }  // namespace
 
 extern "C" {
@@ -516,7 +548,9 @@ lopt_status lopt_create(const lopt_config* cfg, const float* mlp_host, lopt_hand
       if (!std::isfinite(mlp_host[i])) fail(LOPT_ERR_INVALID_ARGUMENT, "MLP weights must be finite");
     auto* h = new lopt_handle();
     h->cfg = *cfg;
+    h->x3_shift = fp16x3_shift(mlp_host, cfg->n_feat, cfg->n_time);
     try {
+      check_fp16x3(h, cfg);
       hip_check(hipGetDevice(&h->device), "hipGetDevice");
       hip_check(hipMalloc(reinterpret_cast<void**>(&h->d_mlp), nw * sizeof(float)), "hipMalloc(weights)");
       hip_check(hipMemcpy(h->d_mlp, mlp_host, nw * sizeof(float), hipMemcpyHostToDevice), "hipMemcpy(weights)");
@@ -633,6 +667,7 @@ lopt_status lopt_set_config(lopt_handle* h, const lopt_config* cfg) {
     validate_config(cfg);
     if (cfg->n_time != h->cfg.n_time || cfg->n_feat != h->cfg.n_feat)
       fail(LOPT_ERR_INVALID_ARGUMENT, "n_feat and n_time are fixed by the MLP weights given to lopt_create");
+    check_fp16x3(h, cfg);
     h->cfg = *cfg;
     if (h->th_active) h->th_dirty = true;  // lr_step depends on step_mult
   });

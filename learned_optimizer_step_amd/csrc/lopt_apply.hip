@@ -7,6 +7,8 @@
 // accumulators; a NaN pre-activation leaves the ReLU as 0 either way).
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "lopt_device.h"
 
 namespace lopt {
@@ -540,11 +542,284 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   });
 }
 
+// ---------------------------------------------------------------------------
+// k_apply_fp16x3: the same layout on the fp16 matrix cores
+// (v_mfma_f32_32x32x16_f16) with two pieces and three products.  An operand x
+// is split as h = fp16(x) (nearest) and l = fp16(x - h), 22 significant bits;
+// a.b is taken as hh + hl + lh (the dropped ll is below 2^-22 |a b|).  fp16's
+// range is the constraint, so the features are normalised on the vector ALU
+// first (x = F s, with |x| <= sqrt(n) < 46341 for every element, and W1
+// unscaled in the A operand), and the two values without such a bound are
+// rescaled by powers of two:
+//   * the constant entries (b1 plus the row term) carry value * 2^-k against a
+//     B value of 2^k, k = x3_shift from a bound on the weights;
+//   * a wave whose layer-2 inputs (layer-1 outputs) reach 2^15 scales them by
+//     2^-j, starts layer 2 from b2 2^-j, and multiplies its layer-3 sums by 2^j
+//     (a ballot over the lanes; the scaling runs only in such a wave).
+// Elements far below 1 lose bits in fp16's subnormal range, so this path is
+// less accurate than k_apply_bf16x6 on them; it is selected explicitly.
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// The two fp16 pieces of x0 and x1 as fp16 pairs: h, l (index 0, 1).
+struct Pieces2h {
+  uint32_t p[2];
+};
+__device__ __forceinline__ Pieces2h split2x2(float x0, float x1) {
+  Pieces2h s;
+  const f16x2 h = __builtin_convertvector(f32x2{x0, x1}, f16x2);
+  s.p[0] = __builtin_bit_cast(uint32_t, h);
+  const float r0 = x0 - (float)h.x, r1 = x1 - (float)h.y;
+  s.p[1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{r0, r1}, f16x2));
+  return s;
+}
+__device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
+// (A piece, B piece) of product t of the three, smallest first: hl, lh, hh.
+__device__ constexpr int x3_a(int t) { return t == 1 ? 1 : 0; }
+__device__ constexpr int x3_b(int t) { return t == 0 ? 1 : 0; }
+
+template <bool VEC, bool NORMAL, int NF, bool RU>
+__device__ __forceinline__ void apply_x3_body(const StepCtx& c, const StepParams& hp, const Chunk& ch,
+                                              const TensorDesc& d, const float* g, X6Lds& L) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = lane >> 5;
+  const int row = lane & 31;
+  const Streams s = make_streams(d, g, c.ws, ch);
+  const float* __restrict__ pk = c.packed;
+  const float* __restrict__ sc = c.scales + size_t(ch.tensor) * kStatStride;
+  const float cscale = __builtin_ldexpf(1.0f, -hp.x3_shift);  // exact powers of two
+  const float bconst = __builtin_ldexpf(1.0f, hp.x3_shift);
+
+  // A operands (two pieces), built once per chunk by the first wave: layer 1
+  // from W1 unscaled (the features carry the scales), its constant entries
+  // (1, 7) as for k_apply_bf16x6 but times 2^-k; layer 2 from W2.
+  if (threadIdx.x < 64) {
+    const float b1half = 0.5f * pk[kPkB1 + row] * cscale;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int q = 2 * (8 * k + i);
+        const int f0 = x6_feature(q, NF, RU), f1 = x6_feature(q + 1, NF, RU);
+        const float w0 = f0 >= 0 ? pk[kPkW1 + row * kNF + f0] : 0.f;
+        const float w1 = f1 >= 0 ? pk[kPkW1 + row * kNF + f1] : 0.f;
+        v[i] = (k == 1 && i == 7) ? (RU ? 0.f : b1half) : half ? w1 : w0;
+      }
+      Pieces2h pc[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pc[j] = split2x2(v[2 * j], v[2 * j + 1]);
+#pragma unroll
+      for (int p = 0; p < 2; ++p) L.a1[k][p][lane] = u32x4{pc[0].p[p], pc[1].p[p], pc[2].p[p], pc[3].p[p]};
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      Pieces2h pc[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        pc[j] = split2x2(pk[kPkW2 + row * kH + acc_row(8 * k + 2 * j, half)],
+                         pk[kPkW2 + row * kH + acc_row(8 * k + 2 * j + 1, half)]);
+#pragma unroll
+      for (int p = 0; p < 2; ++p) L.a2[k][p][lane] = u32x4{pc[0].p[p], pc[1].p[p], pc[2].p[p], pc[3].p[p]};
+    }
+  }
+  float arow[3];       // RU: W1[row][13 + k] * s_(13 + k), the row term's weights
+#pragma unroll
+  for (int k = 0; k < 3; ++k) arow[k] = RU ? pk[kPkW1 + row * kNF + 13 + k] * sc[13 + k] : 0.f;
+  const float b1row = RU ? pk[kPkB1 + row] : 0.f;
+  float scl[kNF];      // the tensor's feature scales (wave-uniform)
+#pragma unroll
+  for (int f = 0; f < kNF; ++f) scl[f] = f < NF ? __int_as_float(uni(__float_as_int(sc[f]))) : 0.f;
+
+  if (threadIdx.x < 96) {
+    const int which = threadIdx.x >> 5, h = (threadIdx.x >> 4) & 1, q = threadIdx.x & 15;
+    const int hr = acc_row(q, h);
+    const float v = which == 0 ? pk[kPkB2 + hr] : which == 1 ? pk[kPkW3 + hr] : pk[kPkW3 + kH + hr];
+    reinterpret_cast<float*>(&L.tab[which][h][0])[q] = v;
+  }
+  __syncthreads();
+  const float b3d = pk[kPkB3], b3m = pk[kPkB3 + 1];
+  float decay, lr_step;
+  update_constants(c, hp, ch, decay, lr_step);
+  uint32_t base = ch.e0 + wave * 64;
+  if (base >= ch.e1) return;
+  for (; base < ch.e1; base += kBlock) {
+    const uint32_t e = base + lane;
+    const bool valid = e < ch.e1;
+    Elem x;
+    load_elem<VEC, RU && !VEC>(s, valid ? e : base, x, base);
+    const float p_decayed = x.p * decay;
+    float F[kNF], cn[3];
+    build_features<VEC, NORMAL, NF>(hp, x, F, cn);
+    if (valid) store_state<VEC>(s, e, x, cn);
+
+    Pieces2h ct = {{0u, 0u}};
+    if (RU) {
+      // constant entries: (b1 + row term) / 2 * 2^-k in both lane halves
+      const float r0 = __int_as_float(uni(__float_as_int(x.rq[0])));
+      const float r1 = __int_as_float(uni(__float_as_int(x.rq[1])));
+      const float r2 = __int_as_float(uni(__float_as_int(x.rq[2])));
+      const float cv = 0.5f * cscale * fmaf(arow[2], r2, fmaf(arow[1], r1, fmaf(arow[0], r0, b1row)));
+      ct = split2x2(cv, cv);  // the upper halves are used
+    }
+    int li = lane;
+    asm volatile("" : "+v"(li));
+    // normalised layer-1 B values, exchanged between the lane halves
+    float v[2][2][8];
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int q = 2 * (8 * k + i);
+        const int f0 = x6_feature(q, NF, RU), f1 = x6_feature(q + 1, NF, RU);
+        if (k == 1 && i == 7) {
+          v[0][k][i] = v[1][k][i] = bconst;
+        } else if (f0 < 0 && f1 < 0) {
+          v[0][k][i] = v[1][k][i] = 0.f;
+        } else {
+          swap_halves(f0 >= 0 ? F[f0] * scl[f0] : 0.f, f1 >= 0 ? F[f1] * scl[f1] : 0.f, v[0][k][i], v[1][k][i]);
+        }
+      }
+    f32x16 acc1s[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc1s[b][q] = 0.f;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      u32x4 a[2];
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        a[p] = L.a1[k][p][li];
+        if (RU && k == 1) a[p][3] = __builtin_amdgcn_perm(ct.p[p], a[p][3], 0x07060100u);
+      }
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        u32x4 bt[2];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const Pieces2h u = split2x2(v[b][k][2 * j], v[b][k][2 * j + 1]);
+          bt[0][j] = u.p[0];
+          bt[1][j] = u.p[1];
+        }
+#pragma unroll
+        for (int t = 0; t < 3; ++t)
+          acc1s[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(a[x3_a(t)]), as_f16x8(bt[x3_b(t)]), acc1s[b], 0, 0, 0);
+      }
+    }
+    // ReLU in place, and the range guard of the layer-2 inputs
+    float top = 0.f;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        acc1s[b][q] = fmaxf(acc1s[b][q], 0.f);
+        top = fmaxf(top, acc1s[b][q]);
+      }
+    // Layers 2 and 3 for both blocks; SCALED: the wave's layer-2 inputs are
+    // multiplied by s2 = 2^-j (b2 and b3 too) and the layer-3 sums by 2^j.
+    float dpart[2], mpart[2];
+    auto layers23 = [&](auto scaled_tag, float s2, float s2inv) {
+      constexpr bool SCALED = decltype(scaled_tag)::value;
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        f32x16 acc2;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 w = L.tab[0][half][q];
+          acc2[4 * q] = w.x; acc2[4 * q + 1] = w.y; acc2[4 * q + 2] = w.z; acc2[4 * q + 3] = w.w;
+        }
+        if (SCALED) {
+#pragma unroll
+          for (int q = 0; q < 16; ++q) acc2[q] *= s2;
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          u32x4 a[2], bt[2];
+#pragma unroll
+          for (int p = 0; p < 2; ++p) a[p] = L.a2[k][p][li];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            float x0 = acc1s[b][8 * k + 2 * j], x1 = acc1s[b][8 * k + 2 * j + 1];
+            if (SCALED) {
+              x0 *= s2;
+              x1 *= s2;
+            }
+            const Pieces2h u = split2x2(x0, x1);
+            bt[0][j] = u.p[0];
+            bt[1][j] = u.p[1];
+          }
+#pragma unroll
+          for (int t = 0; t < 3; ++t)
+            acc2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(a[x3_a(t)]), as_f16x8(bt[x3_b(t)]), acc2, 0, 0, 0);
+        }
+        // half 0's partial sums start at b3, so the sum of the two halves holds it once
+        float dsum = half ? 0.f : b3d, msum = half ? 0.f : b3m;
+        if (SCALED) {
+          dsum *= s2;
+          msum *= s2;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 wd = L.tab[1][half][q], wm = L.tab[2][half][q];
+          const float hq[4] = {fmaxf(acc2[4 * q], 0.f), fmaxf(acc2[4 * q + 1], 0.f), fmaxf(acc2[4 * q + 2], 0.f),
+                               fmaxf(acc2[4 * q + 3], 0.f)};
+          dsum = fmaf(wd.x, hq[0], dsum); msum = fmaf(wm.x, hq[0], msum);
+          dsum = fmaf(wd.y, hq[1], dsum); msum = fmaf(wm.y, hq[1], msum);
+          dsum = fmaf(wd.z, hq[2], dsum); msum = fmaf(wm.z, hq[2], msum);
+          dsum = fmaf(wd.w, hq[3], dsum); msum = fmaf(wm.w, hq[3], msum);
+        }
+        if (SCALED) {
+          dsum *= s2inv;
+          msum *= s2inv;
+        }
+        dpart[b] = dsum;
+        mpart[b] = msum;
+      }
+    };
+    if (__builtin_amdgcn_ballot_w64(!(top < 32768.f)) == 0) {
+      layers23(std::false_type{}, 1.f, 1.f);
+    } else {
+      // rare: scale the wave by 2^-j so that its largest input is below 2^15
+      float m = top;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+      int ex;
+      (void)__builtin_frexpf(m, &ex);  // m < 2^ex
+      const int j = ex > 15 ? ex - 15 : 1;
+      layers23(std::true_type{}, __builtin_ldexpf(1.0f, -j), __builtin_ldexpf(1.0f, j));
+    }
+    float d0, d1, m0, m1;
+    swap_halves(dpart[0], dpart[1], d0, d1);
+    swap_halves(mpart[0], mpart[1], m0, m1);
+    const float dir = d0 + d1;
+    const float mag = m0 + m1;
+    if (valid) store_param(s, e, fmaf(-lr_step, dir * __builtin_amdgcn_exp2f(mag * hp.exp2_mult), p_decayed));
+  }
+}
+
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void k_apply_fp16x3(StepCtx c, StepParams hp) {
+  Chunk ch;
+  TensorDesc d;
+  const float* g;
+  load_chunk(c, blockIdx.x, ch, d, g);
+  if (!g) return;  // no gradient this step: the tensor is skipped
+  __shared__ X6Lds lds;
+  dispatch_variant<true>(d, hp, [&](auto v) {
+    using V = decltype(v);
+    apply_x3_body<V::vec, V::normal, V::nf, V::rowuni>(c, hp, ch, d, g, lds);
+  });
+}
+
 hipError_t launch_apply(const StepCtx& c, const StepParams& p, hipStream_t s) {
   if (c.mlp_impl == 1)
     hipLaunchKernelGGL(k_apply_valu, dim3(c.n_chunks), dim3(kBlock), 0, s, c, p);
   else if (c.mlp_impl == 3)
     hipLaunchKernelGGL(k_apply_bf16x6, dim3(c.n_chunks), dim3(kBlock), 0, s, c, p);
+  else if (c.mlp_impl == 4)
+    hipLaunchKernelGGL(k_apply_fp16x3, dim3(c.n_chunks), dim3(kBlock), 0, s, c, p);
   else
     hipLaunchKernelGGL(k_apply_mfma, dim3(c.n_chunks), dim3(kBlock), 0, s, c, p);
   return hipGetLastError();

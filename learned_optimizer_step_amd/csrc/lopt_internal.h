@@ -113,6 +113,10 @@ struct StepParams {
   int32_t per_tensor;
   int32_t n_feat;            // kNF or kVeloNF
   int32_t n_time;
+  // fp16x3 path: the constant layer-1 entries carry (b1 + row term) / 2 times
+  // 2^-x3_shift against a B value of 2^x3_shift, which keeps them inside
+  // fp16's range for every input (the shift is bounded from the weights)
+  int32_t x3_shift;
   float timescales[kMaxTime];
 };
 

@@ -19,7 +19,7 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU container
 from learned_optimizer_step_amd import lopt as L  # noqa: E402
 from learned_optimizer_step_amd import workloads as W  # noqa: E402
 
-IMPLS = [L.LOPT_MLP_VALU, L.LOPT_MLP_MFMA, L.LOPT_MLP_BF16X6]
+IMPLS = [L.LOPT_MLP_VALU, L.LOPT_MLP_MFMA, L.LOPT_MLP_BF16X6, L.LOPT_MLP_FP16X3]
 
 EDGE_SHAPES = [(1,), (2,), (3,), (15,), (16,), (17,), (63,), (65,), (40000,),
                (1, 1), (2, 3), (3, 1), (7, 1), (17, 33), (65, 3), (4, 513), (300, 2),
@@ -57,7 +57,7 @@ def test_edge_shapes_ten_steps(impl):
     check(parity(w, mlp(bias_std=0.1), L.config_from(mlp_impl=impl), torch))
 
 
-MATRIX_IMPLS = [L.LOPT_MLP_MFMA, L.LOPT_MLP_BF16X6]
+MATRIX_IMPLS = [L.LOPT_MLP_MFMA, L.LOPT_MLP_BF16X6, L.LOPT_MLP_FP16X3]
 
 
 @pytest.mark.parametrize("impl", MATRIX_IMPLS)
@@ -82,12 +82,14 @@ def test_update_accuracy_of_each_mlp_path():
     output rounded once to fp32.  Over the elements whose update is not tiny
     (>= 1e-3 of the largest; smaller ones come from cancellation in the last
     layer):
-      * against the fp64 oracle, every path shows the same error, which comes
-        from the fp32 inputs of the MLP rather than from its evaluation; the
-        bf16x6 path stays within 1.5x of the fp32 paths (rms) and 4x (max);
+      * against the fp64 oracle, every path shows about the same error, which
+        comes from the fp32 inputs of the MLP rather than from its evaluation;
+        the bf16x6 and fp16x3 paths stay within 1.5x of the fp32 paths (rms)
+        and 4x (max);
       * against the fp32 matrix path on identical inputs (evaluation only),
-        the bf16x6 path differs no more than the vector-ALU path does, which
-        computes the same fp32 products in another summation order."""
+        the bf16x6 and fp16x3 paths differ at most twice as much as the
+        vector-ALU path does, which computes the same fp32 products in another
+        summation order."""
     shapes = [(256, 256), (4096,), (100, 300), (64, 128), (33, 65)]
     w = W.custom_workload("updacc", shapes, param_std=0.0, grad_std=1e-2, steps=1, wid=176)
     weights = W.mlp_weights(11, bias_std=0.1)
@@ -111,16 +113,17 @@ def test_update_accuracy_of_each_mlp_path():
         return float(np.sqrt(np.mean(e ** 2))), float(e.max())
 
     vs_oracle = {impl: rel(got[impl], ref) for impl in IMPLS}
-    vs_mfma = {impl: rel(got[impl], got[L.LOPT_MLP_MFMA]) for impl in (L.LOPT_MLP_VALU, L.LOPT_MLP_BF16X6)}
+    split_impls = (L.LOPT_MLP_BF16X6, L.LOPT_MLP_FP16X3)
+    vs_mfma = {impl: rel(got[impl], got[L.LOPT_MLP_MFMA]) for impl in (L.LOPT_MLP_VALU,) + split_impls}
     for impl in IMPLS:
         say(f"[update accuracy] impl {impl} vs oracle: rms {vs_oracle[impl][0]:.3e}, max {vs_oracle[impl][1]:.3e}"
             + (f"; vs fp32 matrix path: rms {vs_mfma[impl][0]:.3e}, max {vs_mfma[impl][1]:.3e}" if impl in vs_mfma
                else "") + f" ({int(keep.sum())} elements)")
-    x6 = L.LOPT_MLP_BF16X6
     rms32 = max(vs_oracle[L.LOPT_MLP_MFMA][0], vs_oracle[L.LOPT_MLP_VALU][0])
     max32 = max(vs_oracle[L.LOPT_MLP_MFMA][1], vs_oracle[L.LOPT_MLP_VALU][1])
-    assert vs_oracle[x6][0] <= 1.5 * rms32 and vs_oracle[x6][1] <= 4.0 * max32, vs_oracle
-    assert vs_mfma[x6][0] <= 2.0 * vs_mfma[L.LOPT_MLP_VALU][0], vs_mfma
+    for impl in split_impls:
+        assert vs_oracle[impl][0] <= 1.5 * rms32 and vs_oracle[impl][1] <= 4.0 * max32, vs_oracle
+        assert vs_mfma[impl][0] <= 2.0 * vs_mfma[L.LOPT_MLP_VALU][0], vs_mfma
 
 
 @pytest.mark.parametrize("impl", IMPLS)
@@ -146,6 +149,29 @@ def test_mlp_weights_four_times_larger(impl):
     w = W.custom_workload("bigw", [(64, 128), (3000,), (33, 65), (200, 7)], grad_std=1e-2, steps=5, wid=178)
     weights = (4.0 * mlp(bias_std=0.2)).astype(np.float32)
     check(parity(w, weights, L.config_from(mlp_impl=impl), torch))
+
+
+@pytest.mark.parametrize("impl", IMPLS)
+def test_first_layer_outputs_beyond_fp16_range(impl):
+    """First-layer weights of the per-element features (all but the row and
+    step features) 20000 times the test MLP's: about 1 % of the hidden
+    activations exceed 2^15 and the largest exceed fp16's largest value
+    (checked on the oracle's own activations), so the fp16x3 path must rescale
+    those waves.  lr and exp_mult are divided by 20000 too, which keeps the
+    update near the unscaled MLP's and its conditioning the usual one."""
+    S = 20000.0
+    w = W.custom_workload("bigh1", [(64, 256), (2048,), (40, 100)], grad_std=1e-2, steps=2, wid=179)
+    weights = mlp(bias_std=0.1).copy()
+    w1 = weights[:32 * (L.LOPT_N_FEATURES + 11)].reshape(32, -1)
+    w1[:, [f for f in range(L.LOPT_N_FEATURES) if f not in (13, 14, 15)]] *= S
+    d = L.lopt_default_config()
+    cfg = L.config_from(mlp_impl=impl, lr=1.0 / S, exp_mult=d.exp_mult / S)
+    hp = hyper_from_cfg(cfg).as_f32()
+    m = oracle.unpack_mlp(weights, hp.n_time, hp.n_feat)
+    _, _, info = oracle.step_tensor(W.param_init(w, 0), W.grad_at(w, 0, 1), W.state_init(w, 0), 1, m, hp, keep=True)
+    h1 = np.maximum(info.x.reshape(-1, info.x.shape[-1]) @ m.W1.T + m.b1, 0.0)
+    assert h1.max() > 65504.0, h1.max()
+    check(parity(w, weights, cfg, torch))
 
 
 @pytest.mark.parametrize("impl", IMPLS)
