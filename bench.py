@@ -118,7 +118,7 @@ def main():
                     help="per-element features: 28 (small_fc_lopt) or 19 (the VeLO-shaped variant)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp32-compare", action="store_true",
-                    help="with the bf16x6 MLP path, skip timing the fp32 matrix path on the same inputs")
+                    help="with the bf16x6 MLP path, skip timing the fp32 matrix and fp16x3 paths on the same inputs")
     ap.add_argument("--peaks", action="store_true",
                     help="also run the machine-figure microbenchmark and include it as measured_peaks")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -178,12 +178,9 @@ def main():
                      for k in range(args.steps)])
     kern_ms = kern.mean(axis=0)
     per_step = np.array([events[k][0].elapsed_time(events[k][nk]) for k in range(args.steps)])
-    fp32_cmp = None
-    if impl in (L.LOPT_MLP_AUTO, L.LOPT_MLP_BF16X6) and not args.no_fp32_compare:
-        # the same optimizer and inputs, apply kernel switched to the fp32 matrix path
-        log("[bench] fp32 matrix path on the same inputs")
-        L.lopt_set_config(opt.handle, L.config_from(mlp_impl=L.LOPT_MLP_MFMA, n_feat=args.n_feat))
-        k2 = min(args.steps, 20)
+    def time_path(path_impl, k2=20):
+        """The same optimizer and inputs for k2 more steps with another apply kernel."""
+        L.lopt_set_config(opt.handle, L.config_from(mlp_impl=path_impl, n_feat=args.n_feat))
         for _ in range(2):
             opt.step(grads)
         ev2 = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(k2)]
@@ -198,10 +195,20 @@ def main():
         torch.cuda.synchronize()
         ms2 = (time.perf_counter() - t2) * 1e3 / k2
         L.lopt_set_timing_events(opt.handle, [])
-        ap2 = float(np.mean([ev2[k][L.KERNEL_NAMES.index("k_apply")].elapsed_time(
-            ev2[k][L.KERNEL_NAMES.index("k_apply") + 1]) for k in range(k2)]))
-        fp32_cmp = {"ms_per_step": round(ms2, 4), "value": round(w.n_params / (ms2 * 1e-3) / 1e9, 4),
-                    "apply_ms": round(ap2, 4), "steps": k2}
+        ka = L.KERNEL_NAMES.index("k_apply")
+        ap2 = float(np.mean([ev2[k][ka].elapsed_time(ev2[k][ka + 1]) for k in range(k2)]))
+        return {"ms_per_step": round(ms2, 4), "value": round(w.n_params / (ms2 * 1e-3) / 1e9, 4),
+                "apply_ms": round(ap2, 4), "steps": k2}
+
+    fp32_cmp = fp16_cmp = None
+    if impl in (L.LOPT_MLP_AUTO, L.LOPT_MLP_BF16X6) and not args.no_fp32_compare:
+        # the apply kernel switched to the fp32 matrix path, then to the opt-in fp16x3 path
+        log("[bench] fp32 matrix path and fp16x3 path on the same inputs")
+        fp32_cmp = time_path(L.LOPT_MLP_MFMA)
+        try:
+            fp16_cmp = time_path(L.LOPT_MLP_FP16X3)
+        except L.LoptError as err:  # weights outside the fp16x3 path's range
+            fp16_cmp = {"error": str(err)}
     opt.close()
     if args.calibrate_copy:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
@@ -264,6 +271,7 @@ def main():
         "step_frac_fp32_peak": round(fpe * n / (ms * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4),
         "kernels_ms": {name: round(float(t), 4) for name, t in zip(L.KERNEL_NAMES, kern_ms)},
         "fp32_matrix_path": fp32_cmp,
+        "fp16x3_path": fp16_cmp,
         "step_ms_median": round(float(np.median(per_step)), 4),
         "step_ms_min": round(float(per_step.min()), 4),
         "step_frac_hbm": round(step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),

@@ -148,6 +148,22 @@ def test_create_rejects_bad_config_without_device(lib):
     assert h.value is None
 
 
+def test_create_refuses_fp16x3_for_weights_outside_its_range_without_device(lib):
+    """LOPT_MLP_FP16X3 needs weights below 2^15 and a constant-term shift of at
+    most 14 (first-layer row-feature weights times sqrt(2^31)); otherwise
+    lopt_create refuses it before touching the device."""
+    h = ctypes.c_void_p()
+    c = L.config_from(mlp_impl=L.LOPT_MLP_FP16X3)
+    big = (ctypes.c_float * 2402)()
+    big[5] = 40000.0                      # a W1 entry beyond fp16's piece range
+    assert lib.lopt_create(ctypes.byref(c), big, ctypes.byref(h)) == L.LOPT_ERR_UNSUPPORTED
+    assert "LOPT_MLP_FP16X3" in L.lopt_last_error()
+    rowf = (ctypes.c_float * 2402)()
+    rowf[13] = 30000.0                    # W1[0][13]: row term up to ~7e8, shift 15
+    assert lib.lopt_create(ctypes.byref(c), rowf, ctypes.byref(h)) == L.LOPT_ERR_UNSUPPORTED
+    assert h.value is None
+
+
 def test_null_handle_calls(lib):
     t = ctypes.c_int64()
     assert lib.lopt_get_step(None, ctypes.byref(t)) == L.LOPT_ERR_INVALID_ARGUMENT
