@@ -294,14 +294,21 @@ Plan build_plan(const lopt_tensor* ts, int32_t n) {
   return pl;
 }
 
+// The fp16x3 path's power-of-two exponents (computed by fp16x3_scales)
+struct X3Scales {
+  int32_t shift = -1;  // constant layer-1 entries: 2^-shift against a B value of 2^shift
+  int32_t w1 = 0;      // W1 enters the A operand times 2^w1
+  int32_t w2 = 0;      // W2 enters the A operand times 2^w2
+};
+
 }  // namespace
 
 struct lopt_handle {
   lopt_config cfg{};
   int device = 0;
   float* d_mlp = nullptr;
-  // fp16x3 path: the constant-entry shift, or -1 when the weights do not fit
-  int32_t x3_shift = -1;
+  // fp16x3 path: its scalings (shift -1 when the weights do not fit)
+  X3Scales x3;
   bool bound = false;
   Plan plan;
   char* ws = nullptr;
@@ -375,7 +382,9 @@ StepParams make_params(const lopt_handle* h) {
   p.per_tensor = h->th_active ? 1 : 0;
   p.n_time = c.n_time;
   p.n_feat = c.n_feat;
-  p.x3_shift = h->x3_shift > 0 ? h->x3_shift : 0;
+  p.x3_shift = h->x3.shift > 0 ? h->x3.shift : 0;
+  p.x3_w1 = h->x3.w1;
+  p.x3_w2 = h->x3.w2;
   for (int q = 0; q < kMaxTime; ++q) p.timescales[q] = q < c.n_time ? c.timescales[q] : 1.f;
   return p;
 }
@@ -470,18 +479,39 @@ void check_same_list(const lopt_handle* h, const lopt_tensor* ts, int32_t n, boo
   if (*grads_changed) validate_tensors(ts, n);
 }
 
-// The fp16x3 path's bound on its constant layer-1 entries, (b1' + row term) / 2
-// with b1' = b1 plus the step features (|tanh| <= 1) and the row term the
-// three normalised row features (each at most sqrt(n) < 46341 for n < 2^31)
-// times their weights: the smallest shift k with bound * 2^-k < 2^15, or -1
-// when k would exceed 14 or a weight has magnitude 2^15 or more (fp16 pieces).
-int32_t fp16x3_shift(const float* mlp, int32_t n_feat, int32_t n_time) {
+// The fp16x3 path's power-of-two scalings.  Each weight matrix W1, W2 enters
+// the A operand times 2^a, a in [0, 24], with a as large as puts its largest
+// magnitude in [4, 8) (never scaled down): the fp16 low pieces of its smaller
+// weights then stay out of fp16's subnormal range.  ReLU commutes with the
+// positive factor, so layer 2 starts from b2 2^(a1 + a2) and layer 3 reads
+// W3 2^-(a1 + a2) (exact in fp32).  The constant layer-1 entries,
+// (b1' + row term) / 2 with b1' = b1 plus the step features (|tanh| <= 1) and
+// the row term the three normalised row features (each at most
+// sqrt(n) < 46341 for n < 2^31) times their weights, carry 2^a1 too (a1 is
+// lowered while their bound would need k > 14); shift is the smallest k with
+// that bound * 2^(a1 - k) < 2^15, or -1 when k would exceed 14 or a weight
+// has magnitude 2^15 or more.
+X3Scales fp16x3_scales(const float* mlp, int32_t n_feat, int32_t n_time) {
+  X3Scales x;
   const int din = n_feat + n_time;
   const size_t nw = lopt_mlp_floats(n_feat, n_time);
   for (size_t i = 0; i < nw; ++i)
-    if (!(std::fabs(mlp[i]) < 32768.f)) return -1;
+    if (!(std::fabs(mlp[i]) < 32768.f)) return x;
   const float* W1 = mlp;
   const float* b1 = W1 + kH * din;
+  const float* W2 = b1 + kH;
+  // 3 - e for the largest magnitude m = f 2^e, f in [0.5, 1): m 2^(3 - e) in [4, 8)
+  auto to_four = [](float m) {
+    int e = 0;
+    (void)std::frexp(m, &e);
+    return m > 0.f ? std::min(std::max(3 - e, 0), 24) : 0;
+  };
+  float m1 = 0.f, m2 = 0.f;
+  for (int u = 0; u < kH; ++u)
+    for (int f = 0; f < n_feat; ++f) m1 = std::max(m1, std::fabs(W1[u * din + f]));
+  for (int i = 0; i < kH * kH; ++i) m2 = std::max(m2, std::fabs(W2[i]));
+  x.w1 = to_four(m1);
+  x.w2 = to_four(m2);
   double bound = 0.0;
   for (int u = 0; u < kH; ++u) {
     double c = std::fabs(double(b1[u]));
@@ -489,13 +519,16 @@ int32_t fp16x3_shift(const float* mlp, int32_t n_feat, int32_t n_time) {
     for (int k = 0; k < 3; ++k) c += 46341.0 * std::fabs(double(W1[u * din + 13 + k]));
     bound = std::max(bound, 0.5 * c * 1.001);
   }
+  while (x.w1 > 0 && std::ldexp(bound, x.w1) >= std::ldexp(32768.0, 14)) --x.w1;
+  bound = std::ldexp(bound, x.w1);
   int32_t k = 0;
   while (bound * std::ldexp(1.0, -k) >= 32768.0) ++k;
-  return k <= 14 ? k : -1;
+  x.shift = k <= 14 ? k : -1;
+  return x;
 }
 
 void check_fp16x3(const lopt_handle* h, const lopt_config* cfg) {
-  if (cfg->mlp_impl == LOPT_MLP_FP16X3 && h->x3_shift < 0)
+  if (cfg->mlp_impl == LOPT_MLP_FP16X3 && h->x3.shift < 0)
     fail(LOPT_ERR_UNSUPPORTED, "the MLP weights are too large for mlp_impl = LOPT_MLP_FP16X3");
 }
 
@@ -548,7 +581,7 @@ lopt_status lopt_create(const lopt_config* cfg, const float* mlp_host, lopt_hand
       if (!std::isfinite(mlp_host[i])) fail(LOPT_ERR_INVALID_ARGUMENT, "MLP weights must be finite");
     auto* h = new lopt_handle();
     h->cfg = *cfg;
-    h->x3_shift = fp16x3_shift(mlp_host, cfg->n_feat, cfg->n_time);
+    h->x3 = fp16x3_scales(mlp_host, cfg->n_feat, cfg->n_time);
     try {
       check_fp16x3(h, cfg);
       hip_check(hipGetDevice(&h->device), "hipGetDevice");

@@ -548,16 +548,20 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
 // is split as h = fp16(x) (nearest) and l = fp16(x - h), 22 significant bits;
 // a.b is taken as hh + hl + lh (the dropped ll is below 2^-22 |a b|).  fp16's
 // range is the constraint, so the features are normalised on the vector ALU
-// first (x = F s, with |x| <= sqrt(n) < 46341 for every element, and W1
-// unscaled in the A operand), and the two values without such a bound are
-// rescaled by powers of two:
-//   * the constant entries (b1 plus the row term) carry value * 2^-k against a
-//     B value of 2^k, k = x3_shift from a bound on the weights;
+// first (x = F s, with |x| <= sqrt(n) < 46341 for every element), and the
+// rest is rescaled by powers of two, all exact in fp32:
+//   * W1 and W2 enter the A operands times 2^a1 and 2^a2 (x3_w1, x3_w2), which
+//     put each matrix's largest weight in [4, 8) and keep the low pieces of the
+//     small weights out of fp16's subnormal range; as ReLU commutes with the
+//     factor, layer 2 starts from b2 2^(a1 + a2) and layer 3 reads
+//     W3 2^-(a1 + a2);
+//   * the constant entries (b1 plus the row term) carry value * 2^(a1 - k)
+//     against a B value of 2^k, k = x3_shift from a bound on the weights;
 //   * a wave whose layer-2 inputs (layer-1 outputs) reach 2^15 scales them by
-//     2^-j, starts layer 2 from b2 2^-j, and multiplies its layer-3 sums by 2^j
-//     (a ballot over the lanes; the scaling runs only in such a wave).
-// Elements far below 1 lose bits in fp16's subnormal range, so this path is
-// less accurate than k_apply_bf16x6 on them; it is selected explicitly.
+//     2^-j, starts layer 2 from b2 2^(a1 + a2 - j), and multiplies its layer-3
+//     sums by 2^j (a ballot over the lanes; the scaling runs only there).
+// A normalised feature or hidden value far below 1 keeps fp16's absolute
+// floor (2^-25 for its low piece), small beside the sum it enters.
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -589,12 +593,12 @@ __device__ __forceinline__ void apply_x3_body(const StepCtx& c, const StepParams
   const Streams s = make_streams(d, g, c.ws, ch);
   const float* __restrict__ pk = c.packed;
   const float* __restrict__ sc = c.scales + size_t(ch.tensor) * kStatStride;
-  const float cscale = __builtin_ldexpf(1.0f, -hp.x3_shift);  // exact powers of two
+  const float cscale = __builtin_ldexpf(1.0f, hp.x3_w1 - hp.x3_shift);  // exact powers of two
   const float bconst = __builtin_ldexpf(1.0f, hp.x3_shift);
 
   // A operands (two pieces), built once per chunk by the first wave: layer 1
-  // from W1 unscaled (the features carry the scales), its constant entries
-  // (1, 7) as for k_apply_bf16x6 but times 2^-k; layer 2 from W2.
+  // from W1 2^a1 (the features carry their scales), its constant entries
+  // (1, 7) as for k_apply_bf16x6 but times 2^(a1 - k); layer 2 from W2 2^a2.
   if (threadIdx.x < 64) {
     const float b1half = 0.5f * pk[kPkB1 + row] * cscale;
 #pragma unroll
@@ -604,8 +608,8 @@ __device__ __forceinline__ void apply_x3_body(const StepCtx& c, const StepParams
       for (int i = 0; i < 8; ++i) {
         const int q = 2 * (8 * k + i);
         const int f0 = x6_feature(q, NF, RU), f1 = x6_feature(q + 1, NF, RU);
-        const float w0 = f0 >= 0 ? pk[kPkW1 + row * kNF + f0] : 0.f;
-        const float w1 = f1 >= 0 ? pk[kPkW1 + row * kNF + f1] : 0.f;
+        const float w0 = f0 >= 0 ? __builtin_ldexpf(pk[kPkW1 + row * kNF + f0], hp.x3_w1) : 0.f;
+        const float w1 = f1 >= 0 ? __builtin_ldexpf(pk[kPkW1 + row * kNF + f1], hp.x3_w1) : 0.f;
         v[i] = (k == 1 && i == 7) ? (RU ? 0.f : b1half) : half ? w1 : w0;
       }
       Pieces2h pc[4];
@@ -619,8 +623,8 @@ __device__ __forceinline__ void apply_x3_body(const StepCtx& c, const StepParams
       Pieces2h pc[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        pc[j] = split2x2(pk[kPkW2 + row * kH + acc_row(8 * k + 2 * j, half)],
-                         pk[kPkW2 + row * kH + acc_row(8 * k + 2 * j + 1, half)]);
+        pc[j] = split2x2(__builtin_ldexpf(pk[kPkW2 + row * kH + acc_row(8 * k + 2 * j, half)], hp.x3_w2),
+                         __builtin_ldexpf(pk[kPkW2 + row * kH + acc_row(8 * k + 2 * j + 1, half)], hp.x3_w2));
 #pragma unroll
       for (int p = 0; p < 2; ++p) L.a2[k][p][lane] = u32x4{pc[0].p[p], pc[1].p[p], pc[2].p[p], pc[3].p[p]};
     }
@@ -636,7 +640,10 @@ __device__ __forceinline__ void apply_x3_body(const StepCtx& c, const StepParams
   if (threadIdx.x < 96) {
     const int which = threadIdx.x >> 5, h = (threadIdx.x >> 4) & 1, q = threadIdx.x & 15;
     const int hr = acc_row(q, h);
-    const float v = which == 0 ? pk[kPkB2 + hr] : which == 1 ? pk[kPkW3 + hr] : pk[kPkW3 + kH + hr];
+    // b2 2^(a1 + a2) and W3 2^-(a1 + a2): layer 2's output carries 2^(a1 + a2)
+    const int a12 = hp.x3_w1 + hp.x3_w2;
+    const float v = which == 0 ? __builtin_ldexpf(pk[kPkB2 + hr], a12)
+                    : __builtin_ldexpf(which == 1 ? pk[kPkW3 + hr] : pk[kPkW3 + kH + hr], -a12);
     reinterpret_cast<float*>(&L.tab[which][h][0])[q] = v;
   }
   __syncthreads();

@@ -113,10 +113,13 @@ struct StepParams {
   int32_t per_tensor;
   int32_t n_feat;            // kNF or kVeloNF
   int32_t n_time;
-  // fp16x3 path: the constant layer-1 entries carry (b1 + row term) / 2 times
-  // 2^-x3_shift against a B value of 2^x3_shift, which keeps them inside
-  // fp16's range for every input (the shift is bounded from the weights)
+  // fp16x3 path: W1 and W2 enter the A operands times 2^x3_w1 and 2^x3_w2;
+  // the constant layer-1 entries carry (b1 + row term) / 2 times
+  // 2^(x3_w1 - x3_shift) against a B value of 2^x3_shift, which keeps them
+  // inside fp16's range for every input (the shift is bounded from the weights)
   int32_t x3_shift;
+  int32_t x3_w1;
+  int32_t x3_w2;
   float timescales[kMaxTime];
 };
 
