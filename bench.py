@@ -118,7 +118,8 @@ def main():
                     help="per-element features: 28 (small_fc_lopt) or 19 (the VeLO-shaped variant)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp32-compare", action="store_true",
-                    help="with the bf16x6 MLP path, skip timing the fp32 matrix and fp16x3 paths on the same inputs")
+                    help="with a split MLP path (fp16x3, bf16x6), skip timing the fp32 matrix path and the other "
+                         "split path on the same inputs")
     ap.add_argument("--peaks", action="store_true",
                     help="also run the machine-figure microbenchmark and include it as measured_peaks")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -152,6 +153,7 @@ def main():
             v = opt.state_views(i)
             for k in ("m", "v", "r", "c"):
                 v[k].copy_(torch.from_numpy(st[k]))
+    impl = L.lopt_get_mlp_impl(opt.handle)   # "auto" resolved for these weights
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -200,15 +202,17 @@ def main():
         return {"ms_per_step": round(ms2, 4), "value": round(w.n_params / (ms2 * 1e-3) / 1e9, 4),
                 "apply_ms": round(ap2, 4), "steps": k2}
 
-    fp32_cmp = fp16_cmp = None
-    if impl in (L.LOPT_MLP_AUTO, L.LOPT_MLP_BF16X6) and not args.no_fp32_compare:
-        # the apply kernel switched to the fp32 matrix path, then to the opt-in fp16x3 path
-        log("[bench] fp32 matrix path and fp16x3 path on the same inputs")
+    fp32_cmp = other_cmp = None
+    other = {L.LOPT_MLP_FP16X3: L.LOPT_MLP_BF16X6, L.LOPT_MLP_BF16X6: L.LOPT_MLP_FP16X3}.get(impl)
+    other_name = {L.LOPT_MLP_FP16X3: "fp16x3_path", L.LOPT_MLP_BF16X6: "bf16x6_path"}.get(other)
+    if other is not None and not args.no_fp32_compare:
+        # the apply kernel switched to the fp32 matrix path, then to the other split path
+        log(f"[bench] fp32 matrix path and {other_name} on the same inputs")
         fp32_cmp = time_path(L.LOPT_MLP_MFMA)
         try:
-            fp16_cmp = time_path(L.LOPT_MLP_FP16X3)
+            other_cmp = time_path(other)
         except L.LoptError as err:  # weights outside the fp16x3 path's range
-            fp16_cmp = {"error": str(err)}
+            other_cmp = {"error": str(err)}
     opt.close()
     if args.calibrate_copy:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
@@ -230,11 +234,12 @@ def main():
     fpe = flop_per_elem(args.n_feat)
     fp32_equiv = fpe * n / (apply_ms * 1e-3) / 1e12  # the MLP's fp32 FLOP per second
     use_mfma = impl != L.LOPT_MLP_VALU
-    x6 = impl in (L.LOPT_MLP_AUTO, L.LOPT_MLP_BF16X6)
+    x6 = impl == L.LOPT_MLP_BF16X6
     x3 = impl == L.LOPT_MLP_FP16X3
     # The roofline of the apply kernel is that of the unit its contraction runs
-    # on: fp32 matrix cores, the vector ALU, or (bf16x6) the bf16 matrix cores,
-    # which execute six bf16 piece products per fp32 product.
+    # on: fp32 matrix cores, the vector ALU, or the fp16 (fp16x3) or bf16
+    # (bf16x6) matrix cores, which execute three fp16 or six bf16 piece
+    # products per fp32 product.
     if x6:
         achieved, peak, apply_kernel = X6_PRODUCTS * fp32_equiv, PEAK_BF16_MFMA_TFLOPS, "k_apply_bf16x6"
     elif x3:
@@ -271,7 +276,7 @@ def main():
         "step_frac_fp32_peak": round(fpe * n / (ms * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4),
         "kernels_ms": {name: round(float(t), 4) for name, t in zip(L.KERNEL_NAMES, kern_ms)},
         "fp32_matrix_path": fp32_cmp,
-        "fp16x3_path": fp16_cmp,
+        **({other_name: other_cmp} if other_name else {}),
         "step_ms_median": round(float(np.median(per_step)), 4),
         "step_ms_min": round(float(per_step.min()), 4),
         "step_frac_hbm": round(step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),

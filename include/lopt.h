@@ -57,7 +57,9 @@ typedef enum lopt_status {
 
 /* Implementation of the per-element MLP in the apply kernel. */
 typedef enum lopt_mlp_impl {
-  LOPT_MLP_AUTO = 0, /* currently LOPT_MLP_BF16X6 (the fastest on gfx950) */
+  LOPT_MLP_AUTO = 0, /* LOPT_MLP_FP16X3 (the fastest on gfx950) when the
+                        weights are inside its range, else LOPT_MLP_BF16X6;
+                        lopt_get_mlp_impl tells which */
   LOPT_MLP_VALU = 1, /* vector FMA, weights broadcast from scalar registers */
   LOPT_MLP_MFMA = 2, /* fp32 matrix-core path (v_mfma_f32_32x32x1_2b_f32 and
                         v_mfma_f32_32x32x2_f32) */
@@ -68,13 +70,15 @@ typedef enum lopt_mlp_impl {
                           below 2^-21 of each product (median below one fp32
                           rounding) */
   LOPT_MLP_FP16X3 = 4  /* fp16 matrix-core path (v_mfma_f32_32x32x16_f16): the
-                          features normalised first, every operand split into
-                          two fp16 pieces (22 significant bits) and the three
-                          largest piece products accumulated in fp32; a wave
-                          whose layer-2 inputs leave fp16's range is rescaled
-                          by a power of two.  Faster than LOPT_MLP_BF16X6,
-                          slightly less accurate for values far below 1.
-                          lopt_create / lopt_set_config refuse it
+                          features normalised first, W1 and W2 scaled by powers
+                          of two that put their largest weights in [4, 8),
+                          every operand split into two fp16 pieces (22
+                          significant bits) and the three largest piece
+                          products accumulated in fp32; a wave whose layer-2
+                          inputs leave fp16's range is rescaled by a power of
+                          two.  Faster than LOPT_MLP_BF16X6 and as accurate;
+                          a normalised input far below 1 keeps an absolute
+                          floor of 2^-25.  lopt_create / lopt_set_config refuse it
                           (LOPT_ERR_UNSUPPORTED) for weights of magnitude
                           2^15 or more, or whose first-layer row-feature
                           weights are too large for its constant term. */
@@ -213,6 +217,12 @@ lopt_status lopt_set_step(lopt_handle* h, int64_t t);
  * Errors: invalid config, or n_feat or n_time different from lopt_create's
  * -> INVALID_ARGUMENT (the handle keeps its previous config). */
 lopt_status lopt_set_config(lopt_handle* h, const lopt_config* cfg);
+
+/* The MLP path that the handle's steps run: the config's mlp_impl, with
+ * LOPT_MLP_AUTO resolved for the handle's weights (LOPT_MLP_FP16X3 or
+ * LOPT_MLP_BF16X6).  Host-side only.  Errors: NULL argument ->
+ * INVALID_ARGUMENT. */
+lopt_status lopt_get_mlp_impl(const lopt_handle* h, int32_t* impl);
 
 /* Per-tensor learning rate and weight decay, as torch's parameter groups give
  * them (the PyLO page, "Library design": the optimizer is a torch optimizer;

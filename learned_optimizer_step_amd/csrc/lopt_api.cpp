@@ -329,6 +329,12 @@ struct lopt_handle {
 
 namespace {
 
+// AUTO: the fp16x3 path when the weights are inside its range, else bf16x6
+int32_t resolved_mlp_impl(const lopt_handle* h) {
+  if (h->cfg.mlp_impl != LOPT_MLP_AUTO) return h->cfg.mlp_impl;
+  return h->x3.shift >= 0 ? LOPT_MLP_FP16X3 : LOPT_MLP_BF16X6;
+}
+
 StepCtx make_ctx(const lopt_handle* h) {
   const Plan& pl = h->plan;
   StepCtx c{};
@@ -349,7 +355,7 @@ StepCtx make_ctx(const lopt_handle* h) {
   c.n_tiles0 = int32_t(pl.tiles0.size());
   c.n_segs1 = int32_t(pl.segs1.size());
   c.n_chunks = int32_t(pl.chunks.size());
-  c.mlp_impl = h->cfg.mlp_impl == LOPT_MLP_AUTO ? LOPT_MLP_BF16X6 : h->cfg.mlp_impl;
+  c.mlp_impl = resolved_mlp_impl(h);
   return c;
 }
 
@@ -703,6 +709,13 @@ lopt_status lopt_set_config(lopt_handle* h, const lopt_config* cfg) {
     check_fp16x3(h, cfg);
     h->cfg = *cfg;
     if (h->th_active) h->th_dirty = true;  // lr_step depends on step_mult
+  });
+}
+
+lopt_status lopt_get_mlp_impl(const lopt_handle* h, int32_t* impl) {
+  return guarded([&] {
+    if (!h || !impl) fail(LOPT_ERR_INVALID_ARGUMENT, "NULL argument");
+    *impl = resolved_mlp_impl(h);
   });
 }
 

@@ -90,6 +90,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "lopt_set_step": (st, [ctypes.c_void_p, ctypes.c_int64]),
         "lopt_set_timing_events": (st, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32]),
         "lopt_set_config": (st, [ctypes.c_void_p, ctypes.POINTER(lopt_config)]),
+        "lopt_get_mlp_impl": (st, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)]),
         "lopt_set_tensor_hyper": (st, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32]),
         "lopt_last_error": (ctypes.c_char_p, []),
     }
@@ -173,6 +174,13 @@ def lopt_set_step(h, t: int) -> None:
 
 def lopt_set_config(h, cfg: lopt_config) -> None:
     _check(load_library().lopt_set_config(h, ctypes.byref(cfg)))
+
+
+def lopt_get_mlp_impl(h) -> int:
+    """The MLP path the handle's steps run (LOPT_MLP_AUTO resolved)."""
+    impl = ctypes.c_int32()
+    _check(load_library().lopt_get_mlp_impl(h, ctypes.byref(impl)))
+    return int(impl.value)
 
 
 def lopt_set_tensor_hyper(h, lr: Optional[Sequence[float]], weight_decay: Optional[Sequence[float]],

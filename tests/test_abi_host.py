@@ -171,6 +171,8 @@ def test_null_handle_calls(lib):
     assert lib.lopt_step(None, None, 0, None) == L.LOPT_ERR_INVALID_ARGUMENT
     assert lib.lopt_init_state(None, None, 0, None, 0, None) == L.LOPT_ERR_INVALID_ARGUMENT
     assert lib.lopt_set_tensor_hyper(None, None, None, 0) == L.LOPT_ERR_INVALID_ARGUMENT
+    impl = ctypes.c_int32()
+    assert lib.lopt_get_mlp_impl(None, ctypes.byref(impl)) == L.LOPT_ERR_INVALID_ARGUMENT
     lib.lopt_destroy(None)  # no-op
 
 

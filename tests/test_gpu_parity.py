@@ -126,6 +126,27 @@ def test_update_accuracy_of_each_mlp_path():
         assert vs_mfma[impl][0] <= 2.0 * vs_mfma[L.LOPT_MLP_VALU][0], vs_mfma
 
 
+def test_auto_picks_fp16x3_inside_its_range_and_bf16x6_outside():
+    """LOPT_MLP_AUTO runs the fp16x3 path for weights inside its range (its
+    result then identical to an explicit LOPT_MLP_FP16X3) and the bf16x6 path
+    for weights the fp16x3 path refuses (W1 entry of 40000)."""
+    w = W.custom_workload("auto", [(64, 128), (300,)], param_std=0.02, grad_std=1e-2, steps=2, wid=180)
+    weights = W.mlp_weights(11, bias_std=0.1)
+    big = weights.copy()
+    big[5] = 40000.0
+    for mlp, want in ((weights, L.LOPT_MLP_FP16X3), (big, L.LOPT_MLP_BF16X6)):
+        out = {}
+        for impl in (L.LOPT_MLP_AUTO, want):
+            run = GpuRun(w, mlp, L.config_from(mlp_impl=impl), torch)
+            assert L.lopt_get_mlp_impl(run.opt.handle) == want
+            for t in (1, 2):
+                run.step(t)
+            out[impl] = [run.fetch(i)["p"] for i in range(len(w.tensors))]
+            run.close()
+        for a, b in zip(out[L.LOPT_MLP_AUTO], out[want]):
+            assert np.array_equal(np.asarray(a), np.asarray(b))
+
+
 @pytest.mark.parametrize("impl", IMPLS)
 @pytest.mark.parametrize("scale", ["large", "small"])
 def test_magnitudes_far_from_one(impl, scale):
