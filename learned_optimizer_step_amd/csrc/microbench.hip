@@ -9,7 +9,7 @@
 //      instructions and the vector ALU share the SIMD's issue, so vector work
 //      adds to the matrix time instead of hiding under it;
 //   4. the same two figures for the bf16 matrix instruction
-//      v_mfma_f32_32x32x16_bf16 (the default apply path), beside which
+//      v_mfma_f32_32x32x16_bf16 (the bf16x6 apply path), beside which
 //      vector instructions of the other waves do issue.
 // Prints one JSON object.  Every kernel writes only out[block * 64 + lane],
 // and out is sized for the largest grid launched.
