@@ -85,7 +85,8 @@ def test_update_accuracy_of_each_mlp_path():
       * against the fp64 oracle, every path shows about the same error, which
         comes from the fp32 inputs of the MLP rather than from its evaluation;
         the bf16x6 and fp16x3 paths stay within 1.5x of the fp32 paths (rms)
-        and 4x (max);
+        and 4x (max), and the default fp16x3 path (scaled weights) is no less
+        accurate than the fp32 paths (rms);
       * against the fp32 matrix path on identical inputs (evaluation only),
         the bf16x6 and fp16x3 paths differ at most twice as much as the
         vector-ALU path does, which computes the same fp32 products in another
@@ -124,6 +125,7 @@ def test_update_accuracy_of_each_mlp_path():
     for impl in split_impls:
         assert vs_oracle[impl][0] <= 1.5 * rms32 and vs_oracle[impl][1] <= 4.0 * max32, vs_oracle
         assert vs_mfma[impl][0] <= 2.0 * vs_mfma[L.LOPT_MLP_VALU][0], vs_mfma
+    assert vs_oracle[L.LOPT_MLP_FP16X3][0] <= min(vs_oracle[L.LOPT_MLP_MFMA][0], vs_oracle[L.LOPT_MLP_VALU][0]), vs_oracle
 
 
 def test_auto_picks_fp16x3_inside_its_range_and_bf16x6_outside():
