@@ -57,9 +57,11 @@ typedef enum lopt_status {
 
 /* Implementation of the per-element MLP in the apply kernel. */
 typedef enum lopt_mlp_impl {
-  LOPT_MLP_AUTO = 0, /* LOPT_MLP_FP16X3 (the fastest on gfx950) when the
-                        weights are inside its range, else LOPT_MLP_BF16X6;
-                        lopt_get_mlp_impl tells which */
+  LOPT_MLP_AUTO = 0, /* LOPT_MLP_BF16X8: the fastest of the paths with
+                        fp32 arithmetic (each product within one fp32
+                        rounding, accumulation in fp32: LOPT_MLP_BF16X8,
+                        LOPT_MLP_BF16X9, LOPT_MLP_MFMA, LOPT_MLP_VALU);
+                        lopt_get_mlp_impl tells which path runs */
   LOPT_MLP_VALU = 1, /* vector FMA, weights broadcast from scalar registers */
   LOPT_MLP_MFMA = 2, /* fp32 matrix-core path (v_mfma_f32_32x32x1_2b_f32 and
                         v_mfma_f32_32x32x2_f32) */
@@ -69,7 +71,7 @@ typedef enum lopt_mlp_impl {
                           (v_mfma_f32_32x32x16_bf16); the dropped products are
                           below 2^-21 of each product (median below one fp32
                           rounding) */
-  LOPT_MLP_FP16X3 = 4  /* fp16 matrix-core path (v_mfma_f32_32x32x16_f16): the
+  LOPT_MLP_FP16X3 = 4, /* fp16 matrix-core path (v_mfma_f32_32x32x16_f16): the
                           features normalised first, W1 and W2 scaled by powers
                           of two that put their largest weights in [4, 8),
                           every operand split into two fp16 pieces (22
@@ -81,7 +83,17 @@ typedef enum lopt_mlp_impl {
                           floor of 2^-25.  lopt_create / lopt_set_config refuse it
                           (LOPT_ERR_UNSUPPORTED) for weights of magnitude
                           2^15 or more, or whose first-layer row-feature
-                          weights are too large for its constant term. */
+                          weights are too large for its constant term.
+                          Narrower than fp32 (22-bit operands). */
+  LOPT_MLP_BF16X9 = 5, /* bf16 matrix-core path with every fp32 operand split
+                          exactly into three bf16 pieces and all nine piece
+                          products (each exact in fp32) accumulated in fp32
+                          (v_mfma_f32_32x32x16_bf16): the products of an fp32
+                          GEMM, exactly, with fp32 accumulation */
+  LOPT_MLP_BF16X8 = 6  /* as LOPT_MLP_BF16X9 without the product of the two
+                          low pieces, which is below 2^-30 of the product:
+                          every product within 1/64 of one fp32 rounding,
+                          accumulated in fp32 */
 } lopt_mlp_impl;
 
 /* Hyperparameters.  lopt_default_config() fills the defaults shown. */
@@ -219,8 +231,7 @@ lopt_status lopt_set_step(lopt_handle* h, int64_t t);
 lopt_status lopt_set_config(lopt_handle* h, const lopt_config* cfg);
 
 /* The MLP path that the handle's steps run: the config's mlp_impl, with
- * LOPT_MLP_AUTO resolved for the handle's weights (LOPT_MLP_FP16X3 or
- * LOPT_MLP_BF16X6).  Host-side only.  Errors: NULL argument ->
+ * LOPT_MLP_AUTO resolved (LOPT_MLP_BF16X8).  Host-side only.  Errors: NULL argument ->
  * INVALID_ARGUMENT. */
 lopt_status lopt_get_mlp_impl(const lopt_handle* h, int32_t* impl);
 

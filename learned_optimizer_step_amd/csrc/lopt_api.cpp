@@ -100,7 +100,7 @@ void validate_config(const lopt_config* c) {
   for (int q = 0; q < c->n_time; ++q)
     if (!(c->timescales[q] > 0.f) || !finite(c->timescales[q]))
       fail(LOPT_ERR_INVALID_ARGUMENT, "timescales must be finite and > 0");
-  if (c->mlp_impl < LOPT_MLP_AUTO || c->mlp_impl > LOPT_MLP_FP16X3)
+  if (c->mlp_impl < LOPT_MLP_AUTO || c->mlp_impl > LOPT_MLP_BF16X8)
     fail(LOPT_ERR_INVALID_ARGUMENT, "unknown mlp_impl");
   if (c->n_feat != LOPT_N_FEATURES && c->n_feat != LOPT_VELO_FEATURES)
     fail(LOPT_ERR_INVALID_ARGUMENT, "n_feat must be 28 or 19");
@@ -329,10 +329,11 @@ struct lopt_handle {
 
 namespace {
 
-// AUTO: the fp16x3 path when the weights are inside its range, else bf16x6
+// AUTO: bf16x8, measured the fastest of the paths with fp32 arithmetic
+// (bf16x8, bf16x9, the fp32 matrix cores, the vector ALU) for any weights
 int32_t resolved_mlp_impl(const lopt_handle* h) {
   if (h->cfg.mlp_impl != LOPT_MLP_AUTO) return h->cfg.mlp_impl;
-  return h->x3.shift >= 0 ? LOPT_MLP_FP16X3 : LOPT_MLP_BF16X6;
+  return LOPT_MLP_BF16X8;
 }
 
 StepCtx make_ctx(const lopt_handle* h) {

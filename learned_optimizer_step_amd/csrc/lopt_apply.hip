@@ -266,19 +266,26 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
 }
 
 // ---------------------------------------------------------------------------
-// k_apply_bf16x6: layers 1 and 2 on the bf16 matrix cores.  Every fp32
-// operand x is split into three bf16 pieces, x = h + m + l exactly: h is x
-// with its low 16 bits cleared, m the same of r = x - h (exact), and
-// l = r - m, which has at most 8 significant bits (truncation split of the
-// 24-bit significand into 8-bit parts; |m| < 2^-7 |x|, |l| < 2^-15 |x|).  A
-// product a.b is then the sum of the six piece products whose orders add up
-// to at most 2 (hh, hm, mh, hl, lh, mm), each exact in the fp32
-// accumulation; the three dropped ones (ml, lm, ll) stay below 2^-21 |a b|,
-// with a median below one fp32 rounding.  (Rounding the pieces to nearest
-// with v_cvt_pk_bf16_f32 bounds them by 2^-23 at the same instruction count
-// but measured 4.6 % slower.)  This is the piece-wise emulation of an fp32
-// GEMM on reduced-precision matrix units known as bf16x6 (bf16x9 keeps all
-// nine).
+// k_apply_bf16x9 / k_apply_bf16x6: layers 1 and 2 on the bf16 matrix cores.
+// Every fp32 operand x is split into three bf16 pieces, x = h + m + l
+// exactly: h is x with its low 16 bits cleared, m the same of r = x - h
+// (exact), and l = r - m, which has at most 8 significant bits (truncation
+// split of the 24-bit significand into 8-bit parts; |m| < 2^-7 |x|,
+// |l| < 2^-15 |x|).  Every piece product (8 x 8 significant bits) is exact
+// in the fp32 accumulator, so
+//   bf16x9: the nine piece products sum to a.b exactly; the dot product is
+//     that of an fp32 GEMM with exact products and fp32 accumulation (the
+//     piece-wise emulation of an fp32 GEMM on reduced-precision matrix units
+//     known as bf16x9: Henry, Tang & Heinecke, 2019);
+//   bf16x8: all but ll, which is below 2^-30 |a b|: each product within
+//     1/64 of one fp32 rounding (2^-24 |a b|), accumulated in fp32;
+//   bf16x6: the six products whose orders add up to at most 2 (hh, hm, mh,
+//     hl, lh, mm); the three dropped ones (ml, lm, ll) stay below
+//     2^-21 |a b|, with a median below one fp32 rounding (narrower than
+//     fp32).
+// (Rounding the pieces to nearest with v_cvt_pk_bf16_f32 bounds bf16x6's
+// dropped products by 2^-23 at the same instruction count but measured 4.6 %
+// slower.)  Products are issued smallest first.
 // On gfx950 a v_mfma_f32_32x32x16_bf16 does 16x the FLOP of the fp32 form in
 // half its cycles, and vector instructions of the other waves issue beside
 // it (the fp32 form shares their issue cycles), so the six products cost
@@ -317,6 +324,21 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 }
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Eight values x[0..7] (the four bf16 pairs of one B operand) to their three
+// pieces, as bf16 pairs.  (Taking the remainders x - h and r - m with
+// v_dot2c_f32_bf16 against the pair (-1, 0) gives the same pieces bit for bit
+// in 7 instead of 11 instructions per pair, but measured 21 % more cycles per
+// element: that instruction does not issue beside the bf16 matrix
+// instructions as the masks and subtractions do.)
+__device__ __forceinline__ void split3_x8(const float (&x)[8], u32x4 (&bt)[3]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const Pieces u0 = split3(x[2 * j]), u1 = split3(x[2 * j + 1]);
+#pragma unroll
+    for (int p = 0; p < 3; ++p) bt[p][j] = pack2(piece(u0, p), piece(u1, p));
+  }
+}
+
 // Layer-1 entries: feature of entry q (q < 30), -1 = zero.
 __device__ constexpr int x6_feature(int q, int nf, bool ru) {
   for (int f = 0; f < nf; ++f) {
@@ -331,10 +353,20 @@ static_assert(x6_feature(24, kNF, true) == 27 && x6_feature(25, kNF, true) == -1
                   x6_feature(13, kNF, true) == 16 && x6_feature(16, kVeloNF, true) == -1,
               "bf16x6 layer-1 entries");
 
-// (A piece, B piece) of product t of the six, smallest terms first:
-// hl, lh, mm, hm, mh, hh.
-__device__ constexpr int x6_a(int t) { return t == 1 ? 2 : (t == 2 || t == 4) ? 1 : 0; }
-__device__ constexpr int x6_b(int t) { return t == 0 ? 2 : (t == 2 || t == 3) ? 1 : 0; }
+// (A piece, B piece) of product t of NP (9, 8 or 6), smallest terms first:
+// bf16x9: ll, then bf16x8's lm, ml, then bf16x6's hl, lh, mm, hm, mh, hh.
+__device__ constexpr int xp_a(int np, int t) {
+  constexpr int a9[9] = {2, 2, 1, 0, 2, 1, 0, 1, 0};
+  return a9[t + 9 - np];
+}
+__device__ constexpr int xp_b(int np, int t) {
+  constexpr int b9[9] = {2, 1, 2, 2, 0, 1, 1, 0, 0};
+  return b9[t + 9 - np];
+}
+static_assert(xp_a(6, 0) == 0 && xp_b(6, 0) == 2 && xp_a(6, 1) == 2 && xp_b(6, 1) == 0 && xp_a(6, 2) == 1 &&
+                  xp_b(6, 2) == 1 && xp_a(6, 5) == 0 && xp_b(6, 5) == 0 && xp_a(9, 0) == 2 && xp_b(9, 0) == 2 &&
+                  xp_a(8, 0) == 2 && xp_b(8, 0) == 1 && xp_a(8, 1) == 1 && xp_b(8, 1) == 2 && xp_a(8, 7) == 0,
+              "piece-product order");
 
 // LDS of the kernel (one copy for every variant the body is instantiated for).
 struct X6Lds {
@@ -343,7 +375,7 @@ struct X6Lds {
   float4 tab[3][2][4];  // {b2, W3 dir, W3 mag} x half x 16 floats
 };
 
-template <bool VEC, bool NORMAL, int NF, bool RU>
+template <int NP, bool VEC, bool NORMAL, int NF, bool RU>
 __device__ __forceinline__ void apply_x6_body(const StepCtx& c, const StepParams& hp, const Chunk& ch,
                                               const TensorDesc& d, const float* g, X6Lds& L) {
   const int lane = threadIdx.x & 63;
@@ -468,15 +500,11 @@ __device__ __forceinline__ void apply_x6_body(const StepCtx& c, const StepParams
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         u32x4 bt[3];
+        split3_x8(v[b][k], bt);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const Pieces u0 = split3(v[b][k][2 * j]), u1 = split3(v[b][k][2 * j + 1]);
-#pragma unroll
-          for (int p = 0; p < 3; ++p) bt[p][j] = pack2(piece(u0, p), piece(u1, p));
-        }
-#pragma unroll
-        for (int t = 0; t < 6; ++t)
-          acc1s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[x6_a(t)]), as_bf16x8(bt[x6_b(t)]), acc1s[b], 0, 0, 0);
+        for (int t = 0; t < NP; ++t)
+          acc1s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[xp_a(NP, t)]), as_bf16x8(bt[xp_b(NP, t)]),
+                                                             acc1s[b], 0, 0, 0);
       }
     }
     float dpart[2], mpart[2];
@@ -494,16 +522,14 @@ __device__ __forceinline__ void apply_x6_body(const StepCtx& c, const StepParams
         u32x4 a[3], bt[3];
 #pragma unroll
         for (int p = 0; p < 3; ++p) a[p] = L.a2[k][p][li];
+        float hx[8];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const Pieces u0 = split3(fmaxf(acc1[8 * k + 2 * j], 0.f));
-          const Pieces u1 = split3(fmaxf(acc1[8 * k + 2 * j + 1], 0.f));
+        for (int i = 0; i < 8; ++i) hx[i] = fmaxf(acc1[8 * k + i], 0.f);
+        split3_x8(hx, bt);
 #pragma unroll
-          for (int p = 0; p < 3; ++p) bt[p][j] = pack2(piece(u0, p), piece(u1, p));
-        }
-#pragma unroll
-        for (int t = 0; t < 6; ++t)
-          acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[x6_a(t)]), as_bf16x8(bt[x6_b(t)]), acc2, 0, 0, 0);
+        for (int t = 0; t < NP; ++t)
+          acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[xp_a(NP, t)]), as_bf16x8(bt[xp_b(NP, t)]), acc2, 0,
+                                                         0, 0);
       }
       float dsum = half ? 0.f : b3d, msum = half ? 0.f : b3m;
 #pragma unroll
@@ -529,7 +555,8 @@ __device__ __forceinline__ void apply_x6_body(const StepCtx& c, const StepParams
   }
 }
 
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void k_apply_bf16x6(StepCtx c, StepParams hp) {
+template <int NP>
+__device__ __forceinline__ void apply_bf16(const StepCtx& c, const StepParams& hp) {
   Chunk ch;
   TensorDesc d;
   const float* g;
@@ -538,8 +565,20 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   __shared__ X6Lds lds;
   dispatch_variant<true>(d, hp, [&](auto v) {
     using V = decltype(v);
-    apply_x6_body<V::vec, V::normal, V::nf, V::rowuni>(c, hp, ch, d, g, lds);
+    apply_x6_body<NP, V::vec, V::normal, V::nf, V::rowuni>(c, hp, ch, d, g, lds);
   });
+}
+
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void k_apply_bf16x9(StepCtx c, StepParams hp) {
+  apply_bf16<9>(c, hp);
+}
+
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void k_apply_bf16x8(StepCtx c, StepParams hp) {
+  apply_bf16<8>(c, hp);
+}
+
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void k_apply_bf16x6(StepCtx c, StepParams hp) {
+  apply_bf16<6>(c, hp);
 }
 
 // ---------------------------------------------------------------------------
@@ -827,6 +866,10 @@ hipError_t launch_apply(const StepCtx& c, const StepParams& p, hipStream_t s) {
     hipLaunchKernelGGL(k_apply_bf16x6, dim3(c.n_chunks), dim3(kBlock), 0, s, c, p);
   else if (c.mlp_impl == 4)
     hipLaunchKernelGGL(k_apply_fp16x3, dim3(c.n_chunks), dim3(kBlock), 0, s, c, p);
+  else if (c.mlp_impl == 5)
+    hipLaunchKernelGGL(k_apply_bf16x9, dim3(c.n_chunks), dim3(kBlock), 0, s, c, p);
+  else if (c.mlp_impl == 6)
+    hipLaunchKernelGGL(k_apply_bf16x8, dim3(c.n_chunks), dim3(kBlock), 0, s, c, p);
   else
     hipLaunchKernelGGL(k_apply_mfma, dim3(c.n_chunks), dim3(kBlock), 0, s, c, p);
   return hipGetLastError();

@@ -139,7 +139,7 @@ struct StepCtx {
   const float* tensor_hyper;         // [n_tensors][2]: decay, lr_step (StepParams::per_tensor)
   const float* mlp;                  // raw weights (handle-owned)
   int32_t n_tensors, n_tiles0, n_segs1, n_chunks;
-  int32_t mlp_impl;                  // 1 = VALU, 2 = MFMA
+  int32_t mlp_impl;                  // lopt_mlp_impl, AUTO resolved: 1 VALU, 2 MFMA, 3 BF16X6, 4 FP16X3, 5 BF16X9, 6 BF16X8
 };
 
 hipError_t launch_zero_state(const StepCtx& c, hipStream_t s);

@@ -32,6 +32,8 @@ LOPT_MLP_VALU = 1
 LOPT_MLP_MFMA = 2
 LOPT_MLP_BF16X6 = 3
 LOPT_MLP_FP16X3 = 4
+LOPT_MLP_BF16X9 = 5
+LOPT_MLP_BF16X8 = 6
 LOPT_MAX_TIME = 11
 LOPT_N_FEATURES = 28     # small_fc_lopt's per-element features
 LOPT_VELO_FEATURES = 19  # the VeLO-shaped variant's (features 0..18)

@@ -142,6 +142,9 @@ def test_create_rejects_bad_config_without_device(lib):
     c = L.config_from(n_feat=20)
     assert lib.lopt_create(ctypes.byref(c), w, ctypes.byref(h)) == L.LOPT_ERR_INVALID_ARGUMENT
     assert "n_feat" in L.lopt_last_error()
+    c = L.config_from(mlp_impl=L.LOPT_MLP_BF16X8 + 1)
+    assert lib.lopt_create(ctypes.byref(c), w, ctypes.byref(h)) == L.LOPT_ERR_INVALID_ARGUMENT
+    assert "mlp_impl" in L.lopt_last_error()
     c = L.lopt_default_config()
     assert lib.lopt_create(ctypes.byref(c), None, ctypes.byref(h)) == L.LOPT_ERR_INVALID_ARGUMENT
     assert lib.lopt_create(None, w, ctypes.byref(h)) == L.LOPT_ERR_INVALID_ARGUMENT
