@@ -250,6 +250,25 @@ lopt_status lopt_get_mlp_impl(const lopt_handle* h, int32_t* impl);
  * non-finite value -> INVALID_ARGUMENT (nothing changes). */
 lopt_status lopt_set_tensor_hyper(lopt_handle* h, const float* lr, const float* weight_decay, int32_t n);
 
+/* Floats per tensor in lopt_get_tensor_stats' output. */
+#define LOPT_STAT_FLOATS 32
+
+/* The per-tensor statistics of the step: what the PyLO page's kernel 1
+ * collects ("CUDA kernel design: two-pass fusion" > "Fused kernel strategy":
+ * one statistic of the squares of each feature over the whole tensor), as the
+ * normalisers the apply pass used.  For tensor i of the bound list (n: its
+ * length) and d < n_feat:
+ *   out[i * LOPT_STAT_FLOATS + d] = s_d = (mean over the tensor of F_d^2 + eps_norm)^(-1/2),
+ * 0 for n_feat <= d < 28, then
+ *   out[i * LOPT_STAT_FLOATS + 28 + k] = sqrt(mean_i r_k) (k = 0, 1, 2; r_k
+ *   after the step's update), and entry 31 = 0.
+ * The values are those of the last step that gave tensor i a gradient
+ * (unspecified before it has had one).  out: host memory, n *
+ * LOPT_STAT_FLOATS floats.  Waits for the device (hipDeviceSynchronize).
+ * Errors: NULL handle or out -> INVALID_ARGUMENT; no bound list or n
+ * different from its length -> STATE; copy failure -> HIP. */
+lopt_status lopt_get_tensor_stats(const lopt_handle* h, float* out, int32_t n);
+
 /* Kernels of one step, in launch order. */
 #define LOPT_N_KERNELS 5 /* row/col sums, moving averages, statistics, finalize, apply */
 

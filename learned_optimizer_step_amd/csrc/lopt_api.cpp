@@ -742,6 +742,32 @@ lopt_status lopt_set_tensor_hyper(lopt_handle* h, const float* lr, const float* 
   });
 }
 
+lopt_status lopt_get_tensor_stats(const lopt_handle* h, float* out, int32_t n) {
+  return guarded([&] {
+    if (!h || !out) fail(LOPT_ERR_INVALID_ARGUMENT, "NULL handle or output");
+    if (!h->bound) fail(LOPT_ERR_STATE, "lopt_init_state has not been called");
+    if (n != int32_t(h->plan.bound.size())) fail(LOPT_ERR_STATE, "n differs from the bound tensor count");
+    if (n == 0) return;
+    // the workspace records: s_d, except s_d sqrt(mean r_k) for the features
+    // that carry rho_k (the apply pass folds that factor in), sqrt(mean r_k)
+    // at 28..30
+    std::vector<float> rec(size_t(n) * kStatStride);
+    hip_check(hipDeviceSynchronize(), "hipDeviceSynchronize");
+    hip_check(hipMemcpy(rec.data(), h->ws + h->plan.off_scales, rec.size() * sizeof(float), hipMemcpyDeviceToHost),
+              "hipMemcpy(tensor statistics)");
+    for (int32_t i = 0; i < n; ++i) {
+      const float* r = rec.data() + size_t(i) * kStatStride;
+      float* o = out + size_t(i) * LOPT_STAT_FLOATS;
+      for (int f = 0; f < kNF; ++f) {
+        const int k = rho_feature(f);
+        o[f] = k < 0 ? r[f] : float(double(r[f]) / double(r[kNF + k]));
+      }
+      for (int k = 0; k < 3; ++k) o[kNF + k] = r[kNF + k];
+      o[kNF + 3] = 0.f;
+    }
+  });
+}
+
 lopt_status lopt_set_timing_events(lopt_handle* h, void* const* events, int32_t n) {
   return guarded([&] {
     if (!h) fail(LOPT_ERR_INVALID_ARGUMENT, "handle is NULL");

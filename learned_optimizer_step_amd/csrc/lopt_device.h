@@ -25,11 +25,6 @@ __device__ __forceinline__ float block_sum(float x, float* red) {
   return (red[0] + red[1]) + (red[2] + red[3]);
 }
 
-// k for the features that carry rho_k (g rho_k, m_a rho_k), else -1.
-__host__ __device__ constexpr int rho_feature(int f) {
-  return (f >= 10 && f < 13) ? f - 10 : (f >= 19 && f < 28) ? (f - 19) % 3 : -1;
-}
-
 __device__ __forceinline__ uint32_t div_c(uint32_t e, uint32_t magic, uint32_t shift) {
   return (__umulhi(e, magic) + e) >> shift;
 }

@@ -148,6 +148,11 @@ constexpr int kNumKernels = 5;
 hipError_t launch_step(const StepCtx& c, const StepParams& p, hipStream_t s, const hipEvent_t* events);
 hipError_t launch_apply(const StepCtx& c, const StepParams& p, hipStream_t s);
 
+// k for the features that carry rho_k (g rho_k, m_a rho_k), else -1.
+__host__ __device__ constexpr int rho_feature(int f) {
+  return (f >= 10 && f < 13) ? f - 10 : (f >= 19 && f < 28) ? (f - 19) % 3 : -1;
+}
+
 // Fast division by a 32-bit divisor for numerators below 2^31
 // (round-up multiplier method, Granlund & Montgomery 1994).
 inline void fastdiv_magic(uint32_t d, uint32_t* magic, uint32_t* shift) {

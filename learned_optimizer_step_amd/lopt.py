@@ -94,6 +94,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "lopt_set_config": (st, [ctypes.c_void_p, ctypes.POINTER(lopt_config)]),
         "lopt_get_mlp_impl": (st, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)]),
         "lopt_set_tensor_hyper": (st, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32]),
+        "lopt_get_tensor_stats": (st, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32]),
         "lopt_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -201,6 +202,17 @@ def lopt_set_tensor_hyper(h, lr: Optional[Sequence[float]], weight_decay: Option
         raise ValueError(f"expected {n} values, got {a.size}")
     _check(load_library().lopt_set_tensor_hyper(h, a.ctypes.data_as(ctypes.c_void_p), b.ctypes.data_as(ctypes.c_void_p),
                                                  a.size if n is None else n))
+
+
+LOPT_STAT_FLOATS = 32
+
+
+def lopt_get_tensor_stats(h, n: int) -> np.ndarray:
+    """(n, LOPT_STAT_FLOATS) float32: per tensor, the feature normalisers s_d of
+    its last step (entries 0..27) and sqrt(mean r_k) (28..30)."""
+    out = np.zeros((max(n, 0), LOPT_STAT_FLOATS), np.float32)
+    _check(load_library().lopt_get_tensor_stats(h, out.ctypes.data_as(ctypes.c_void_p), n))
+    return out
 
 
 LOPT_N_KERNELS = 5
@@ -319,6 +331,11 @@ class LOpt:
     def set_tensor_hyper(self, lr: Optional[Sequence[float]], weight_decay: Optional[Sequence[float]]) -> None:
         """Per-parameter lr and weight decay (None, None: the config's for all)."""
         lopt_set_tensor_hyper(self.handle, lr, weight_decay, len(self.params))
+
+    def tensor_stats(self) -> np.ndarray:
+        """Per tensor, the feature normalisers of its last step and sqrt(mean r_k)
+        (lopt_get_tensor_stats)."""
+        return lopt_get_tensor_stats(self.handle, len(self.params))
 
     def state_views(self, i: int) -> dict:
         """Views of tensor i's state: m (3,R,C), v (R,C), r (3,R), c (3,C)."""

@@ -353,6 +353,47 @@ def step_tensor_rows(p, g, state: dict, t: int, mlp: Mlp, hp: Hyper, rows: Seque
     return p_new.astype(np.float32), st
 
 
+def step_tensor_sub(p, g, state: dict, t: int, mlp: Mlp, hp: Hyper,
+                    rows: Optional[Sequence[int]] = None, cols: Optional[Sequence[int]] = None,
+                    block_rows: Optional[int] = None):
+    """One step of one tensor, with the update evaluated on a sub-block only.
+
+    Everything per tensor -- the row/column moving averages r, c, their means
+    rbar and every feature's sum of squares -- is computed over the whole
+    tensor, as in ``step_tensor``; the features, the MLP and the update are
+    then evaluated on the elements of the listed ``rows`` x ``cols`` (all of
+    them when None).  Returns (p_new[rows][:, cols], {"m": (3, nr, nc), "v":
+    (nr, nc), "r": (3, R), "c": (3, C)}, StepInfo(sum_sq, scales, acc)) with
+    the arrays rounded to fp32 (r and c in full)."""
+    P = as_matrix(p)
+    G = as_matrix(g)
+    R, C = G.shape
+    n = R * C
+    ri = np.arange(R) if rows is None else np.asarray(rows, dtype=np.int64)
+    ci = np.arange(C) if cols is None else np.asarray(cols, dtype=np.int64)
+    acc = accumulate(G, state, hp)
+    if block_rows is None:
+        block_rows = max(1, (1 << 14) // max(C, 1))
+    nf = hp.n_feat
+    sum_sq = np.zeros(nf)
+    for r0 in range(0, R, block_rows):
+        F = features(P, G, acc, hp, slice(r0, min(r0 + block_rows, R)))
+        sum_sq += (F * F).reshape(-1, nf).sum(axis=0)
+    scales = feature_scales(sum_sq, n, hp)
+    T = time_features(t, hp)
+    sub = Accumulators(acc.m[:, ri][:, :, ci], acc.v[ri][:, ci], acc.r[:, ri], acc.c[:, ci], acc.rbar)
+    Psub = P[ri][:, ci]
+    F = features(Psub, G[ri][:, ci], sub, hp)
+    x = np.concatenate([F * scales, np.broadcast_to(T, F.shape[:2] + (hp.n_time,))], axis=-1)
+    d, mg = mlp_forward(x, mlp)
+    u = update_from_output(d, mg, hp)
+    p_old = Psub.astype(np.float64)
+    p_new = p_old - hp.lr * u - hp.lr * hp.weight_decay * p_old
+    st = {"m": sub.m.astype(np.float32), "v": sub.v.astype(np.float32),
+          "r": acc.r.astype(np.float32), "c": acc.c.astype(np.float32)}
+    return p_new.astype(np.float32), st, StepInfo(sum_sq, scales, acc=acc)
+
+
 def step(params: Sequence[np.ndarray], grads: Sequence[np.ndarray], states: Sequence[dict],
          t: int, mlp_flat: np.ndarray, hp: Hyper = Hyper(),
          tensor_hyper: Optional[Sequence[Tuple[float, float]]] = None, **kw):

@@ -176,6 +176,8 @@ def test_null_handle_calls(lib):
     assert lib.lopt_set_tensor_hyper(None, None, None, 0) == L.LOPT_ERR_INVALID_ARGUMENT
     impl = ctypes.c_int32()
     assert lib.lopt_get_mlp_impl(None, ctypes.byref(impl)) == L.LOPT_ERR_INVALID_ARGUMENT
+    out = (ctypes.c_float * L.LOPT_STAT_FLOATS)()
+    assert lib.lopt_get_tensor_stats(None, out, 1) == L.LOPT_ERR_INVALID_ARGUMENT
     lib.lopt_destroy(None)  # no-op
 
 
