@@ -152,7 +152,12 @@ lopt_status lopt_default_config(lopt_config* out);
  * for (19, 11).  Returns 0 if n_feat or n_time is out of range. */
 size_t lopt_mlp_floats(int32_t n_feat, int32_t n_time);
 
-/* Creates a handle on the current HIP device.  cfg: hyperparameters (copied);
+/* Creates the optimizer object: the PyLO page's "Library design" section
+ * describes the learned optimizer as an object that holds the meta-learned
+ * MLP's weights and is then stepped over a model's parameters; the handle is
+ * that object (the weights and hyperparameters; the per-parameter state stays
+ * in the caller's buffers, bound by lopt_init_state).
+ * Creates a handle on the current HIP device.  cfg: hyperparameters (copied);
  * mlp_host: host pointer to lopt_mlp_floats(cfg->n_feat, cfg->n_time) floats (copied to
  * device memory that the handle owns).  The call is synchronous.
  * Errors: null pointers or out-of-range config -> INVALID_ARGUMENT;
@@ -174,7 +179,11 @@ size_t lopt_state_floats(int64_t rows, int64_t cols);
 lopt_status lopt_workspace_bytes(const lopt_handle* h, const lopt_tensor* ts, int32_t n,
                                  size_t* bytes);
 
-/* Binds the tensor list to the handle: validates it, lays out the plan (per-
+/* The per-parameter accumulators of "Library design" (momentum and
+ * second-moment moving averages, and the factored row/column averages of the
+ * feature families the page names) start at zero for a new optimizer; this
+ * call binds them.
+ * Binds the tensor list to the handle: validates it, lays out the plan (per-
  * tensor descriptors, work lists and reduction buffers) inside `workspace`,
  * zero-fills every state buffer and sets the step counter to 0.  workspace:
  * device pointer, 256-byte aligned, >= lopt_workspace_bytes(); owned by the
@@ -191,7 +200,14 @@ lopt_status lopt_workspace_bytes(const lopt_handle* h, const lopt_tensor* ts, in
 lopt_status lopt_init_state(lopt_handle* h, const lopt_tensor* ts, int32_t n, void* workspace,
                             size_t ws_bytes, void* stream);
 
-/* One optimizer step over the bound tensor list: queues the five kernels of
+/* The optimizer's step ("Library design": one call per training iteration
+ * updates every parameter), computed as "CUDA kernel design: two-pass fusion"
+ * > "Fused kernel strategy" lays it out: a statistics pass that sums each
+ * feature's squares over every tensor (kernel 1), then a pass that rebuilds
+ * the features, normalises them with those sums, evaluates the MLP per
+ * element and writes the update (kernel 2); the row/column averages the
+ * features need come first, from a pass over the gradients.
+ * One optimizer step over the bound tensor list: queues the five kernels of
  * the step on `stream` and returns (asynchronous); the step's finalize kernel
  * advances t.  An empty list queues nothing and leaves t unchanged.  ts must
  * list the same tensors (param, state, rows, cols) in the same order as

@@ -749,8 +749,8 @@ lopt_status lopt_get_tensor_stats(const lopt_handle* h, float* out, int32_t n) {
     if (n != int32_t(h->plan.bound.size())) fail(LOPT_ERR_STATE, "n differs from the bound tensor count");
     if (n == 0) return;
     // the workspace records: s_d, except s_d sqrt(mean r_k) for the features
-    // that carry rho_k (the apply pass folds that factor in), sqrt(mean r_k)
-    // at 28..30
+    // that carry rho_k in a matrix (the apply pass folds that factor in; a 1-D
+    // tensor's rho_k has none), sqrt(mean r_k) at 28..30
     std::vector<float> rec(size_t(n) * kStatStride);
     hip_check(hipDeviceSynchronize(), "hipDeviceSynchronize");
     hip_check(hipMemcpy(rec.data(), h->ws + h->plan.off_scales, rec.size() * sizeof(float), hipMemcpyDeviceToHost),
@@ -758,9 +758,10 @@ lopt_status lopt_get_tensor_stats(const lopt_handle* h, float* out, int32_t n) {
     for (int32_t i = 0; i < n; ++i) {
       const float* r = rec.data() + size_t(i) * kStatStride;
       float* o = out + size_t(i) * LOPT_STAT_FLOATS;
+      const bool matrix = h->plan.bound[size_t(i)].rows > 1;
       for (int f = 0; f < kNF; ++f) {
         const int k = rho_feature(f);
-        o[f] = k < 0 ? r[f] : float(double(r[f]) / double(r[kNF + k]));
+        o[f] = (k < 0 || !matrix) ? r[f] : float(double(r[f]) / double(r[kNF + k]));
       }
       for (int k = 0; k < 3; ++k) o[kNF + k] = r[kNF + k];
       o[kNF + 3] = 0.f;

@@ -400,7 +400,8 @@ __global__ __launch_bounds__(kBlock) void k_finalize(StepCtx c, StepParams hp) {
   if (threadIdx.x < kNF) {
     const int f = threadIdx.x;
     const int k = rho_feature(f);
-    const float rb = k < 0 ? 1.0f : sr[k];
+    // a 1-D tensor's rho_k is c_k^(-1/2) itself (its r_k over their mean is 1)
+    const float rb = (k < 0 || d.vec) ? 1.0f : sr[k];
     const float S = ((lds[0][f] + lds[1][f]) + (lds[2][f] + lds[3][f])) * (rb * rb);
     // features the variant does not feed get scale 0 (their weights are 0 too)
     sc[f] = f < hp.n_feat ? rb / sqrtf(S / float(d.n) + hp.eps_norm) : 0.f;

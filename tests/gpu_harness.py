@@ -3,7 +3,10 @@ binding) and through the CPU oracle on identical seeded inputs, and compares
 them element by element."""
 from __future__ import annotations
 
+import dataclasses
+import hashlib
 import sys
+from collections import OrderedDict
 from typing import Dict, List, Optional, Sequence
 
 import numpy as np
@@ -14,6 +17,11 @@ from learned_optimizer_step_amd import workloads as W
 
 RTOL = 1e-5   # parity bar on p, m1..m3, v, r1..r3, c1..c3
 ATOL = 1e-7
+
+# Every MLP path, the default first: bf16x8 and bf16x9 (fp32 arithmetic from
+# bf16 pieces), the fp32 matrix cores, the vector ALU, and the two narrower
+# split paths (bf16x6, fp16x3).
+IMPLS = [L.LOPT_MLP_BF16X8, L.LOPT_MLP_BF16X9, L.LOPT_MLP_MFMA, L.LOPT_MLP_VALU, L.LOPT_MLP_BF16X6, L.LOPT_MLP_FP16X3]
 
 
 def say(msg: str) -> None:
@@ -68,18 +76,57 @@ class GpuRun:
         self.opt.close()
 
 
+_ORACLE_CACHE: "OrderedDict[tuple, Dict[int, dict]]" = OrderedDict()
+
+
 def oracle_run(w: W.Workload, mlp: np.ndarray, hp: oracle.Hyper, steps: int,
                subset: Optional[Sequence[int]] = None, tensor_hyper=None) -> Dict[int, dict]:
     """Oracle trajectory of the tensors in ``subset`` (tensors are independent);
-    tensor_hyper: optional (lr, weight_decay) for every tensor of the workload."""
+    tensor_hyper: optional (lr, weight_decay) for every tensor of the workload.
+    Per tensor: p, m, v, r, c after the last step, and that step's feature
+    normalisers (scales) and sqrt(mean r_k) (sqrt_rbar).  The result does not
+    depend on the GPU's MLP path, so it is kept for the next call with the same
+    inputs (a few recent ones)."""
     idx = list(range(len(w.tensors))) if subset is None else list(subset)
-    th = None if tensor_hyper is None else [tensor_hyper[i] for i in idx]
-    ps = [W.param_init(w, i) for i in idx]
-    sts = [W.state_init(w, i) for i in idx]
-    for t in range(1, steps + 1):
-        gs = [W.grad_at(w, i, t) for i in idx]
-        ps, sts = oracle.step(ps, gs, sts, t, mlp, hp, tensor_hyper=th)
-    return {i: dict(p=p, **s) for i, p, s in zip(idx, ps, sts)}
+    th = None if tensor_hyper is None else tuple(tuple(float(x) for x in tensor_hyper[i]) for i in idx)
+    key = (w, steps, hp, hashlib.sha1(np.ascontiguousarray(mlp, np.float32).tobytes()).hexdigest(), tuple(idx), th)
+    if key in _ORACLE_CACHE:
+        _ORACLE_CACHE.move_to_end(key)
+        return _ORACLE_CACHE[key]
+    hp32 = hp.as_f32()
+    m = oracle.unpack_mlp(mlp, hp32.n_time, hp32.n_feat)
+    out = {}
+    for j, i in enumerate(idx):
+        # the per-tensor (lr, weight decay), fp32 numbers as the library takes them
+        hpi = hp32 if th is None else dataclasses.replace(hp32, lr=float(np.float32(th[j][0])),
+                                                          weight_decay=float(np.float32(th[j][1])))
+        p, st = W.param_init(w, i), W.state_init(w, i)
+        for t in range(1, steps + 1):
+            p, st, info = oracle.step_tensor(p, W.grad_at(w, i, t), st, t, m, hpi)
+        out[i] = dict(p=p, **st, scales=np.asarray(info.scales, np.float64),
+                      sqrt_rbar=np.sqrt(np.asarray(st["r"], np.float64).mean(axis=1)))
+    _ORACLE_CACHE[key] = out
+    while len(_ORACLE_CACHE) > 4:
+        _ORACLE_CACHE.popitem(last=False)
+    return out
+
+
+def compare_stats(got: np.ndarray, want: dict, n_feat: int, label: str, rtol=RTOL, atol=ATOL) -> List[str]:
+    """The GPU's per-tensor statistics (a lopt_get_tensor_stats row) against the
+    oracle's: the feature normalisers s_d (relative) and sqrt(mean r_k)."""
+    errs = []
+    s_got = np.asarray(got[:n_feat], np.float64)
+    s_want = np.asarray(want["scales"], np.float64)
+    bad = ~(np.abs(s_got - s_want) <= rtol * np.abs(s_want))
+    if bad.any():
+        d = int(np.argmax(bad))
+        errs.append(f"{label}.s_{d}: gpu={s_got[d]!r} oracle={s_want[d]!r} ({int(bad.sum())} features off)")
+    if np.any(np.asarray(got[n_feat:28]) != 0):
+        errs.append(f"{label}: normalisers of the features the variant does not feed are not 0")
+    r_got = np.asarray(got[28:31], np.float64)
+    if not np.all(np.abs(r_got - want["sqrt_rbar"]) <= atol + rtol * want["sqrt_rbar"]):
+        errs.append(f"{label}.sqrt_rbar: gpu={r_got!r} oracle={want['sqrt_rbar']!r}")
+    return errs
 
 
 def compare(got: dict, want: dict, label: str, rtol=RTOL, atol=ATOL) -> List[str]:
@@ -112,11 +159,14 @@ def parity(w: W.Workload, mlp: np.ndarray, cfg, torch, steps: Optional[int] = No
         run.step(t)
     idx = list(range(len(w.tensors))) if subset is None else list(subset)
     got = {i: run.fetch(i) for i in idx}
+    stats = run.opt.tensor_stats()
     run.close()
     want = oracle_run(w, mlp, hyper_from_cfg(cfg), steps, idx, tensor_hyper)
     errs = []
     for i in idx:
-        errs += compare(got[i], want[i], f"{w.key}[{i}:{w.tensors[i].name} {w.tensors[i].rows}x{w.tensors[i].cols}]")
+        label = f"{w.key}[{i}:{w.tensors[i].name} {w.tensors[i].rows}x{w.tensors[i].cols}]"
+        errs += compare(got[i], want[i], label)
+        errs += compare_stats(stats[i], want[i], int(cfg.n_feat), label)
     return errs
 
 

@@ -10,8 +10,8 @@ round differently from the tile's).  Sampled copies are compared, first and
 last included.  This exercises the 32-bit offsets, the magic-number division
 and the multi-level reductions at the top of their ranges.
 
-Each case needs ~80 GB of device memory (parameters, gradients, state) and
-releases it before the next test.
+Each case needs ~60 GB of device memory (parameters, gradients, state) and
+releases it before the next test; it steps every MLP path on the same buffers.
 """
 import gc
 
@@ -19,7 +19,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_harness import compare, hyper_from_cfg, say
+from gpu_harness import IMPLS, compare, hyper_from_cfg, say
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -44,6 +44,8 @@ def need_bytes(n, rows, cols):
 @pytest.mark.parametrize("kind", ["vector", "matrix"])
 @pytest.mark.parametrize("n_feat", [L.LOPT_N_FEATURES, L.LOPT_VELO_FEATURES])
 def test_maximum_size_tensor_equals_its_tile(kind, n_feat):
+    """One step on every MLP path (the buffers are allocated once; parameters,
+    state and step counter are reset between the paths)."""
     if kind == "vector":
         tile_shape, reps = (VEC_TILE,), VEC_REPS
         rows, cols = 1, VEC_TILE * VEC_REPS
@@ -64,11 +66,10 @@ def test_maximum_size_tensor_equals_its_tile(kind, n_feat):
     cfg = L.config_from(n_feat=n_feat)
 
     rep = (reps,) if kind == "vector" else (reps, 1)
-    p = torch.from_numpy(p_tile).cuda().repeat(*rep)
+    p_dev_tile = torch.from_numpy(p_tile).cuda()
+    p = p_dev_tile.repeat(*rep)
     g = torch.from_numpy(g_tile).cuda().repeat(*rep)
     opt = L.LOpt([p], mlp, cfg)
-    opt.step([g])
-    torch.cuda.synchronize()
 
     hp = hyper_from_cfg(cfg).as_f32()
     st0 = oracle.zero_state(*((1, VEC_TILE) if kind == "vector" else MAT_TILE))
@@ -80,20 +81,31 @@ def test_maximum_size_tensor_equals_its_tile(kind, n_feat):
     picks = sorted(set([0, 1, reps // 2, reps - 1] + rng.choice(reps, 6, replace=False).tolist()))
     views = opt.state_views(0)
     errs = []
-    for k in picks:
+    for impl in IMPLS:
+        say(f"[maxsize] {kind} n_feat={n_feat} impl={impl}")
         if kind == "vector":
-            sl = slice(k * VEC_TILE, (k + 1) * VEC_TILE)
-            got = {"p": p[sl].reshape(1, -1), "m": views["m"][:, :, sl], "v": views["v"][:, sl],
-                   "r": views["r"], "c": views["c"][:, sl]}
+            p.view(reps, -1).copy_(p_dev_tile.view(1, -1).expand(reps, -1))
         else:
-            sl = slice(k * MAT_TILE[0], (k + 1) * MAT_TILE[0])
-            got = {"p": p[sl], "m": views["m"][:, sl], "v": views["v"][sl], "r": views["r"][:, sl],
-                   "c": views["c"]}
-        got = {key: t.cpu().numpy() for key, t in got.items()}
-        errs += compare(got, want, f"{kind}[copy {k}]")
-    assert opt.t == 1
+            p.view(reps, *MAT_TILE).copy_(p_dev_tile.view(1, *MAT_TILE).expand(reps, *MAT_TILE))
+        opt.states[0].zero_()
+        opt.t = 0
+        L.lopt_set_config(opt.handle, L.config_from(n_feat=n_feat, mlp_impl=impl))
+        opt.step([g])
+        torch.cuda.synchronize()
+        assert opt.t == 1
+        for k in picks:
+            if kind == "vector":
+                sl = slice(k * VEC_TILE, (k + 1) * VEC_TILE)
+                got = {"p": p[sl].reshape(1, -1), "m": views["m"][:, :, sl], "v": views["v"][:, sl],
+                       "r": views["r"], "c": views["c"][:, sl]}
+            else:
+                sl = slice(k * MAT_TILE[0], (k + 1) * MAT_TILE[0])
+                got = {"p": p[sl], "m": views["m"][:, sl], "v": views["v"][sl], "r": views["r"][:, sl],
+                       "c": views["c"]}
+            got = {key: t.cpu().numpy() for key, t in got.items()}
+            errs += compare(got, want, f"{kind}[impl {impl}, copy {k}]")
     opt.close()
-    del opt, p, g, views
+    del opt, p, g, views, p_dev_tile
     gc.collect()
     torch.cuda.empty_cache()
     assert not errs, "\n".join(errs[:20])

@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_harness import GpuRun, compare, hyper_from_cfg, oracle_run, parity, parity_one_step_rows, say
+from gpu_harness import IMPLS, GpuRun, compare, hyper_from_cfg, oracle_run, parity, parity_one_step_rows, say
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -19,8 +19,6 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU container
 from learned_optimizer_step_amd import lopt as L  # noqa: E402
 from learned_optimizer_step_amd import workloads as W  # noqa: E402
 
-IMPLS = [L.LOPT_MLP_BF16X8, L.LOPT_MLP_BF16X9, L.LOPT_MLP_MFMA, L.LOPT_MLP_VALU, L.LOPT_MLP_BF16X6,
-         L.LOPT_MLP_FP16X3]
 
 EDGE_SHAPES = [(1,), (2,), (3,), (15,), (16,), (17,), (63,), (65,), (40000,),
                (1, 1), (2, 3), (3, 1), (7, 1), (17, 33), (65, 3), (4, 513), (300, 2),
@@ -222,51 +220,9 @@ def test_zero_gradients_stay_finite(impl):
     check(parity(w, mlp(bias_std=0.1), L.config_from(mlp_impl=impl), torch))
 
 
-@pytest.mark.parametrize("impl", IMPLS)
-def test_single4096_prewarmed(impl):
-    w = W.get_workload("single4096")
-    check(parity(w, mlp(), L.config_from(mlp_impl=impl), torch))
-
-
-@pytest.mark.parametrize("impl", IMPLS)
-def test_vit_b16_five_steps_subset(impl):
-    # full 147-tensor workload on the GPU for 5 steps; the oracle follows a
-    # subset covering every shape class (tensors are independent)
-    w = W.get_workload("vit_b16")
-    names = [t.name for t in w.tensors]
-    subset = [names.index(n) for n in ("pos_embed", "blocks.0.qkv.weight", "blocks.0.qkv.bias",
-                                       "blocks.5.norm2.weight", "blocks.11.fc2.weight",
-                                       "blocks.11.fc1.bias", "head")]
-    check(parity(w, mlp(), L.config_from(mlp_impl=impl), torch, subset=subset))
-
-
 def sample_rows(R, k, seed):
     rng = np.random.default_rng(seed)
     return sorted(set([0, R - 1] + rng.choice(R, min(R, k), replace=False).tolist()))
-
-
-@pytest.mark.parametrize("impl", IMPLS)
-def test_llama1b_one_step_sampled(impl):
-    w = W.get_workload("llama1b")
-    names = [t.name for t in w.tensors]
-    picks = {names.index("layers.0.q"): sample_rows(2048, 24, 1),
-             names.index("layers.21.down"): sample_rows(5632, 24, 2),
-             names.index("layers.3.attn_norm"): None,
-             names.index("unembed"): sample_rows(32000, 24, 3)}
-    check(parity_one_step_rows(w, mlp(), L.config_from(mlp_impl=impl), torch, picks))
-
-
-@pytest.mark.parametrize("impl", IMPLS)
-def test_ragged10k_one_step_sampled(impl):
-    w = W.get_workload("ragged10k")
-    sizes = np.array([t.n for t in w.tensors])
-    rng = np.random.default_rng(7)
-    idx = set(rng.choice(len(w.tensors), 120, replace=False).tolist())
-    picks = {i: None for i in idx if sizes[i] < 300_000}
-    big = int(sizes.argmax())
-    picks[int(sizes.argmin())] = None
-    picks[big] = sample_rows(w.tensors[big].rows, 16, 4) if w.tensors[big].rows > 1 else None
-    check(parity_one_step_rows(w, mlp(), L.config_from(mlp_impl=impl), torch, picks))
 
 
 def _run_states(w, cfg, steps, m):
@@ -604,17 +560,6 @@ def test_empty_tensor_list_steps():
     opt.step([])
     assert opt.t == 0     # no kernels, so the device counter does not advance
     opt.close()
-
-
-def test_gpt2_355m_one_step_sampled():
-    w = W.get_workload("gpt2_355m")
-    names = [t.name for t in w.tensors]
-    picks = {names.index("wte"): sample_rows(50257, 16, 5),
-             names.index("h.0.attn.c_attn.weight"): sample_rows(1024, 24, 6),
-             names.index("h.23.mlp.c_proj.weight"): sample_rows(4096, 24, 7),
-             names.index("h.11.mlp.c_fc.bias"): None,
-             names.index("ln_f.weight"): None}
-    check(parity_one_step_rows(w, mlp(), L.config_from(), torch, picks))
 
 
 # ----------------------------------------------------------------- VeLO-shaped variant
