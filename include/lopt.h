@@ -200,6 +200,30 @@ lopt_status lopt_workspace_bytes(const lopt_handle* h, const lopt_tensor* ts, in
 lopt_status lopt_init_state(lopt_handle* h, const lopt_tensor* ts, int32_t n, void* workspace,
                             size_t ws_bytes, void* stream);
 
+/* Bytes of the device array behind lopt_init_state_static, per GPU. */
+#define LOPT_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* For callers that cannot allocate memory: code being captured into a HIP
+ * graph, tight serving loops, harnesses that forbid allocation.  Binds the
+ * tensor list as lopt_init_state does, but lays the plan out in a device
+ * array of LOPT_STATIC_SCRATCH_BYTES that the library holds on each GPU (from
+ * the first such call on it until the process ends) instead of in a caller
+ * workspace, and allocates no memory, device or pinned (lopt_create has
+ * allocated the handle's weights before).  A list whose lopt_workspace_bytes
+ * exceeds LOPT_STATIC_SCRATCH_BYTES is refused with LOPT_ERR_WORKSPACE, and
+ * nothing changes.  The array is shared by every call on that GPU and keeps
+ * the last binding's contents: a binding made here (from any handle) replaces
+ * the previous static binding on that device, whose handle then gets
+ * LOPT_ERR_STATE from lopt_step, lopt_get_step, lopt_set_step and
+ * lopt_get_tensor_stats until it is bound again; calls on one GPU that
+ * overlap in time (from two threads, or steps of two static bindings queued
+ * on different streams) race on the array.  With such a binding, gradient
+ * pointers and per-tensor values that change between steps are copied from
+ * the handle's host memory and lopt_step then waits for `stream`.  Otherwise
+ * as lopt_init_state: state zero-filled, t = 0, the same stream semantics and
+ * errors. */
+lopt_status lopt_init_state_static(lopt_handle* h, const lopt_tensor* ts, int32_t n, void* stream);
+
 /* The optimizer's step ("Library design": one call per training iteration
  * updates every parameter), computed as "CUDA kernel design: two-pass fusion"
  * > "Fused kernel strategy" lays it out: a statistics pass that sums each

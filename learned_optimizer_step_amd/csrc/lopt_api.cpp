@@ -13,6 +13,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <stdexcept>
 #include <string>
@@ -325,9 +326,37 @@ struct lopt_handle {
   size_t staging_cap = 0;          // tensors per slot
   hipEvent_t slot_done[2] = {nullptr, nullptr};
   int next_slot = 0;
+  // Bound with lopt_init_state_static: the plan lives in the device's static
+  // scratch array (shared by every handle on that device) and changes between
+  // steps are copied from host memory without pinned slots.
+  bool static_ws = false;
 };
 
 namespace {
+
+// The handle whose list the static scratch array of each device holds.
+std::mutex g_scratch_mu;
+const lopt_handle* g_scratch_owner[kMaxDevices] = {};
+
+bool owns_scratch(const lopt_handle* h) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  return h->device >= 0 && h->device < kMaxDevices && g_scratch_owner[h->device] == h;
+}
+
+void set_scratch_owner(const lopt_handle* h, bool own) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (h->device < 0 || h->device >= kMaxDevices) return;
+  if (own) g_scratch_owner[h->device] = h;
+  else if (g_scratch_owner[h->device] == h) g_scratch_owner[h->device] = nullptr;
+}
+
+// A static binding's data is in the shared scratch only while no later static
+// binding on its device has replaced it.
+void check_static_owner(const lopt_handle* h) {
+  if (h->bound && h->static_ws && !owns_scratch(h))
+    fail(LOPT_ERR_STATE, "the device's static scratch now holds another binding (lopt_init_state_static was "
+                         "called again on this device); bind this list again");
+}
 
 // AUTO: bf16x8, measured the fastest of the paths with fp32 arithmetic
 // (bf16x8, bf16x9, the fp32 matrix cores, the vector ALU) for any weights
@@ -442,6 +471,32 @@ void reserve_slots(lopt_handle* h, size_t n) {
 // lr_step) pairs.  The source is a pinned slot that no queued copy still
 // reads, so the host does not wait for the stream.
 void upload_changes(lopt_handle* h, const lopt_tensor* ts, int32_t n, bool grads, bool pairs, hipStream_t s) {
+  if (!h->staging) {
+    // no pinned slots (a static binding): copy from the handle's host memory
+    // and wait for the stream, so the host copy can change afterwards
+    std::vector<float> th;
+    if (grads)
+      for (int32_t i = 0; i < n; ++i) {
+        h->plan.grads[i] = ts[i].grad;
+        h->plan.bound[i].grad = ts[i].grad;
+      }
+    if (grads && n > 0)
+      hip_check(hipMemcpyAsync(h->ws + h->plan.off_grads, h->plan.grads.data(), sizeof(const float*) * size_t(n),
+                               hipMemcpyHostToDevice, s),
+                "hipMemcpyAsync(gradient pointers)");
+    if (pairs && n > 0) {
+      th.resize(2 * size_t(n));
+      for (int32_t i = 0; i < n; ++i) {
+        th[2 * i] = 1.0f - h->th_lr[i] * h->th_wd[i];
+        th[2 * i + 1] = h->th_lr[i] * h->cfg.step_mult;
+      }
+      hip_check(hipMemcpyAsync(h->ws + h->plan.off_th, th.data(), th.size() * sizeof(float), hipMemcpyHostToDevice, s),
+                "hipMemcpyAsync(per-tensor hyperparameters)");
+    }
+    hip_check(hipStreamSynchronize(s), "hipStreamSynchronize(upload)");
+    if (pairs) h->th_dirty = false;
+    return;
+  }
   const int k = h->next_slot;
   hip_check(hipEventSynchronize(h->slot_done[k]), "hipEventSynchronize(staging slot)");
   char* slot = h->staging + size_t(k) * slot_bytes(h->staging_cap);
@@ -605,6 +660,7 @@ lopt_status lopt_create(const lopt_config* cfg, const float* mlp_host, lopt_hand
 
 void lopt_destroy(lopt_handle* h) {
   if (!h) return;
+  set_scratch_owner(h, false);
   for (hipEvent_t e : h->slot_done)
     if (e) {
       (void)hipEventSynchronize(e);
@@ -650,7 +706,44 @@ lopt_status lopt_init_state(lopt_handle* h, const lopt_tensor* ts, int32_t n, vo
     h->ws = ws;
     h->ws_bytes = ws_bytes;
     h->bound = true;
+    h->static_ws = false;
+    set_scratch_owner(h, false);
     h->th_active = h->th_dirty = false;  // per-tensor values belong to the previous list
+    h->th_lr.clear();
+    h->th_wd.clear();
+    hip_check(launch_zero_state(make_ctx(h), s), "launch(zero state)");
+  });
+}
+
+lopt_status lopt_init_state_static(lopt_handle* h, const lopt_tensor* ts, int32_t n, void* stream) {
+  return guarded([&] {
+    if (!h) fail(LOPT_ERR_INVALID_ARGUMENT, "handle is NULL");
+    check_device(h);
+    Plan pl = build_plan(ts, n);
+    if (pl.total > kScratchBytes)
+      fail(LOPT_ERR_WORKSPACE, "the tensor list needs " + std::to_string(pl.total) +
+                                   " bytes of workspace; the static scratch holds " + std::to_string(kScratchBytes) +
+                                   ": use lopt_init_state with a workspace");
+    void* scratch = nullptr;
+    hip_check(scratch_address(h->device, &scratch), "hipGetSymbolAddress(scratch)");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    drain_slots(h);  // a queued copy of the previous binding may still target its workspace
+    char* ws = static_cast<char*>(scratch);
+    const std::vector<int64_t> step0{0};
+    upload(ws, pl.off_desc, pl.desc, s);
+    upload(ws, pl.off_grads, pl.grads, s);
+    upload(ws, pl.off_tiles0, pl.tiles0, s);
+    upload(ws, pl.off_segs1, pl.segs1, s);
+    upload(ws, pl.off_chunks, pl.chunks, s);
+    upload(ws, pl.off_step, step0, s);
+    hip_check(hipStreamSynchronize(s), "hipStreamSynchronize(plan upload)");
+    h->plan = std::move(pl);
+    h->ws = ws;
+    h->ws_bytes = kScratchBytes;
+    h->bound = true;
+    h->static_ws = true;
+    set_scratch_owner(h, true);
+    h->th_active = h->th_dirty = false;
     h->th_lr.clear();
     h->th_wd.clear();
     hip_check(launch_zero_state(make_ctx(h), s), "launch(zero state)");
@@ -662,6 +755,7 @@ lopt_status lopt_step(lopt_handle* h, const lopt_tensor* ts, int32_t n, void* st
     if (!h) fail(LOPT_ERR_INVALID_ARGUMENT, "handle is NULL");
     bool grads_changed = false;
     check_same_list(h, ts, n, &grads_changed);
+    check_static_owner(h);
     check_device(h);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool pairs_changed = h->th_active && h->th_dirty;
@@ -686,6 +780,7 @@ lopt_status lopt_get_step(const lopt_handle* h, int64_t* t) {
       *t = 0;
       return;
     }
+    check_static_owner(h);
     hip_check(hipDeviceSynchronize(), "hipDeviceSynchronize");
     hip_check(hipMemcpy(t, h->ws + h->plan.off_step, sizeof(int64_t), hipMemcpyDeviceToHost), "hipMemcpy(step)");
   });
@@ -696,6 +791,7 @@ lopt_status lopt_set_step(lopt_handle* h, int64_t t) {
     if (!h) fail(LOPT_ERR_INVALID_ARGUMENT, "handle is NULL");
     if (t < 0) fail(LOPT_ERR_INVALID_ARGUMENT, "step must be >= 0");
     if (!h->bound) fail(LOPT_ERR_STATE, "lopt_init_state has not been called");
+    check_static_owner(h);
     hip_check(hipDeviceSynchronize(), "hipDeviceSynchronize");
     hip_check(hipMemcpy(h->ws + h->plan.off_step, &t, sizeof(int64_t), hipMemcpyHostToDevice), "hipMemcpy(step)");
   });
@@ -747,6 +843,7 @@ lopt_status lopt_get_tensor_stats(const lopt_handle* h, float* out, int32_t n) {
     if (!h || !out) fail(LOPT_ERR_INVALID_ARGUMENT, "NULL handle or output");
     if (!h->bound) fail(LOPT_ERR_STATE, "lopt_init_state has not been called");
     if (n != int32_t(h->plan.bound.size())) fail(LOPT_ERR_STATE, "n differs from the bound tensor count");
+    check_static_owner(h);
     if (n == 0) return;
     // the workspace records: s_d, except s_d sqrt(mean r_k) for the features
     // that carry rho_k in a matrix (the apply pass folds that factor in; a 1-D

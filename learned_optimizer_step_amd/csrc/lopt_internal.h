@@ -143,6 +143,14 @@ struct StepCtx {
 };
 
 hipError_t launch_zero_state(const StepCtx& c, hipStream_t s);
+
+// lopt_init_state_static's workspace: a device array of kScratchBytes per GPU
+// (LOPT_STATIC_SCRATCH_BYTES), 256-byte aligned.  scratch_address gives its
+// device address on `device`, which must be the current device (the address
+// is taken once per device and kept).
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+hipError_t scratch_address(int device, void** out);
 constexpr int kNumKernels = 5;
 // events: nullptr, or kNumKernels + 1 events recorded around the launches.
 hipError_t launch_step(const StepCtx& c, const StepParams& p, hipStream_t s, const hipEvent_t* events);

@@ -20,6 +20,8 @@
 // bitwise reproducible run to run.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "lopt_device.h"
 
 namespace lopt {
@@ -430,6 +432,30 @@ __global__ __launch_bounds__(kBlock) void k_zero_state(StepCtx c) {
     const size_t rc = d.vec ? 3 : 3 * (size_t(d.R) + size_t(d.C));
     for (size_t q = threadIdx.x; q < rc; q += kBlock) st[4 * n + q] = 0.f;
   }
+}
+
+// ---------------------------------------------------------------------------
+// The workspace of lopt_init_state_static: a file-scope device array that each
+// GPU the library runs on holds until the process ends.  In host code its name
+// is only a host-side stand-in, so its device address is taken once per device
+// with hipGetSymbolAddress (with that device current) and used from then on:
+// kernel arguments and copies receive that address, never the name.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+hipError_t scratch_address(int device, void** out) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[device]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p || (reinterpret_cast<uintptr_t>(p) & 255u)) return hipErrorInvalidSymbol;
+    addr[device] = p;
+  }
+  *out = addr[device];
+  return hipSuccess;
 }
 
 hipError_t launch_zero_state(const StepCtx& c, hipStream_t s) {

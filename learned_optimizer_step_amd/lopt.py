@@ -87,6 +87,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                       ctypes.POINTER(ctypes.c_size_t)]),
         "lopt_init_state": (st, [ctypes.c_void_p, ctypes.POINTER(lopt_tensor), ctypes.c_int32,
                                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+        "lopt_init_state_static": (st, [ctypes.c_void_p, ctypes.POINTER(lopt_tensor), ctypes.c_int32, ctypes.c_void_p]),
         "lopt_step": (st, [ctypes.c_void_p, ctypes.POINTER(lopt_tensor), ctypes.c_int32, ctypes.c_void_p]),
         "lopt_get_step": (st, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64)]),
         "lopt_set_step": (st, [ctypes.c_void_p, ctypes.c_int64]),
@@ -159,6 +160,13 @@ def lopt_workspace_bytes(h, ts: Sequence[lopt_tensor]) -> int:
 def lopt_init_state(h, ts: Sequence[lopt_tensor], workspace: int, ws_bytes: int, stream: int) -> None:
     _check(load_library().lopt_init_state(h, tensor_array(ts), len(ts), ctypes.c_void_p(workspace),
                                           ws_bytes, ctypes.c_void_p(stream)))
+
+
+LOPT_STATIC_SCRATCH_BYTES = 64 << 20
+
+
+def lopt_init_state_static(h, ts: Sequence[lopt_tensor], stream: int) -> None:
+    _check(load_library().lopt_init_state_static(h, tensor_array(ts), len(ts), ctypes.c_void_p(stream)))
 
 
 def lopt_step(h, ts: Sequence[lopt_tensor], stream: int) -> None:

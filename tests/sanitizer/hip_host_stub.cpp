@@ -209,6 +209,13 @@ void touch_workspace(const lopt::StepCtx& c) {
 }  // namespace
 
 namespace lopt {
+// lopt_init_state_static's array: host memory of the same size here
+alignas(256) static unsigned char g_scratch[kScratchBytes];
+hipError_t scratch_address(int device, void** out) {
+  if (device != 0) return hipErrorInvalidDevice;
+  *out = g_scratch;
+  return hipSuccess;
+}
 hipError_t launch_zero_state(const StepCtx& c, hipStream_t) {
   check_plan(c);
   return hipSuccess;

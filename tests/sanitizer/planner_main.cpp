@@ -117,6 +117,46 @@ void run_list(const std::vector<Shape>& shapes, const std::string& name, int n_f
   std::free(ws);
 }
 
+// lopt_init_state_static: the same checks on the library's static array (the
+// stand-in holds LOPT_STATIC_SCRATCH_BYTES of host memory), a list too large
+// for it, and a second static binding that takes the array over.
+void static_cases() {
+  FakeSpace fs;
+  lopt_config cfg;
+  lopt_default_config(&cfg);
+  std::vector<float> mlp(lopt_mlp_floats(28, 11), 0.01f);
+  lopt_handle *a = nullptr, *b = nullptr;
+  expect(lopt_create(&cfg, mlp.data(), &a) == LOPT_OK && lopt_create(&cfg, mlp.data(), &b) == LOPT_OK, "create");
+  std::vector<lopt_tensor> big = make_list(std::vector<Shape>(12, Shape{32000, 2048}), fs);
+  size_t bytes = 0;
+  expect(lopt_workspace_bytes(nullptr, big.data(), int32_t(big.size()), &bytes) == LOPT_OK &&
+             bytes > LOPT_STATIC_SCRATCH_BYTES, "a list larger than the static array");
+  g_stub_ws_bytes = LOPT_STATIC_SCRATCH_BYTES;
+  expect(lopt_init_state_static(a, big.data(), int32_t(big.size()), nullptr) == LOPT_ERR_WORKSPACE,
+         "static binding refuses a list larger than the array");
+  expect(lopt_step(a, big.data(), int32_t(big.size()), nullptr) == LOPT_ERR_STATE, "still unbound");
+  g_stub_ws_bytes = LOPT_STATIC_SCRATCH_BYTES;
+  std::vector<lopt_tensor> l1 = make_list({{300, 512}, {1, 7000}, {64, 64}, {33, 65}}, fs);
+  std::vector<lopt_tensor> l2 = make_list({{40, 64}, {1, 100}}, fs);
+  expect(lopt_init_state_static(a, l1.data(), 4, nullptr) == LOPT_OK, "static binding");
+  for (int k = 0; k < 3; ++k) {
+    for (auto& t : l1) t.grad = fs.take(4 * uint64_t(t.rows) * uint64_t(t.cols));   // new gradients each step
+    expect(lopt_step(a, l1.data(), 4, nullptr) == LOPT_OK, "static step");
+  }
+  std::vector<float> lr(4, 0.5f), wd(4, 0.01f);
+  expect(lopt_set_tensor_hyper(a, lr.data(), wd.data(), 4) == LOPT_OK && lopt_step(a, l1.data(), 4, nullptr) == LOPT_OK,
+         "static step with per-tensor values");
+  expect(lopt_init_state_static(b, l2.data(), 2, nullptr) == LOPT_OK, "second static binding, smaller list");
+  expect(lopt_step(b, l2.data(), 2, nullptr) == LOPT_OK, "step of the second binding");
+  int64_t t = 0;
+  expect(lopt_step(a, l1.data(), 4, nullptr) == LOPT_ERR_STATE, "the replaced binding's step is refused");
+  expect(lopt_get_step(a, &t) == LOPT_ERR_STATE, "the replaced binding's counter is refused");
+  expect(lopt_init_state_static(a, l1.data(), 4, nullptr) == LOPT_OK && lopt_step(a, l1.data(), 4, nullptr) == LOPT_OK,
+         "binding again");
+  lopt_destroy(b);
+  lopt_destroy(a);
+}
+
 void validation_cases() {
   FakeSpace fs;
   auto status = [](const std::vector<lopt_tensor>& ts) {
@@ -189,6 +229,7 @@ std::vector<Shape> read_list(const char* path) {
 
 int main(int argc, char** argv) {
   validation_cases();
+  static_cases();
   // the edges of the size range
   run_list({{1, 1}}, "1x1", 28);
   run_list({{1, (int64_t(1) << 31) - 1}}, "1 x (2^31 - 1)", 28);
