@@ -9,8 +9,13 @@
 //      instructions and the vector ALU share the SIMD's issue, so vector work
 //      adds to the matrix time instead of hiding under it;
 //   4. the same two figures for the bf16 matrix instruction
-//      v_mfma_f32_32x32x16_bf16 (the bf16x6 apply path), beside which
-//      vector instructions of the other waves do issue.
+//      v_mfma_f32_32x32x16_bf16 (the bf16x8, bf16x9 and bf16x6 apply paths),
+//      beside which vector instructions of the other waves do issue, and the
+//      time of 4 of them with 16, 32, 48 or 64 independent v_fma_f32 beside
+//      them (the apply kernels issue about one vector cycle per matrix
+//      cycle): how much vector work the matrix instructions hide;
+//   5. the throughput of the fp16 matrix instruction v_mfma_f32_32x32x16_f16
+//      (the fp16x3 apply path).
 // Prints one JSON object.  Every kernel writes only out[block * 64 + lane],
 // and out is sized for the largest grid launched.
 #include <hip/hip_runtime.h>
@@ -115,6 +120,28 @@ __device__ __forceinline__ bf16x8 bf16_operand(float a, float b) {
   return v;
 }
 
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// 16 fp16 matrix instructions per iteration over 2 independent accumulators.
+__global__ __launch_bounds__(64) void mfma_f16_chains(float* out, int iters, float s) {
+  f32x16 a0 = {0}, a1 = {0};
+  f16x8 x, y;
+  for (int i = 0; i < 8; ++i) {
+    x[i] = (_Float16)(i & 1 ? s : s * threadIdx.x * 1e-3f);
+    y[i] = (_Float16)(i & 1 ? s * 0.5f : s + 1e-3f);
+  }
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      a0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(x, y, a0, 0, 0, 0);
+      a1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(x, y, a1, 0, 0, 0);
+    }
+  }
+  float acc = 0.f;
+  for (int i = 0; i < 16; ++i) acc += a0[i] + a1[i];
+  out[size_t(blockIdx.x) * 64 + threadIdx.x] = acc;
+}
+
 // 16 bf16 matrix instructions per iteration over NACC independent accumulators.
 template <int NACC>
 __global__ __launch_bounds__(64) void mfma_bf16_chains(float* out, int iters, float s) {
@@ -135,8 +162,8 @@ __global__ __launch_bounds__(64) void mfma_bf16_chains(float* out, int iters, fl
   out[size_t(blockIdx.x) * 64 + threadIdx.x] = acc;
 }
 
-// 4 bf16 matrix instructions (2 chains) plus 16 independent v_fma_f32 (OP 1)
-// or none (OP 0) per iteration.
+// 4 bf16 matrix instructions (2 chains) plus 16 * OP independent v_fma_f32
+// per iteration (OP = 0: none).
 template <int OP>
 __global__ __launch_bounds__(64) void mfma_bf16_plus(float* out, int iters, float s) {
   f32x16 a0 = {0}, a1 = {0};
@@ -150,8 +177,9 @@ __global__ __launch_bounds__(64) void mfma_bf16_plus(float* out, int iters, floa
     a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, y, a0, 0, 0, 0);
     a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, y, a1, 0, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (OP == 1) v[i] = fmaf(v[i], s, xf);
+    for (int r = 0; r < OP; ++r)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = fmaf(v[i], s, xf);
   }
   float acc = 0.f;
   for (int i = 0; i < 16; ++i) acc += a0[i] + a1[i] + v[i];
@@ -294,6 +322,29 @@ int main() {
     });
     if (m0 <= 0.f || m1 <= 0.f) return 1;
     printf(", \"added_cycles_per_v_fma_f32_beside_bf16_mfma\": %.2f", (m1 - m0) / m0 * 128.0 / 16);
+    // SIMD cycles per iteration (4 matrix instructions = 128 alone) with
+    // 16 k vector FMAs beside them (alone: 4 cycles each)
+    const float m2 = time_ms([&] {
+      hipLaunchKernelGGL(mfma_bf16_plus<2>, dim3(blocks), dim3(64), 0, 0, out, it2, 1.0001f);
+    });
+    const float m3 = time_ms([&] {
+      hipLaunchKernelGGL(mfma_bf16_plus<3>, dim3(blocks), dim3(64), 0, 0, out, it2, 1.0001f);
+    });
+    const float m4 = time_ms([&] {
+      hipLaunchKernelGGL(mfma_bf16_plus<4>, dim3(blocks), dim3(64), 0, 0, out, it2, 1.0001f);
+    });
+    if (m2 <= 0.f || m3 <= 0.f || m4 <= 0.f) return 1;
+    printf(", \"bf16_mfma_cycles_with_vector_fmas\": {\"0\": 128.0, \"16\": %.1f, \"32\": %.1f, \"48\": %.1f, \"64\": %.1f}",
+           128.0 * m1 / m0, 128.0 * m2 / m0, 128.0 * m3 / m0, 128.0 * m4 / m0);
+  }
+  // 5. fp16 matrix instruction throughput (4 waves x 2 chains)
+  {
+    const int blocks = cus * 4 * 4;
+    const float ms = time_ms([&] {
+      hipLaunchKernelGGL(mfma_f16_chains, dim3(blocks), dim3(64), 0, 0, out, iters, 1.0001f);
+    });
+    if (ms <= 0.f) return 1;
+    printf(", \"f16_mfma_4waves_2chains_tflops\": %.1f", double(blocks) * iters * 16 * 32768 / (ms * 1e-3) / 1e12);
   }
   printf("}\n");
   CHECK(hipFree(out));
