@@ -129,12 +129,16 @@ def cpu_baseline(blocks: int = 7):
                       f"{cores} host cores visible"}
 
 
-def roofline(name: str, n: int, n_vec: int, apply_ms: float, fpe: int, traffic):
+def roofline(name: str, n: int, n_vec: int, apply_ms: float, fpe: int, traffic, single: bool = False):
     """The apply kernel against the peak of the unit its contraction runs on.
 
     achieved = algorithmic FLOP (fpe per element: the MLP's fp32 multiply-adds,
-    not the piece products a split path issues) over the kernel's time."""
+    not the piece products a split path issues) over the kernel's time.  A
+    one-launch step (single) has no separate apply kernel: its one kernel,
+    all five passes, takes that place."""
     kernel, unit, peak, pieces, _ = PATHS[name]
+    if single:
+        kernel = f"k_step_single ({kernel[len('k_apply_'):]}; all five passes)"
     tflops = fpe * n / (apply_ms * 1e-3) / 1e12
     out = {"bound": "alu" if name == "valu" else "mfma", "kernel": kernel, "unit_of_contraction": unit,
            "achieved": round(tflops, 3), "peak": peak, "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
@@ -162,6 +166,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="vit_b16")
     ap.add_argument("--impl", default="auto", choices=["auto"] + list(PATHS))
+    ap.add_argument("--launch", default="auto", choices=["auto", "split", "single"],
+                    help="five kernels per step (split), one (single), or the library's choice (auto: "
+                         "split)")
     ap.add_argument("--n-feat", type=int, default=28, choices=(28, 19),
                     help="per-element features: 28 (small_fc_lopt) or 19 (the VeLO-shaped variant)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -190,6 +197,8 @@ def main():
                "bf16x6": L.LOPT_MLP_BF16X6, "fp16x3": L.LOPT_MLP_FP16X3, "bf16x9": L.LOPT_MLP_BF16X9,
                "bf16x8": L.LOPT_MLP_BF16X8}
     name_of = {v: k for k, v in impl_of.items() if k != "auto"}
+    launch_of = {"auto": L.LOPT_LAUNCH_AUTO, "split": L.LOPT_LAUNCH_SPLIT, "single": L.LOPT_LAUNCH_SINGLE}
+    launch_name = {L.LOPT_LAUNCH_SPLIT: "split", L.LOPT_LAUNCH_SINGLE: "single"}
     w = W.get_workload(args.workload)
     log(f"[bench] {w.key}: {len(w.tensors)} tensors, {w.n_params} params; generating inputs")
     dev = torch.device("cuda:0")
@@ -198,7 +207,8 @@ def main():
         params.append(torch.from_numpy(W.param_init(w, i).reshape(t.shape)).to(dev))
         grads.append(torch.from_numpy(W.grad_at(w, i, 1).reshape(t.shape)).to(dev))
     mlp = W.mlp_weights(n_feat=args.n_feat)
-    opt = L.LOpt(params, mlp, L.config_from(mlp_impl=impl_of[args.impl], n_feat=args.n_feat))
+    opt = L.LOpt(params, mlp, L.config_from(mlp_impl=impl_of[args.impl], n_feat=args.n_feat,
+                                            launch=launch_of[args.launch]))
     if w.prewarm_std is not None:
         for i in range(len(w.tensors)):
             st = W.state_init(w, i)
@@ -206,25 +216,29 @@ def main():
             for k in ("m", "v", "r", "c"):
                 v[k].copy_(torch.from_numpy(st[k]))
     head = name_of[L.lopt_get_mlp_impl(opt.handle)]   # "auto" resolved
+    launch = launch_name[L.lopt_get_launch(opt.handle)]
     # the initial state, restored before each path is timed
     p0 = [p.clone() for p in params]
     s0 = [s.clone() for s in opt.states]
     torch.cuda.synchronize()
 
-    def restore(path: str):
+    def restore(path: str, mode: str):
         for p, q in zip(params, p0):
             p.copy_(q)
         for s, q in zip(opt.states, s0):
             s.copy_(q)
-        L.lopt_set_config(opt.handle, L.config_from(mlp_impl=impl_of[path], n_feat=args.n_feat))
+        L.lopt_set_config(opt.handle, L.config_from(mlp_impl=impl_of[path], n_feat=args.n_feat,
+                                                    launch=launch_of[mode]))
         opt.t = 0    # waits for the device, then resets the step counter
 
     nk = L.LOPT_N_KERNELS
     stream = torch.cuda.current_stream(dev)
 
-    def time_path(path: str, steps: int, warmup: int):
-        """warmup untimed steps, then exactly ``steps`` timed ones, from the initial state."""
-        restore(path)
+    def time_path(path: str, steps: int, warmup: int, mode: str):
+        """warmup untimed steps, then exactly ``steps`` timed ones, from the initial state.
+        A one-launch step records its first five events before its kernel, so
+        its whole time counts as k_apply's."""
+        restore(path, mode)
         for _ in range(warmup):
             opt.step(grads)
         events = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(steps)]
@@ -243,16 +257,14 @@ def main():
         per_step = np.array([events[k][0].elapsed_time(events[k][nk]) for k in range(steps)])
         return (t1 - t0) * 1e3 / steps, kern.mean(axis=0), per_step
 
-    log(f"[bench] {head}: warmup {args.warmup} steps, then {args.steps} timed")
-    ms, kern_ms, per_step = time_path(head, args.steps, args.warmup)
+    log(f"[bench] {head}, {launch} launch: warmup {args.warmup} steps, then {args.steps} timed")
+    ms, kern_ms, per_step = time_path(head, args.steps, args.warmup, launch)
 
-    graph = None
-    if args.graph or w.n_params < 10_000_000:
-        # one step captured into a HIP graph and replayed: the five kernels
-        # without the host's per-launch work (the step counter lives on the
-        # device, so replays see t = 1, 2, ...)
-        log("[bench] graph replay")
-        restore(head)
+    def time_graph(mode: str):
+        """One step captured into a HIP graph and replayed: the step's kernels
+        without the host's per-launch work (the step counter lives on the
+        device, so replays see t = 1, 2, ...)."""
+        restore(head, mode)
         opt.step(grads)                    # binds the gradient pointers outside the capture
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
@@ -266,9 +278,22 @@ def main():
             g.replay()
         torch.cuda.synchronize()
         gms = (time.perf_counter() - t0) * 1e3 / args.steps
-        graph = {"ms_per_step": round(gms, 4), "value": round(w.n_params / (gms * 1e-3) / 1e9, 4),
-                 "steps": args.steps, "launches_per_step": nk}
         del g
+        return {"ms_per_step": round(gms, 4), "value": round(w.n_params / (gms * 1e-3) / 1e9, 4),
+                "steps": args.steps, "launches_per_step": 1 if mode == "single" else nk}
+
+    graph, launches = None, None
+    if args.graph or w.n_params < 10_000_000:
+        log("[bench] graph replay")
+        graph = time_graph(launch)
+        # the other launch mode, eager and replayed, on the same inputs and initial state
+        other = "split" if launch == "single" else "single"
+        log(f"[bench] {other} launch, eager and graph replay")
+        ms_o, _, _ = time_path(head, args.steps, args.warmup, other)
+        launches = {launch: {"ms_per_step": round(ms, 4), "value": round(w.n_params / (ms * 1e-3) / 1e9, 4),
+                             "launches_per_step": 1 if launch == "single" else nk, "graph_replay": graph},
+                    other: {"ms_per_step": round(ms_o, 4), "value": round(w.n_params / (ms_o * 1e-3) / 1e9, 4),
+                            "launches_per_step": 1 if other == "single" else nk, "graph_replay": time_graph(other)}}
 
     fpe = flop_per_elem(args.n_feat)
     n = w.n_params
@@ -280,7 +305,7 @@ def main():
         log(f"[bench] the same inputs and initial state on {', '.join(others)}")
         for p in others:
             try:
-                ms2, k2, _ = time_path(p, 20, 2)
+                ms2, k2, _ = time_path(p, 20, 2, launch)
             except L.LoptError as err:  # weights outside the fp16x3 path's range
                 side_paths[p] = {"error": str(err)}
                 continue
@@ -322,10 +347,11 @@ def main():
         "dtype": "f32" if head in ("bf16x8", "bf16x9", "mfma", "valu") else head,
         "data": "synthetic",
         "config": {"workload": f"{w.key}: {w.description}", "n_params": n, "n_tensors": len(w.tensors),
-                   "mlp_impl": head, "mlp_arithmetic": PATHS[head][4],
+                   "mlp_impl": head, "mlp_arithmetic": PATHS[head][4], "launch": launch,
                    "state": "zero-init, gradients fixed" if w.prewarm_std is None else "pre-warmed, gradients fixed",
                    "variant": "small_fc_lopt" if args.n_feat == 28 else "VeLO-shaped (19 features, 30 inputs)"},
-        "roofline": roofline(head, n, n_vec, apply_ms, fpe, traffic),
+        "roofline": roofline(head, n, n_vec, apply_ms, fpe, traffic if launch == "split" else None,
+                             single=launch == "single"),
         "kernels_ms": {name: round(float(t), 4) for name, t in zip(L.KERNEL_NAMES, kern_ms)},
         "step_ms_median": round(float(np.median(per_step)), 4),
         "step_ms_min": round(float(per_step.min()), 4),
@@ -337,9 +363,10 @@ def main():
         out["step_frac_fp32_peak"] = round(step_fp32, 4)
     if graph is not None:
         out["graph_replay"] = graph
+        out["launch_modes"] = launches
     out["other_paths"] = side_paths
     for j, name in enumerate(L.KERNEL_NAMES):
-        if name in stream_bytes:
+        if name in stream_bytes and launch == "split":
             gbs = stream_bytes[name] / (kern_ms[j] * 1e-3) / 1e9
             out["hbm_kernels"][name] = {"achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                         "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes": stream_bytes[name]}
@@ -356,7 +383,8 @@ def main():
                 "k_apply_vs_mfma_4waves_2chains": round(achieved / mp["mfma_4waves_2chains_tflops"], 4)
                 if head == "mfma" else None,
                 "k_stats_vs_read_bw": round(out["hbm_kernels"]["k_stats"]["achieved"] /
-                                            (max(mp["read_bw_TBps"], mp["read_bw_nontemporal_TBps"]) * 1e3), 4),
+                                            (max(mp["read_bw_TBps"], mp["read_bw_nontemporal_TBps"]) * 1e3), 4)
+                if "k_stats" in out["hbm_kernels"] else None,
             }
         else:
             out["measured_peaks"] = {"error": res.stderr[-300:]}

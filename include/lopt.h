@@ -96,6 +96,30 @@ typedef enum lopt_mlp_impl {
                           accumulated in fp32 */
 } lopt_mlp_impl;
 
+/* How lopt_step launches a step.  The PyLO page counts kernel launches as a
+ * cost of the step ("Naive implementation bottleneck": 74-252 per step; "Use
+ * of the memory hierarchy": 30-114 once fused into its two passes). */
+typedef enum lopt_launch {
+  LOPT_LAUNCH_AUTO = 0,   /* LOPT_LAUNCH_SPLIT, the faster of the two at every
+                             list size measured (65,536 to 4.2 M elements) */
+  LOPT_LAUNCH_SPLIT = 1,  /* five kernels: row/column sums of g^2, row/column
+                             moving averages, statistics pass, per-tensor
+                             finalize, apply pass */
+  LOPT_LAUNCH_SINGLE = 2  /* one kernel that runs the same five passes in turn,
+                             separated by grid-wide barriers, with a grid no
+                             larger than the device keeps resident at once.
+                             Results are bit for bit those of
+                             LOPT_LAUNCH_SPLIT; slower (each barrier, which
+                             writes back and invalidates the caches of every
+                             block across the device's eight XCDs, costs more
+                             than a kernel boundary).  Each barrier wait is
+                             bounded (~2 s): if the blocks of the grid cannot
+                             all become resident (a persistent kernel of
+                             another stream holds the device), the step ends
+                             with invalid results and lopt_get_step reports
+                             LOPT_ERR_HIP */
+} lopt_launch;
+
 /* Hyperparameters.  lopt_default_config() fills the defaults shown. */
 typedef struct lopt_config {
   float beta_m[3];    /* momentum decays, default 0.1, 0.5, 0.9 */
@@ -113,6 +137,7 @@ typedef struct lopt_config {
   int32_t mlp_impl;   /* lopt_mlp_impl */
   int32_t n_feat;     /* per-element MLP inputs: LOPT_N_FEATURES (small_fc_lopt,
                          default) or LOPT_VELO_FEATURES (features 0..18 only) */
+  int32_t launch;     /* lopt_launch, default LOPT_LAUNCH_AUTO */
 } lopt_config;
 
 /* One parameter tensor.  All pointers are device pointers (hipMalloc / torch),
@@ -232,8 +257,8 @@ lopt_status lopt_init_state_static(lopt_handle* h, const lopt_tensor* ts, int32_
  * element and writes the update (kernel 2); the row/column averages the
  * features need come first, from a pass over the gradients.
  * One optimizer step over the bound tensor list: queues the five kernels of
- * the step on `stream` and returns (asynchronous); the step's finalize kernel
- * advances t.  An empty list queues nothing and leaves t unchanged.  ts must
+ * the step, or the one kernel that runs them in turn (lopt_config.launch), on
+ * `stream` and returns (asynchronous); the step's finalize pass advances t.  An empty list queues nothing and leaves t unchanged.  ts must
  * list the same tensors (param, state, rows, cols) in the same order as
  * lopt_init_state; grad pointers may differ from the previous call's: the new
  * pointers are copied to the device on `stream` from the handle's pinned
@@ -252,7 +277,9 @@ lopt_status lopt_step(lopt_handle* h, const lopt_tensor* ts, int32_t n, void* st
 /* Step counter: the number of steps taken (t of the last step).  The counter
  * lives in the workspace and the step's finalize kernel advances it, so steps
  * replayed from a captured HIP graph see t = 1, 2, 3, ...  Waits for the
- * device (hipDeviceSynchronize); 0 before lopt_init_state. */
+ * device (hipDeviceSynchronize); 0 before lopt_init_state.  Errors: a
+ * one-launch step since the binding whose grid barrier timed out
+ * (LOPT_LAUNCH_SINGLE) -> HIP (*t is still set); copy failure -> HIP. */
 lopt_status lopt_get_step(const lopt_handle* h, int64_t* t);
 
 /* Sets the step counter (to resume from saved state); t >= 0.  Waits for the
@@ -274,6 +301,12 @@ lopt_status lopt_set_config(lopt_handle* h, const lopt_config* cfg);
  * LOPT_MLP_AUTO resolved (LOPT_MLP_BF16X8).  Host-side only.  Errors: NULL argument ->
  * INVALID_ARGUMENT. */
 lopt_status lopt_get_mlp_impl(const lopt_handle* h, int32_t* impl);
+
+/* How the handle's steps over the bound list are launched: the config's
+ * launch mode, with LOPT_LAUNCH_AUTO resolved for the bound list's size
+ * (LOPT_LAUNCH_SINGLE or LOPT_LAUNCH_SPLIT; before a binding, as for an empty
+ * list).  Host-side only.  Errors: NULL argument -> INVALID_ARGUMENT. */
+lopt_status lopt_get_launch(const lopt_handle* h, int32_t* launch);
 
 /* Per-tensor learning rate and weight decay, as torch's parameter groups give
  * them (the PyLO page, "Library design": the optimizer is a torch optimizer;
@@ -316,8 +349,10 @@ lopt_status lopt_get_tensor_stats(const lopt_handle* h, float* out, int32_t n);
  * "Step-time reduction"; this lets a caller time each kernel of the step on
  * the step's own stream).  events: n caller-owned hipEvent_t handles; with
  * n == LOPT_N_KERNELS + 1 every following lopt_step records events[k] on its
- * stream just before kernel k and events[LOPT_N_KERNELS] after the last one;
- * n == 0 switches recording off.  The array is copied; the events must stay
+ * stream just before kernel k and events[LOPT_N_KERNELS] after the last one
+ * (a one-launch step records events[0..LOPT_N_KERNELS-1] before its kernel
+ * and events[LOPT_N_KERNELS] after it, so the whole step counts as the apply
+ * kernel's time); n == 0 switches recording off.  The array is copied; the events must stay
  * valid while steps that record them are queued.  Errors: NULL handle, NULL
  * events with n > 0, other n -> INVALID_ARGUMENT. */
 lopt_status lopt_set_timing_events(lopt_handle* h, void* const* events, int32_t n);

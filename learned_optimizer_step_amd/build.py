@@ -4,6 +4,7 @@
 """
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import shutil
 import subprocess
@@ -13,9 +14,11 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "liblopt.so")
-# (source, extra flags).  The apply kernels assume finite values in their
-# ReLUs (-fno-honor-nans gives a single v_max_f32 per ReLU).
-SOURCES = [("lopt_kernels.hip", []), ("lopt_apply.hip", ["-fno-honor-nans"]), ("lopt_api.cpp", [])]
+# (source, extra flags).  The apply kernels, and the one-launch step that
+# runs them, assume finite values in their ReLUs (-fno-honor-nans gives a
+# single v_max_f32 per ReLU).  The sources are compiled in parallel.
+SOURCES = [("lopt_kernels.hip", []), ("lopt_apply.hip", ["-fno-honor-nans"]),
+           ("lopt_single.hip", ["-fno-honor-nans"]), ("lopt_api.cpp", [])]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU instructions are disabled for all device code.
@@ -44,14 +47,17 @@ def _run(cmd, verbose):
 def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
     objdir = os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
-    objs = []
+    cmds, objs = [], []
     for src, extra in SOURCES:
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
-        _run([hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-c", "-Wall",
-              "-Wno-unused-function", "-I", os.path.join(ROOT, "include"), *DEVICE_FLAGS, *extra,
-              *[f"-D{d}" for d in defines],
-              os.path.join(CSRC, src), "-o", obj], verbose)
+        cmds.append([hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-c", "-Wall",
+                     "-Wno-unused-function", "-I", os.path.join(ROOT, "include"), *DEVICE_FLAGS, *extra,
+                     *[f"-D{d}" for d in defines],
+                     os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
+    with concurrent.futures.ThreadPoolExecutor(len(cmds)) as ex:
+        for f in [ex.submit(_run, cmd, verbose) for cmd in cmds]:
+            f.result()
     out_tmp = out + ".tmp"
     _run([hipcc(), "-shared", "-fPIC", *objs, "-o", out_tmp], verbose)
     os.replace(out_tmp, out)

@@ -79,7 +79,8 @@ struct Plan {
   uint32_t chunk_elems = 0;
   // byte offsets inside the workspace
   size_t off_desc = 0, off_grads = 0, off_tiles0 = 0, off_segs1 = 0, off_chunks = 0;
-  size_t off_rbar = 0, off_stats = 0, off_scales = 0, off_packed = 0, off_step = 0, off_th = 0, off_floats = 0;
+  size_t off_rbar = 0, off_stats = 0, off_scales = 0, off_packed = 0, off_step = 0, off_sync = 0, off_th = 0;
+  size_t off_floats = 0;
   size_t floats = 0;  // per-tensor float arrays (row/col partials, rq, cq)
   size_t total = 0;
   std::vector<lopt_tensor> bound;
@@ -105,6 +106,8 @@ void validate_config(const lopt_config* c) {
     fail(LOPT_ERR_INVALID_ARGUMENT, "unknown mlp_impl");
   if (c->n_feat != LOPT_N_FEATURES && c->n_feat != LOPT_VELO_FEATURES)
     fail(LOPT_ERR_INVALID_ARGUMENT, "n_feat must be 28 or 19");
+  if (c->launch < LOPT_LAUNCH_AUTO || c->launch > LOPT_LAUNCH_SINGLE)
+    fail(LOPT_ERR_INVALID_ARGUMENT, "unknown launch mode");
 }
 
 struct Range {
@@ -281,6 +284,7 @@ Plan build_plan(const lopt_tensor* ts, int32_t n) {
   pl.off_scales = take(sizeof(float) * kStatStride * pl.desc.size());
   pl.off_packed = take(sizeof(float) * kPkFloats);
   pl.off_step = take(sizeof(int64_t));
+  pl.off_sync = take(sizeof(uint32_t) * kSyncWords);
   pl.off_th = take(sizeof(float) * 2 * pl.desc.size());
   pl.off_floats = take(sizeof(float) * pl.floats);
   pl.total = off;
@@ -365,6 +369,13 @@ int32_t resolved_mlp_impl(const lopt_handle* h) {
   return LOPT_MLP_BF16X8;
 }
 
+// AUTO: the five kernels, measured faster than the one-launch step at every
+// list size (its grid-wide barriers each cost more than a kernel boundary)
+int32_t resolved_launch(const lopt_handle* h) {
+  if (h->cfg.launch != LOPT_LAUNCH_AUTO) return h->cfg.launch;
+  return LOPT_LAUNCH_SPLIT;
+}
+
 StepCtx make_ctx(const lopt_handle* h) {
   const Plan& pl = h->plan;
   StepCtx c{};
@@ -379,6 +390,7 @@ StepCtx make_ctx(const lopt_handle* h) {
   c.scales = reinterpret_cast<float*>(h->ws + pl.off_scales);
   c.packed = reinterpret_cast<float*>(h->ws + pl.off_packed);
   c.step = reinterpret_cast<int64_t*>(h->ws + pl.off_step);
+  c.sync = reinterpret_cast<uint32_t*>(h->ws + pl.off_sync);
   c.tensor_hyper = reinterpret_cast<const float*>(h->ws + pl.off_th);
   c.mlp = h->d_mlp;
   c.n_tensors = int32_t(pl.desc.size());
@@ -617,6 +629,7 @@ lopt_status lopt_default_config(lopt_config* out) {
     std::memcpy(c.timescales, ts, sizeof(ts));
     c.mlp_impl = LOPT_MLP_AUTO;
     c.n_feat = LOPT_N_FEATURES;
+    c.launch = LOPT_LAUNCH_AUTO;
     *out = c;
   });
 }
@@ -695,12 +708,14 @@ lopt_status lopt_init_state(lopt_handle* h, const lopt_tensor* ts, int32_t n, vo
     drain_slots(h);  // a queued copy of the previous binding may still target the old workspace
     char* ws = static_cast<char*>(workspace);
     const std::vector<int64_t> step0{0};
+    const std::vector<uint32_t> sync0(kSyncWords, 0u);
     upload(ws, pl.off_desc, pl.desc, s);
     upload(ws, pl.off_grads, pl.grads, s);
     upload(ws, pl.off_tiles0, pl.tiles0, s);
     upload(ws, pl.off_segs1, pl.segs1, s);
     upload(ws, pl.off_chunks, pl.chunks, s);
     upload(ws, pl.off_step, step0, s);
+    upload(ws, pl.off_sync, sync0, s);
     hip_check(hipStreamSynchronize(s), "hipStreamSynchronize(plan upload)");
     h->plan = std::move(pl);
     h->ws = ws;
@@ -730,12 +745,14 @@ lopt_status lopt_init_state_static(lopt_handle* h, const lopt_tensor* ts, int32_
     drain_slots(h);  // a queued copy of the previous binding may still target its workspace
     char* ws = static_cast<char*>(scratch);
     const std::vector<int64_t> step0{0};
+    const std::vector<uint32_t> sync0(kSyncWords, 0u);
     upload(ws, pl.off_desc, pl.desc, s);
     upload(ws, pl.off_grads, pl.grads, s);
     upload(ws, pl.off_tiles0, pl.tiles0, s);
     upload(ws, pl.off_segs1, pl.segs1, s);
     upload(ws, pl.off_chunks, pl.chunks, s);
     upload(ws, pl.off_step, step0, s);
+    upload(ws, pl.off_sync, sync0, s);
     hip_check(hipStreamSynchronize(s), "hipStreamSynchronize(plan upload)");
     h->plan = std::move(pl);
     h->ws = ws;
@@ -769,7 +786,17 @@ lopt_status lopt_step(lopt_handle* h, const lopt_tensor* ts, int32_t n, void* st
       upload_changes(h, ts, n, grads_changed, pairs_changed, s);
     }
     const StepParams p = make_params(h);
-    hip_check(launch_step(make_ctx(h), p, s, h->events.empty() ? nullptr : h->events.data()), "launch(step)");
+    const StepCtx c = make_ctx(h);
+    const hipEvent_t* ev = h->events.empty() ? nullptr : h->events.data();
+    if (resolved_launch(h) == LOPT_LAUNCH_SINGLE) {
+      int cap = 0;
+      hip_check(single_grid_cap(h->device, c.mlp_impl, &cap), "occupancy query (one-launch step)");
+      const int work = std::max(std::max(c.n_tiles0, c.n_segs1), std::max(c.n_chunks, c.n_tensors + 1));
+      hip_check(launch_single(c, p, std::min(std::min(cap, work), kSingleMaxBlocks), s, ev),
+                "launch(one-launch step)");
+    } else {
+      hip_check(launch_step(c, p, s, ev), "launch(step)");
+    }
   });
 }
 
@@ -783,6 +810,12 @@ lopt_status lopt_get_step(const lopt_handle* h, int64_t* t) {
     check_static_owner(h);
     hip_check(hipDeviceSynchronize(), "hipDeviceSynchronize");
     hip_check(hipMemcpy(t, h->ws + h->plan.off_step, sizeof(int64_t), hipMemcpyDeviceToHost), "hipMemcpy(step)");
+    uint32_t fault = 0;
+    hip_check(hipMemcpy(&fault, h->ws + h->plan.off_sync + sizeof(uint32_t) * kSyncFault, sizeof(fault),
+                        hipMemcpyDeviceToHost), "hipMemcpy(sync)");
+    if (fault)
+      fail(LOPT_ERR_HIP, "a one-launch step's grid barrier timed out: its blocks were not all resident at once "
+                         "(another kernel held the device); the results of that step are not valid");
   });
 }
 
@@ -813,6 +846,13 @@ lopt_status lopt_get_mlp_impl(const lopt_handle* h, int32_t* impl) {
   return guarded([&] {
     if (!h || !impl) fail(LOPT_ERR_INVALID_ARGUMENT, "NULL argument");
     *impl = resolved_mlp_impl(h);
+  });
+}
+
+lopt_status lopt_get_launch(const lopt_handle* h, int32_t* launch) {
+  return guarded([&] {
+    if (!h || !launch) fail(LOPT_ERR_INVALID_ARGUMENT, "NULL argument");
+    *launch = resolved_launch(h);
   });
 }
 

@@ -136,6 +136,7 @@ struct StepCtx {
   float* scales;                     // [n_tensors][32]: s_0..s_27, sqrt(rbar_k) at 28..30
   float* packed;                     // kPkFloats
   int64_t* step;                     // steps taken; advanced by k_finalize (graph-replay safe)
+  uint32_t* sync;                    // kSyncWords: the one-launch step's barrier words (lopt_single.hip)
   const float* tensor_hyper;         // [n_tensors][2]: decay, lr_step (StepParams::per_tensor)
   const float* mlp;                  // raw weights (handle-owned)
   int32_t n_tensors, n_tiles0, n_segs1, n_chunks;
@@ -155,6 +156,21 @@ constexpr int kNumKernels = 5;
 // events: nullptr, or kNumKernels + 1 events recorded around the launches.
 hipError_t launch_step(const StepCtx& c, const StepParams& p, hipStream_t s, const hipEvent_t* events);
 hipError_t launch_apply(const StepCtx& c, const StepParams& p, hipStream_t s);
+
+// The one-launch step (lopt_single.hip).  Barrier words in the workspace,
+// zero at binding: [0] launch count, [1] release word, [2] fault (a barrier
+// wait ran out: the grid was not resident at once), [kSyncArrive + b] the
+// arrival word of block b (at most kSingleMaxBlocks blocks).
+constexpr int kSingleMaxBlocks = 2048;
+constexpr int kSyncArrive = 16;
+constexpr int kSyncWords = kSyncArrive + kSingleMaxBlocks;
+constexpr int kSyncFault = 2;
+// Blocks of the one-launch kernel for MLP path `impl` that `device` keeps
+// resident at once (compute units x blocks per compute unit); cached.
+hipError_t single_grid_cap(int device, int impl, int* blocks);
+// events as launch_step's: the first kNumKernels are recorded before the
+// launch, the last after it.
+hipError_t launch_single(const StepCtx& c, const StepParams& p, int blocks, hipStream_t s, const hipEvent_t* events);
 
 // k for the features that carry rho_k (g rho_k, m_a rho_k), else -1.
 __host__ __device__ constexpr int rho_feature(int f) {

@@ -22,396 +22,24 @@
 
 #include <mutex>
 
-#include "lopt_device.h"
+#include "lopt_passes.h"
 
 namespace lopt {
 
 
 // ---------------------------------------------------------------------------
-// k_rowcol_sumsq: per-tile row sums and column sums of g^2.
-//   2-D tile: rows [r0, r1) x a window of CW <= 256 columns.  Thread t handles
-//   column c0 + (t mod CW) for rows r0 + (t / CW) + RS q, RS = 256 / CW.
-//   Row sums: butterfly over the CW lanes of a row slot (CW <= 64), or over
-//   the wave and then the CW/64 waves of the slot through LDS.
-//   Column sums: per-thread over its rows, then over the RS row slots in LDS.
-//   Flat tile (1-D tensors): one partial of sum g^2 over [c0, c1).
-__global__ __launch_bounds__(kBlock) void k_rowcol_sumsq(StepCtx c) {
-  const Tile0 tl = c.tiles0[blockIdx.x];
-  const float* __restrict__ g = uni(c.grads[tl.tensor]);
-  if (!g) return;  // no gradient this step: the tensor is skipped
-  const TensorDesc d = c.desc[tl.tensor];
-  float* __restrict__ ws = c.ws;
-  const int tid = threadIdx.x;
-  __shared__ float lds_rows[4 * kTile0Iters];
-  __shared__ float lds_cols[kBlock];
-  __shared__ float red[4];
+// The four streaming passes, one kernel each (bodies in lopt_passes.h).
+__global__ __launch_bounds__(kBlock) void k_rowcol_sumsq(StepCtx c) { rowcol_block(c, blockIdx.x); }
 
-  if (tl.flat) {
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    uint32_t e = tl.c0 + tid;
-    for (; e + 7 * kBlock < uint32_t(tl.c1); e += 8 * kBlock) {
-      float x[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) x[u] = __builtin_nontemporal_load(g + e + u * kBlock);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) acc[u] = fmaf(x[u], x[u], acc[u]);
-    }
-    for (; e < uint32_t(tl.c1); e += kBlock) {
-      const float a = __builtin_nontemporal_load(g + e);
-      acc[0] = fmaf(a, a, acc[0]);
-    }
-    const float s = block_sum(((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7])), red);
-    if (tid == 0) ws[d.off_rowpart + tl.win] = s;
-    return;
-  }
-
-  if (tl.cw_log2 == 8 && (d.C & 3) == 0 && (reinterpret_cast<uintptr_t>(g) & 15) == 0) {
-    // 256-column window, rows 16-byte aligned: each wave reads whole row
-    // segments with 16-byte loads (lane = 4 columns), waves take rows
-    // r0 + wave + 4u; a row's window sum completes inside one wave.
-    constexpr int kB = 8;  // rows per wave per batch
-    const int lane = tid & 63, wave = tid >> 6;
-    const int cb = tl.c0 + 4 * lane;
-    const bool act = cb < tl.c1;  // cols % 4 == 0: all four columns valid
-    const f32x4* __restrict__ g4 = reinterpret_cast<const f32x4*>(g);
-    const int C4 = d.C >> 2;
-    float4 ca = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int r = tl.r0 + wave; r < tl.r1; r += 4 * kB) {
-      f32x4 x[kB];
-#pragma unroll
-      for (int u = 0; u < kB; ++u) {
-        const int i = r + 4 * u;
-        x[u] = (act && i < tl.r1) ? __builtin_nontemporal_load(g4 + size_t(i) * C4 + (cb >> 2)) : f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int u = 0; u < kB; ++u) {
-        const float4 v = make_float4(x[u].x * x[u].x, x[u].y * x[u].y, x[u].z * x[u].z, x[u].w * x[u].w);
-        ca.x += v.x; ca.y += v.y; ca.z += v.z; ca.w += v.w;
-        const float rs = wave_sum((v.x + v.y) + (v.z + v.w));
-        const int i = r + 4 * u;
-        if (lane == 0 && i < tl.r1) ws[d.off_rowpart + size_t(tl.win) * d.R + i] = rs;
-      }
-    }
-    __shared__ float lds_c4[4][kBlock];
-    lds_c4[wave][4 * lane] = ca.x;
-    lds_c4[wave][4 * lane + 1] = ca.y;
-    lds_c4[wave][4 * lane + 2] = ca.z;
-    lds_c4[wave][4 * lane + 3] = ca.w;
-    __syncthreads();
-    const int j = tl.c0 + tid;
-    if (j < tl.c1)
-      ws[d.off_colpart + size_t(tl.rb) * d.C + j] = (lds_c4[0][tid] + lds_c4[1][tid]) + (lds_c4[2][tid] + lds_c4[3][tid]);
-    return;
-  }
-
-  const int cwl = tl.cw_log2;
-  const int CW = 1 << cwl;
-  const int RS = kBlock >> cwl;
-  const int slot = tid >> cwl;
-  const int lc = tid & (CW - 1);
-  const int j = tl.c0 + lc;
-  const bool colok = j < tl.c1;
-  const int R = d.R, C = d.C;
-  const int iters = (tl.r1 - tl.r0 + RS - 1) / RS;
-  const int wave = tid >> 6;
-  float colacc = 0.f;
-  constexpr int kRowBatch = 16;  // rows loaded per thread before reducing (bytes in flight)
-  for (int q0 = 0; q0 < iters; q0 += kRowBatch) {
-    float x[kRowBatch];
-#pragma unroll
-    for (int u = 0; u < kRowBatch; ++u) {
-      const int i = tl.r0 + slot + RS * (q0 + u);
-      x[u] = (colok && q0 + u < iters && i < tl.r1) ? __builtin_nontemporal_load(g + size_t(i) * C + j) : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < kRowBatch; ++u) {
-      const int q = q0 + u;
-      if (q < iters) {  // uniform across the block
-        const int i = tl.r0 + slot + RS * q;
-        const float x2 = x[u] * x[u];
-        colacc += x2;
-        float rs = x2;
-        if (CW <= 64) {
-          for (int o = CW >> 1; o > 0; o >>= 1) rs += __shfl_xor(rs, o);
-          if (lc == 0 && i < tl.r1) ws[d.off_rowpart + size_t(tl.win) * R + i] = rs;
-        } else {
-          rs = wave_sum(rs);
-          if ((tid & 63) == 0) lds_rows[wave * kTile0Iters + q] = rs;
-        }
-      }
-    }
-  }
-  lds_cols[tid] = colacc;
-  __syncthreads();
-  if (CW > 64) {
-    const int wps = CW >> 6;  // waves per row slot
-    if (tid < RS * iters) {
-      const int s = tid / iters, q = tid - s * iters;
-      const int i = tl.r0 + s + RS * q;
-      if (i < tl.r1) {
-        float v = 0.f;
-        for (int w = 0; w < wps; ++w) v += lds_rows[(s * wps + w) * kTile0Iters + q];
-        ws[d.off_rowpart + size_t(tl.win) * R + i] = v;
-      }
-    }
-  }
-  if (tid < CW && colok) {
-    float v = 0.f;
-    for (int s = 0; s < RS; ++s) v += lds_cols[s * CW + lc];
-    ws[d.off_colpart + size_t(tl.rb) * C + j] = v;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Compensated (Kahan) running sum: the moving-average kernel adds up to
-// thousands of similar positive partials per row or column in sequence (a
-// 2^31-element matrix has ~11,000 row blocks), where a plain fp32 sum would
-// drift by ~sqrt(count) roundings.  The device code is compiled without
-// reassociation, so the compensation is kept as written.  Once the sum is
-// infinite the compensation stays 0, so an infinite partial gives an
-// infinite sum (as a plain sum would), not inf - inf = NaN.
-struct KahanSum {
-  float s = 0.f, comp = 0.f;
-  __device__ __forceinline__ void add(float x) {
-    const float y = x - comp;
-    const float t = s + y;
-    comp = __builtin_isfinite(t) ? (t - s) - y : 0.f;
-    s = t;
-  }
-};
-
-// k_moving_avg: r_k and c_k moving averages (written to the state), their
-// inverse square roots (workspace) and per-segment partial sums of r_k.
-__global__ __launch_bounds__(kBlock) void k_moving_avg(StepCtx c, StepParams hp) {
-  const Seg1 sg = c.segs1[blockIdx.x];
-  if (!uni(c.grads[sg.tensor])) return;  // no gradient this step: the tensor is skipped
-  const TensorDesc d = c.desc[sg.tensor];
-  float* __restrict__ ws = c.ws;
-  const int tid = threadIdx.x;
-  __shared__ float red[4];
-  const size_t n = d.n;
-  float* r = d.st + 4 * n;
-  float* cst = r + 3 * size_t(d.R);
-
-  if (sg.kind == kSegRows) {
-    const int i = sg.a + tid;
-    float loc[3] = {0.f, 0.f, 0.f};
-    if (i < sg.b) {
-      KahanSum ks;
-      for (int w = 0; w < d.ncw; ++w) ks.add(ws[d.off_rowpart + size_t(w) * d.R + i]);
-      const float mean = ks.s / float(d.C);
-      float q[3];
-#pragma unroll
-      for (int k = 0; k < 3; ++k) {
-        const float rk = fmaf(hp.beta_f[k], r[size_t(k) * d.R + i], hp.omb_f[k] * (mean + hp.eps_f));
-        r[size_t(k) * d.R + i] = rk;
-        q[k] = rsqrtf(rk);
-        loc[k] = rk;
-      }
-      reinterpret_cast<float4*>(ws + d.off_rq)[i] = make_float4(q[0], q[1], q[2], 0.f);
-    }
-#pragma unroll
-    for (int k = 0; k < 3; ++k) {
-      const float s = block_sum(loc[k], red);
-      if (tid == 0) c.rbar_part[sg.slot * 4 + k] = s;
-    }
-  } else if (sg.kind == kSegCols) {
-    // 64 columns per segment, 4 thread groups per column over the row-block
-    // partials (b = group, group + 4, ...), combined in LDS in group order.
-    __shared__ float part[kColGroups][kSegCols1];
-    const int jl = tid % kSegCols1, grp = tid / kSegCols1;
-    const int j = sg.a + jl;
-    KahanSum ks;
-    if (j < sg.b)
-      for (int b = grp; b < d.nrb; b += kColGroups) ks.add(ws[d.off_colpart + size_t(b) * d.C + j]);
-    part[grp][jl] = ks.s;
-    __syncthreads();
-    if (grp == 0 && j < sg.b) {
-      const float s = (part[0][jl] + part[1][jl]) + (part[2][jl] + part[3][jl]);
-      const float mean = s / float(d.R);
-      float q[3];
-#pragma unroll
-      for (int k = 0; k < 3; ++k) {
-        const float ck = fmaf(hp.beta_f[k], cst[size_t(k) * d.C + j], hp.omb_f[k] * (mean + hp.eps_f));
-        cst[size_t(k) * d.C + j] = ck;
-        q[k] = rsqrtf(ck);
-      }
-      reinterpret_cast<float4*>(ws + d.off_cq)[j] = make_float4(q[0], q[1], q[2], 0.f);
-    }
-  } else {  // 1-D tensor: r_k is one value per tensor
-    KahanSum ks;
-    for (int w = tid; w < d.ncw; w += kBlock) ks.add(ws[d.off_rowpart + w]);
-    const float s = block_sum(ks.s, red);
-    if (tid == 0) {
-      const float mean = s / float(d.C);
-#pragma unroll
-      for (int k = 0; k < 3; ++k) {
-        const float rk = fmaf(hp.beta_f[k], r[k], hp.omb_f[k] * (mean + hp.eps_f));
-        r[k] = rk;
-        ws[d.off_rq + k] = rsqrtf(rk);
-        c.rbar_part[sg.slot * 4 + k] = rk;
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// k_stats: per-chunk sums of the squares of the 28 features (the page's
-// kernel 1).  Accumulators are updated in registers only; the apply kernel
-// recomputes them from the same inputs.
-template <bool VEC, bool NORMAL, int NF>
-__device__ __forceinline__ void stats_accumulate(const StepParams& hp, Elem& x, float acc[kNF]) {
-  float F[kNF], cn[3];
-  build_features<VEC, NORMAL, NF>(hp, x, F, cn);
-#pragma unroll
-  for (int f = 0; f < NF; ++f) acc[f] = fmaf(F[f], F[f], acc[f]);
-}
-
-// Four elements per thread per iteration, their loads issued together, so
-// each thread keeps ~100 bytes of HBM reads in flight.  RU (2-D tensors whose
-// column count is a multiple of 64): a wave's 64 consecutive elements lie in
-// one row (chunks start at multiples of 256 and end at multiples of 64), so
-// the row index is divided once per wave and the row record read once, and
-// every loop condition is the same for all lanes of a wave.
-template <bool VEC, bool NORMAL, int NF, bool RU>
-__device__ __forceinline__ void stats_body(const StepCtx& c, const StepParams& hp, const Chunk& ch,
-                                           const TensorDesc& d, const float* g, float acc[kNF]) {
-  constexpr bool ROW = RU && !VEC;
-  const Streams st = make_streams(d, g, c.ws, ch);
-  const uint32_t lane = threadIdx.x & 63;
-  uint32_t e = ch.e0 + threadIdx.x;
-  for (; e + 3 * kBlock < ch.e1; e += 4 * kBlock) {
-    Elem x[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint32_t eu = e + u * kBlock;
-      load_elem<VEC, ROW>(st, eu, x[u], ROW ? uni(eu - lane) : 0u);
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) stats_accumulate<VEC, NORMAL, NF>(hp, x[u], acc);
-  }
-  for (; e < ch.e1; e += kBlock) {
-    Elem x;
-    load_elem<VEC, ROW>(st, e, x, ROW ? uni(e - lane) : 0u);
-    stats_accumulate<VEC, NORMAL, NF>(hp, x, acc);
-  }
-}
+__global__ __launch_bounds__(kBlock) void k_moving_avg(StepCtx c, StepParams hp) { moving_avg_block(c, hp, blockIdx.x); }
 
 // Six waves per SIMD (80 VGPRs, a few spilled): 0.370 against 0.372 ms at
 // five on ViT-B/16.
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) void k_stats(StepCtx c, StepParams hp) {
-  Chunk ch;
-  TensorDesc d;
-  const float* g;
-  load_chunk(c, blockIdx.x, ch, d, g);
-  if (!g) return;  // no gradient this step: the tensor is skipped
-  __shared__ float lds[4][kNF];
-  float acc[kNF];
-#pragma unroll
-  for (int f = 0; f < kNF; ++f) acc[f] = 0.f;
-  dispatch_variant<true>(d, hp, [&](auto v) {
-    using V = decltype(v);
-    stats_body<V::vec, V::normal, V::nf, V::rowuni>(c, hp, ch, d, g, acc);
-  });
-  const int w = threadIdx.x >> 6;
-#pragma unroll
-  for (int f = 0; f < kNF; ++f) {
-    const float s = wave_sum(acc[f]);
-    if ((threadIdx.x & 63) == 0) lds[w][f] = s;
-  }
-  __syncthreads();
-  if (threadIdx.x < kNF) {
-    const int f = threadIdx.x;
-    c.stats_part[size_t(blockIdx.x) * kStatStride + f] = (lds[0][f] + lds[1][f]) + (lds[2][f] + lds[3][f]);
-  }
+  stats_block(c, hp, blockIdx.x);
 }
 
-// Packs the MLP for the apply kernel (one block): W1's feature columns, b1
-// with the step features folded in, W2, b2, W3, b3; advances the step counter.
-__device__ void pack_mlp(const StepCtx& c, const StepParams& hp) {
-  // The step counter lives in device memory so that a captured step, replayed
-  // from a graph, still sees t = 1, 2, 3, ...  Every thread reads it, then
-  // thread 0 advances it after the barrier below.
-  const int64_t step = *c.step + 1;
-  const float tf = float(step);
-  const int nf = hp.n_feat;
-  const int din = nf + hp.n_time;
-  const float* W1 = c.mlp;
-  const float* b1 = W1 + kH * din;
-  const float* W2 = b1 + kH;
-  const float* b2 = W2 + kH * kH;
-  const float* W3 = b2 + kH;
-  const float* b3 = W3 + 2 * kH;
-  float* pk = c.packed;
-  for (int q = threadIdx.x; q < kH * kNF; q += kBlock) {
-    const int o = q / kNF, f = q - o * kNF;
-    pk[kPkW1 + q] = f < nf ? W1[o * din + f] : 0.f;
-  }
-  if (threadIdx.x < kH) {
-    const int o = threadIdx.x;
-    float b = b1[o];
-    for (int s = 0; s < hp.n_time; ++s) b = fmaf(W1[o * din + nf + s], tanhf(tf / hp.timescales[s]), b);
-    pk[kPkB1 + o] = b;
-    pk[kPkB2 + o] = b2[o];
-    pk[kPkW3 + o] = W3[o];
-    pk[kPkW3 + kH + o] = W3[kH + o];
-  }
-  for (int q = threadIdx.x; q < kH * kH; q += kBlock) pk[kPkW2 + q] = W2[q];
-  if (threadIdx.x < 2) pk[kPkB3 + threadIdx.x] = b3[threadIdx.x];
-  __syncthreads();
-  if (threadIdx.x == 0) *c.step = step;
-}
-
-// ---------------------------------------------------------------------------
-// k_finalize: per tensor, S'_d = sum of the chunk partials (chunk order).  The
-// statistics pass leaves sqrt(rbar_k) out of rho_k, so for the rho features
-// S_d = S'_d rbar_k.  Then s_d = (S_d / n + eps_norm)^(-1/2), and the scale
-// stored for the apply kernel (which also leaves sqrt(rbar_k) out) is s_d, or
-// s_d sqrt(rbar_k) for the rho features.  The last block (index n_tensors)
-// packs the MLP for the apply kernel, folding the step features into the first
-// bias: b1' = b1 + W1[:, 28:28+n_time] tanh(t / tau); it runs beside the
-// per-tensor blocks instead of after tensor 0's.
-__global__ __launch_bounds__(kBlock) void k_finalize(StepCtx c, StepParams hp) {
-  const int t = blockIdx.x;
-  if (t == c.n_tensors) {
-    pack_mlp(c, hp);
-    return;
-  }
-  if (!uni(c.grads[t])) return;  // no gradient this step: the tensor is skipped
-  const TensorDesc d = c.desc[t];
-  __shared__ float lds[4][kNF];
-  __shared__ float red[4];
-  float sr[3];
-  block_sr(c, d, sr, red);
-  float acc[kNF];
-#pragma unroll
-  for (int f = 0; f < kNF; ++f) acc[f] = 0.f;
-  for (int q = threadIdx.x; q < d.nchunk; q += kBlock) {
-    const float* sp = c.stats_part + size_t(d.chunk0 + q) * kStatStride;
-#pragma unroll
-    for (int f = 0; f < kNF; ++f) acc[f] += sp[f];
-  }
-  const int w = threadIdx.x >> 6;
-#pragma unroll
-  for (int f = 0; f < kNF; ++f) {
-    const float s = wave_sum(acc[f]);
-    if ((threadIdx.x & 63) == 0) lds[w][f] = s;
-  }
-  __syncthreads();
-  float* sc = c.scales + size_t(t) * kStatStride;
-  if (threadIdx.x < kNF) {
-    const int f = threadIdx.x;
-    const int k = rho_feature(f);
-    // a 1-D tensor's rho_k is c_k^(-1/2) itself (its r_k over their mean is 1)
-    const float rb = (k < 0 || d.vec) ? 1.0f : sr[k];
-    const float S = ((lds[0][f] + lds[1][f]) + (lds[2][f] + lds[3][f])) * (rb * rb);
-    // features the variant does not feed get scale 0 (their weights are 0 too)
-    sc[f] = f < hp.n_feat ? rb / sqrtf(S / float(d.n) + hp.eps_norm) : 0.f;
-  } else if (threadIdx.x < kNF + 3) {
-    const int k = threadIdx.x - kNF;
-    sc[kNF + k] = sr[k];
-  }
-}
+__global__ __launch_bounds__(kBlock) void k_finalize(StepCtx c, StepParams hp) { finalize_block(c, hp, blockIdx.x); }
 
 // ---------------------------------------------------------------------------
 // k_zero_state: zero-fills the state over the chunk list (per-element blocks

@@ -34,6 +34,9 @@ LOPT_MLP_BF16X6 = 3
 LOPT_MLP_FP16X3 = 4
 LOPT_MLP_BF16X9 = 5
 LOPT_MLP_BF16X8 = 6
+LOPT_LAUNCH_AUTO = 0     # LOPT_LAUNCH_SPLIT (measured faster at every size)
+LOPT_LAUNCH_SPLIT = 1    # five kernels per step
+LOPT_LAUNCH_SINGLE = 2   # one kernel per step (the five passes behind grid-wide barriers)
 LOPT_MAX_TIME = 11
 LOPT_N_FEATURES = 28     # small_fc_lopt's per-element features
 LOPT_VELO_FEATURES = 19  # the VeLO-shaped variant's (features 0..18)
@@ -52,7 +55,7 @@ class lopt_config(ctypes.Structure):
                 ("exp_mult", ctypes.c_float), ("step_mult", ctypes.c_float),
                 ("lr", ctypes.c_float), ("weight_decay", ctypes.c_float),
                 ("n_time", ctypes.c_int32), ("timescales", ctypes.c_float * LOPT_MAX_TIME),
-                ("mlp_impl", ctypes.c_int32), ("n_feat", ctypes.c_int32)]
+                ("mlp_impl", ctypes.c_int32), ("n_feat", ctypes.c_int32), ("launch", ctypes.c_int32)]
 
 
 class lopt_tensor(ctypes.Structure):
@@ -94,6 +97,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "lopt_set_timing_events": (st, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32]),
         "lopt_set_config": (st, [ctypes.c_void_p, ctypes.POINTER(lopt_config)]),
         "lopt_get_mlp_impl": (st, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)]),
+        "lopt_get_launch": (st, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)]),
         "lopt_set_tensor_hyper": (st, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32]),
         "lopt_get_tensor_stats": (st, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32]),
         "lopt_last_error": (ctypes.c_char_p, []),
@@ -192,6 +196,13 @@ def lopt_get_mlp_impl(h) -> int:
     impl = ctypes.c_int32()
     _check(load_library().lopt_get_mlp_impl(h, ctypes.byref(impl)))
     return int(impl.value)
+
+
+def lopt_get_launch(h) -> int:
+    """How the handle's steps over the bound list are launched (LOPT_LAUNCH_AUTO resolved)."""
+    mode = ctypes.c_int32()
+    _check(load_library().lopt_get_launch(h, ctypes.byref(mode)))
+    return int(mode.value)
 
 
 def lopt_set_tensor_hyper(h, lr: Optional[Sequence[float]], weight_decay: Optional[Sequence[float]],

@@ -11,6 +11,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <cstdint>
+#include <algorithm>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -225,5 +226,25 @@ hipError_t launch_step(const StepCtx& c, const StepParams& p, hipStream_t, const
   touch_workspace(c);
   if (p.n_feat != kNF && p.n_feat != kVeloNF) return hipErrorInvalidValue;
   return hipSuccess;
+}
+// the one-launch step: 1024 resident blocks, as a 256-CU device at four per CU
+hipError_t single_grid_cap(int device, int impl, int* blocks) {
+  if (device != 0 || impl < 1 || impl > 6) return hipErrorInvalidValue;
+  *blocks = 1024;
+  return hipSuccess;
+}
+hipError_t launch_single(const StepCtx& c, const StepParams& p, int blocks, hipStream_t s, const hipEvent_t* ev) {
+  const int work = std::max(std::max(c.n_tiles0, c.n_segs1), std::max(c.n_chunks, c.n_tensors + 1));
+  if (c.n_tensors > 0) REQUIRE(blocks >= 1 && blocks <= 1024 && blocks <= work, blocks, work);
+  const char* ws = reinterpret_cast<const char*>(c.ws);
+  const char* q = reinterpret_cast<const char*>(c.sync);
+  REQUIRE(q >= ws && q + sizeof(uint32_t) * kSyncWords <= ws + g_stub_ws_bytes, q - ws, g_stub_ws_bytes);
+  REQUIRE(blocks <= kSingleMaxBlocks, blocks, kSingleMaxBlocks);
+  std::vector<uint32_t> words(kSyncWords);
+  std::memcpy(words.data(), c.sync, sizeof(uint32_t) * kSyncWords);
+  ++words[0];
+  for (int b = 0; b < blocks; ++b) words[kSyncArrive + b] = 4 * words[0];
+  std::memcpy(c.sync, words.data(), sizeof(uint32_t) * kSyncWords);
+  return launch_step(c, p, s, ev);
 }
 }  // namespace lopt

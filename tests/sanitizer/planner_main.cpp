@@ -102,6 +102,11 @@ void run_list(const std::vector<Shape>& shapes, const std::string& name, int n_f
   expect(lopt_step(h, ts.data(), n, nullptr) == LOPT_OK, name + ": step with per-tensor values");
   expect(lopt_set_tensor_hyper(h, lr.data(), wd.data(), n + 1) == LOPT_ERR_STATE, name + ": hyper count");
   expect(lopt_set_tensor_hyper(h, nullptr, nullptr, n) == LOPT_OK, name + ": clear per-tensor values");
+  for (int32_t mode : {LOPT_LAUNCH_SINGLE, LOPT_LAUNCH_SPLIT, LOPT_LAUNCH_AUTO}) {
+    cfg.launch = mode;
+    expect(lopt_set_config(h, &cfg) == LOPT_OK && lopt_step(h, ts.data(), n, nullptr) == LOPT_OK,
+           name + ": step with launch mode " + std::to_string(mode));
+  }
   int64_t t = -1;
   expect(lopt_set_step(h, 41) == LOPT_OK && lopt_get_step(h, &t) == LOPT_OK && t == 41, name + ": step counter");
   std::vector<float> stats(size_t(n) * LOPT_STAT_FLOATS + 1);
@@ -192,6 +197,9 @@ void validation_cases() {
   lopt_handle* h = nullptr;
   cfg.mlp_impl = 99;
   expect(lopt_create(&cfg, mlp.data(), &h) == LOPT_ERR_INVALID_ARGUMENT && !h, "unknown mlp_impl");
+  lopt_default_config(&cfg);
+  cfg.launch = 3;
+  expect(lopt_create(&cfg, mlp.data(), &h) == LOPT_ERR_INVALID_ARGUMENT && !h, "unknown launch mode");
   lopt_default_config(&cfg);
   mlp[7] = std::nanf("");
   expect(lopt_create(&cfg, mlp.data(), &h) == LOPT_ERR_INVALID_ARGUMENT && !h, "NaN weight");

@@ -43,7 +43,8 @@ def test_default_config_values(lib):
     assert c.eps_norm == pytest.approx(1e-30)
     assert c.exp_mult == pytest.approx(1e-3) and c.step_mult == pytest.approx(1e-3)
     assert c.lr == 1.0 and c.weight_decay == 0.0 and c.n_time == 11
-    assert c.n_feat == 28 and c.mlp_impl == L.LOPT_MLP_AUTO   # last field: the struct layouts agree
+    assert c.n_feat == 28 and c.mlp_impl == L.LOPT_MLP_AUTO
+    assert c.launch == L.LOPT_LAUNCH_AUTO   # last field: the struct layouts agree
     assert list(c.timescales) == pytest.approx([1, 3, 10, 30, 100, 300, 1e3, 3e3, 1e4, 3e4, 1e5])
     assert lib.lopt_default_config(None) == L.LOPT_ERR_INVALID_ARGUMENT
     assert "NULL" in L.lopt_last_error()
@@ -145,6 +146,10 @@ def test_create_rejects_bad_config_without_device(lib):
     c = L.config_from(mlp_impl=L.LOPT_MLP_BF16X8 + 1)
     assert lib.lopt_create(ctypes.byref(c), w, ctypes.byref(h)) == L.LOPT_ERR_INVALID_ARGUMENT
     assert "mlp_impl" in L.lopt_last_error()
+    for bad in (-1, L.LOPT_LAUNCH_SINGLE + 1):
+        c = L.config_from(launch=bad)
+        assert lib.lopt_create(ctypes.byref(c), w, ctypes.byref(h)) == L.LOPT_ERR_INVALID_ARGUMENT
+        assert "launch" in L.lopt_last_error()
     c = L.lopt_default_config()
     assert lib.lopt_create(ctypes.byref(c), None, ctypes.byref(h)) == L.LOPT_ERR_INVALID_ARGUMENT
     assert lib.lopt_create(None, w, ctypes.byref(h)) == L.LOPT_ERR_INVALID_ARGUMENT
@@ -176,6 +181,7 @@ def test_null_handle_calls(lib):
     assert lib.lopt_set_tensor_hyper(None, None, None, 0) == L.LOPT_ERR_INVALID_ARGUMENT
     impl = ctypes.c_int32()
     assert lib.lopt_get_mlp_impl(None, ctypes.byref(impl)) == L.LOPT_ERR_INVALID_ARGUMENT
+    assert lib.lopt_get_launch(None, ctypes.byref(impl)) == L.LOPT_ERR_INVALID_ARGUMENT
     out = (ctypes.c_float * L.LOPT_STAT_FLOATS)()
     assert lib.lopt_get_tensor_stats(None, out, 1) == L.LOPT_ERR_INVALID_ARGUMENT
     lib.lopt_destroy(None)  # no-op
