@@ -65,8 +65,8 @@ def log(msg):
 
 # Sources of the apply kernel; the committed HBM-traffic figure is only valid
 # for the code it was measured on (comments and blank lines do not count).
-APPLY_SOURCES = ("learned_optimizer_step_amd/csrc/lopt_apply.hip", "learned_optimizer_step_amd/csrc/lopt_device.h",
-                 "learned_optimizer_step_amd/csrc/lopt_internal.h")
+APPLY_SOURCES = ("learned_optimizer_step_amd/csrc/lopt_apply.hip", "learned_optimizer_step_amd/csrc/lopt_apply_body.h",
+                 "learned_optimizer_step_amd/csrc/lopt_device.h", "learned_optimizer_step_amd/csrc/lopt_internal.h")
 
 
 def code_text(src: str) -> str:
