@@ -496,6 +496,10 @@ __device__ __forceinline__ void apply_x6_body(const StepCtx& c, const StepParams
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc1s[b][q] = 0.f;
+    // Raised issue priority over the MLP: this wave's matrix instructions
+    // (and the splits that feed them) go ahead of other waves' feature work
+    // (measured: apply 1.2 % faster on ViT-B/16).
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       u32x4 a[3];
@@ -552,6 +556,7 @@ __device__ __forceinline__ void apply_x6_body(const StepCtx& c, const StepParams
       dpart[b] = dsum;
       mpart[b] = msum;
     }
+    __builtin_amdgcn_s_setprio(0);
     const float dA = dpart[0], dB = dpart[1], mA = mpart[0], mB = mpart[1];
     float d0, d1, m0, m1;
     swap_halves(dA, dB, d0, d1);
