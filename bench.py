@@ -110,7 +110,7 @@ def cpu_baseline(blocks: int = 7):
     from learned_optimizer_step_amd import workloads as W
 
     cores = len(os.sched_getaffinity(0))
-    threads = min(cores, 16)     # BLAS threads (the GPU machine allots 16 CPUs to one GPU)
+    threads = min(cores, 16)     # BLAS threads: at most 16, a one-GPU host share of cores
     w = W.get_workload("vit_b16")
     prefixes = tuple(f"blocks.{b}." for b in range(blocks))
     idx = [i for i, t in enumerate(w.tensors) if t.name.startswith(prefixes)]

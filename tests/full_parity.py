@@ -51,7 +51,7 @@ def say(msg: str) -> None:
 
 
 def n_workers() -> int:
-    """The host cores this process may use, at most 16 (a GPU machine's share)."""
+    """The host cores this process may use, at most 16 (a one-GPU host share)."""
     return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
