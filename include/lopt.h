@@ -225,6 +225,61 @@ lopt_status lopt_workspace_bytes(const lopt_handle* h, const lopt_tensor* ts, in
 lopt_status lopt_init_state(lopt_handle* h, const lopt_tensor* ts, int32_t n, void* workspace,
                             size_t ws_bytes, void* stream);
 
+/* Row shards.  The PyLO page ("Benchmark results" > "Distributed optimization
+ * step") distributes the step across GPUs, and lists as future work
+ * ("Limitations and outlook" > "Future directions") a sharded step whose
+ * exchange is only the d_feat feature statistics.  Here each rank binds its
+ * share of every tensor (a 2-D tensor: some of its rows, all of its columns;
+ * a 1-D tensor: some of its elements), and a step runs in three phases with
+ * two sums exchanged (summed over the ranks, e.g. by an all-reduce) between
+ * them: after phase 0, the column sums of g^2 of each 2-D tensor and the sum
+ * of g^2 of each 1-D tensor (the column means and a 1-D tensor's r_k need
+ * every row); after phase 1, per tensor, the sums of the squares of the 28
+ * features and of r_k over the rows (the normalisers and the mean of r_k).
+ * The step's result on every shard is then the whole tensor's step restricted
+ * to the shard's rows or elements.
+ *
+ * global_dims: 2 n values, the (rows, cols) of the whole tensor each list
+ * entry is a shard of.  A whole tensor with rows > 1 is a matrix: its shard
+ * must have cols columns and at most rows rows (one row stays a matrix); a
+ * whole tensor with rows == 1 is 1-D: its shard is 1 x (at most cols).
+ * Rows and cols lie in [1, 2^40]; a matrix has fewer than 2^28 columns.
+ * Errors: as lopt_workspace_bytes / lopt_init_state, and shards that do not
+ * fit global_dims -> INVALID_ARGUMENT. */
+lopt_status lopt_workspace_bytes_sharded(const lopt_handle* h, const lopt_tensor* ts, int32_t n,
+                                         const int64_t* global_dims, size_t* bytes);
+
+/* Binds a list of row shards as lopt_init_state binds a list (state zeroed,
+ * t = 0, the same workspace, stream and error rules), with the exchange
+ * buffers in the workspace.  Such a binding steps with lopt_step_shard only
+ * (lopt_step returns LOPT_ERR_STATE). */
+lopt_status lopt_init_state_sharded(lopt_handle* h, const lopt_tensor* ts, int32_t n, const int64_t* global_dims,
+                                    void* workspace, size_t ws_bytes, void* stream);
+
+/* The exchange buffers of a row-shard binding, device pointers into its
+ * workspace: sums1 (n1 floats: per list entry in order, cols floats for a
+ * matrix shard, 1 for a 1-D shard) and sums2 (n2 = 32 n floats: per entry,
+ * 28 feature sums, 3 sums of r_k, 1 unused).  Every rank's buffers have the
+ * same layout when the ranks bind shards of the same tensors in the same
+ * order.  Errors: NULL argument -> INVALID_ARGUMENT; no row-shard binding ->
+ * STATE. */
+lopt_status lopt_get_shard_sums(const lopt_handle* h, float** sums1, size_t* n1, float** sums2, size_t* n2);
+
+/* One phase of a row-shard step, queued on `stream` (asynchronous):
+ *   phase 0: row and column sums of g^2; writes sums1 (this shard's sums);
+ *   -- the caller replaces sums1 by its sum over the ranks, on the stream --
+ *   phase 1: moving averages (from the summed sums1), statistics pass;
+ *            writes sums2 (this shard's sums);
+ *   -- the caller replaces sums2 by its sum over the ranks --
+ *   phase 2: normalisers from the summed sums2, apply pass; advances t.
+ * Phases run in the order 0, 1, 2, 0, ...; ts as for lopt_step, gradient
+ * pointers read at phase 0 (a change in a later phase is refused).  With one
+ * rank (no exchange) the three phases give lopt_step's result for the whole
+ * tensors, bit for bit.  Errors: no row-shard binding, a phase out of order,
+ * or a different list -> STATE; as lopt_step otherwise.  On error nothing is
+ * queued and the expected phase does not change. */
+lopt_status lopt_step_shard(lopt_handle* h, const lopt_tensor* ts, int32_t n, int32_t phase, void* stream);
+
 /* Bytes of the device array behind lopt_init_state_static, per GPU. */
 #define LOPT_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
 

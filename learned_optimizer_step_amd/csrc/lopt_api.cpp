@@ -81,6 +81,9 @@ struct Plan {
   size_t off_desc = 0, off_grads = 0, off_tiles0 = 0, off_segs1 = 0, off_chunks = 0;
   size_t off_rbar = 0, off_stats = 0, off_scales = 0, off_packed = 0, off_step = 0, off_sync = 0, off_th = 0;
   size_t off_floats = 0;
+  // row shards (lopt_init_state_sharded): the two exchanged buffers
+  bool sharded = false;
+  size_t off_sums1 = 0, n_sums1 = 0, off_sums2 = 0;
   size_t floats = 0;  // per-tensor float arrays (row/col partials, rq, cq)
   size_t total = 0;
   std::vector<lopt_tensor> bound;
@@ -161,9 +164,13 @@ void validate_tensors(const lopt_tensor* ts, int32_t n) {
   }
 }
 
-Plan build_plan(const lopt_tensor* ts, int32_t n) {
+// sharded: a row-shard binding, with global_dims the (rows, cols) of the
+// whole tensor each list entry is a shard of (validated by the caller).
+Plan build_plan(const lopt_tensor* ts, int32_t n, bool sharded = false, const int64_t* global_dims = nullptr) {
   validate_tensors(ts, n);
   Plan pl;
+  pl.sharded = sharded;
+  if (!sharded) global_dims = nullptr;
   pl.bound.assign(ts, ts + n);
   pl.desc.resize(n);
   pl.grads.resize(n);
@@ -183,7 +190,12 @@ Plan build_plan(const lopt_tensor* ts, int32_t n) {
     d.R = int32_t(t.rows);
     d.C = int32_t(t.cols);
     d.n = uint32_t(t.rows * t.cols);
-    d.vec = t.rows == 1;
+    // a shard of a matrix stays a matrix even when it holds one row
+    d.vec = global_dims ? global_dims[2 * ti] == 1 : t.rows == 1;
+    d.Rg = global_dims ? global_dims[2 * ti] : int64_t(d.R);
+    d.ng = global_dims ? global_dims[2 * ti] * global_dims[2 * ti + 1] : int64_t(d.n);
+    d.off_sum1 = int64_t(pl.n_sums1);
+    pl.n_sums1 += d.vec ? 1 : size_t(d.C);
     fastdiv_magic(uint32_t(d.C), &d.cmagic, &d.cshift);
     // host check of the divisor constants at the edges of the index range
     for (uint64_t e : {uint64_t(0), uint64_t(d.C) - 1, uint64_t(d.C), uint64_t(d.n) - 1,
@@ -287,6 +299,10 @@ Plan build_plan(const lopt_tensor* ts, int32_t n) {
   pl.off_sync = take(sizeof(uint32_t) * kSyncWords);
   pl.off_th = take(sizeof(float) * 2 * pl.desc.size());
   pl.off_floats = take(sizeof(float) * pl.floats);
+  if (pl.sharded) {
+    pl.off_sums1 = take(sizeof(float) * pl.n_sums1);
+    pl.off_sums2 = take(sizeof(float) * kStatStride * pl.desc.size());
+  }
   pl.total = off;
   // per-tensor float offsets are relative to the workspace base
   const int64_t base = int64_t(pl.off_floats / sizeof(float));
@@ -334,6 +350,8 @@ struct lopt_handle {
   // scratch array (shared by every handle on that device) and changes between
   // steps are copied from host memory without pinned slots.
   bool static_ws = false;
+  // Row-shard binding: the phase lopt_step_shard runs next (0, 1, 2).
+  int32_t shard_next = 0;
 };
 
 namespace {
@@ -391,6 +409,9 @@ StepCtx make_ctx(const lopt_handle* h) {
   c.packed = reinterpret_cast<float*>(h->ws + pl.off_packed);
   c.step = reinterpret_cast<int64_t*>(h->ws + pl.off_step);
   c.sync = reinterpret_cast<uint32_t*>(h->ws + pl.off_sync);
+  c.sharded = pl.sharded ? 1 : 0;
+  c.sums1 = pl.sharded ? reinterpret_cast<float*>(h->ws + pl.off_sums1) : nullptr;
+  c.sums2 = pl.sharded ? reinterpret_cast<float*>(h->ws + pl.off_sums2) : nullptr;
   c.tensor_hyper = reinterpret_cast<const float*>(h->ws + pl.off_th);
   c.mlp = h->d_mlp;
   c.n_tensors = int32_t(pl.desc.size());
@@ -693,40 +714,134 @@ lopt_status lopt_workspace_bytes(const lopt_handle* h, const lopt_tensor* ts, in
   });
 }
 
+namespace {
+
+// The whole tensors of a row-shard binding: (rows, cols) per list entry; a
+// 2-D shard holds all columns and some rows, a 1-D shard some elements.
+void validate_global_dims(const lopt_tensor* ts, int32_t n, const int64_t* dims) {
+  if (n > 0 && !dims) fail(LOPT_ERR_INVALID_ARGUMENT, "global_dims is NULL");
+  for (int32_t i = 0; i < n; ++i) {
+    const int64_t R = dims[2 * i], C = dims[2 * i + 1];
+    const std::string at = "tensor " + std::to_string(i) + ": ";
+    if (R < 1 || C < 1 || R > (int64_t(1) << 40) || C > (int64_t(1) << 40))
+      fail(LOPT_ERR_INVALID_ARGUMENT, at + "global dims must lie in [1, 2^40]");
+    if (R == 1) {
+      if (ts[i].rows != 1 || ts[i].cols > C)
+        fail(LOPT_ERR_INVALID_ARGUMENT, at + "a shard of a 1-D tensor is 1 x (at most its length)");
+    } else {
+      if (ts[i].cols != C || ts[i].rows > R)
+        fail(LOPT_ERR_INVALID_ARGUMENT, at + "a shard of a matrix holds all of its columns and at most its rows");
+      if (C >= (int64_t(1) << 28)) fail(LOPT_ERR_UNSUPPORTED, at + "matrices must have fewer than 2^28 columns");
+    }
+  }
+}
+
+// Binds a planned list to a workspace (a caller's, or the static scratch):
+// uploads the plan, zeroes the state, resets the step counter.
+void bind_plan(lopt_handle* h, Plan&& pl, char* ws, size_t ws_bytes, bool static_ws, hipStream_t s) {
+  if (!static_ws) reserve_slots(h, pl.bound.size());
+  drain_slots(h);  // a queued copy of the previous binding may still target its workspace
+  const std::vector<int64_t> step0{0};
+  const std::vector<uint32_t> sync0(kSyncWords, 0u);
+  upload(ws, pl.off_desc, pl.desc, s);
+  upload(ws, pl.off_grads, pl.grads, s);
+  upload(ws, pl.off_tiles0, pl.tiles0, s);
+  upload(ws, pl.off_segs1, pl.segs1, s);
+  upload(ws, pl.off_chunks, pl.chunks, s);
+  upload(ws, pl.off_step, step0, s);
+  upload(ws, pl.off_sync, sync0, s);
+  hip_check(hipStreamSynchronize(s), "hipStreamSynchronize(plan upload)");
+  h->plan = std::move(pl);
+  h->ws = ws;
+  h->ws_bytes = ws_bytes;
+  h->bound = true;
+  h->static_ws = static_ws;
+  h->shard_next = 0;
+  set_scratch_owner(h, static_ws);
+  h->th_active = h->th_dirty = false;  // per-tensor values belong to the previous list
+  h->th_lr.clear();
+  h->th_wd.clear();
+  hip_check(launch_zero_state(make_ctx(h), s), "launch(zero state)");
+}
+
+void bind_workspace(lopt_handle* h, Plan&& pl, void* workspace, size_t ws_bytes, void* stream) {
+  if (pl.total > 0 && !workspace) fail(LOPT_ERR_WORKSPACE, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u) fail(LOPT_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < pl.total)
+    fail(LOPT_ERR_WORKSPACE, "workspace too small: need " + std::to_string(pl.total) + " bytes");
+  bind_plan(h, std::move(pl), static_cast<char*>(workspace), ws_bytes, false, static_cast<hipStream_t>(stream));
+}
+
+}  // namespace
+
 lopt_status lopt_init_state(lopt_handle* h, const lopt_tensor* ts, int32_t n, void* workspace, size_t ws_bytes,
                             void* stream) {
   return guarded([&] {
     if (!h) fail(LOPT_ERR_INVALID_ARGUMENT, "handle is NULL");
     check_device(h);
-    Plan pl = build_plan(ts, n);
-    if (pl.total > 0 && !workspace) fail(LOPT_ERR_WORKSPACE, "workspace is NULL");
-    if (reinterpret_cast<uintptr_t>(workspace) & 255u) fail(LOPT_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-    if (ws_bytes < pl.total)
-      fail(LOPT_ERR_WORKSPACE, "workspace too small: need " + std::to_string(pl.total) + " bytes");
+    bind_workspace(h, build_plan(ts, n), workspace, ws_bytes, stream);
+  });
+}
+
+lopt_status lopt_workspace_bytes_sharded(const lopt_handle* h, const lopt_tensor* ts, int32_t n,
+                                         const int64_t* global_dims, size_t* bytes) {
+  return guarded([&] {
+    (void)h;
+    if (!bytes) fail(LOPT_ERR_INVALID_ARGUMENT, "NULL output");
+    validate_tensors(ts, n);
+    validate_global_dims(ts, n, global_dims);
+    *bytes = build_plan(ts, n, true, global_dims).total;
+  });
+}
+
+lopt_status lopt_init_state_sharded(lopt_handle* h, const lopt_tensor* ts, int32_t n, const int64_t* global_dims,
+                                    void* workspace, size_t ws_bytes, void* stream) {
+  return guarded([&] {
+    if (!h) fail(LOPT_ERR_INVALID_ARGUMENT, "handle is NULL");
+    check_device(h);
+    validate_tensors(ts, n);
+    validate_global_dims(ts, n, global_dims);
+    bind_workspace(h, build_plan(ts, n, true, global_dims), workspace, ws_bytes, stream);
+  });
+}
+
+lopt_status lopt_get_shard_sums(const lopt_handle* h, float** sums1, size_t* n1, float** sums2, size_t* n2) {
+  return guarded([&] {
+    if (!h || !sums1 || !n1 || !sums2 || !n2) fail(LOPT_ERR_INVALID_ARGUMENT, "NULL argument");
+    if (!h->bound || !h->plan.sharded) fail(LOPT_ERR_STATE, "no row-shard binding (lopt_init_state_sharded)");
+    check_static_owner(h);
+    *sums1 = reinterpret_cast<float*>(h->ws + h->plan.off_sums1);
+    *n1 = h->plan.n_sums1;
+    *sums2 = reinterpret_cast<float*>(h->ws + h->plan.off_sums2);
+    *n2 = size_t(kStatStride) * h->plan.desc.size();
+  });
+}
+
+lopt_status lopt_step_shard(lopt_handle* h, const lopt_tensor* ts, int32_t n, int32_t phase, void* stream) {
+  return guarded([&] {
+    if (!h) fail(LOPT_ERR_INVALID_ARGUMENT, "handle is NULL");
+    if (!h->bound || !h->plan.sharded) fail(LOPT_ERR_STATE, "no row-shard binding (lopt_init_state_sharded)");
+    if (phase != h->shard_next)
+      fail(LOPT_ERR_STATE, "shard phase " + std::to_string(phase) + " called where phase " +
+                               std::to_string(h->shard_next) + " comes next");
+    bool grads_changed = false;
+    check_same_list(h, ts, n, &grads_changed);
+    check_device(h);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    reserve_slots(h, size_t(n));
-    drain_slots(h);  // a queued copy of the previous binding may still target the old workspace
-    char* ws = static_cast<char*>(workspace);
-    const std::vector<int64_t> step0{0};
-    const std::vector<uint32_t> sync0(kSyncWords, 0u);
-    upload(ws, pl.off_desc, pl.desc, s);
-    upload(ws, pl.off_grads, pl.grads, s);
-    upload(ws, pl.off_tiles0, pl.tiles0, s);
-    upload(ws, pl.off_segs1, pl.segs1, s);
-    upload(ws, pl.off_chunks, pl.chunks, s);
-    upload(ws, pl.off_step, step0, s);
-    upload(ws, pl.off_sync, sync0, s);
-    hip_check(hipStreamSynchronize(s), "hipStreamSynchronize(plan upload)");
-    h->plan = std::move(pl);
-    h->ws = ws;
-    h->ws_bytes = ws_bytes;
-    h->bound = true;
-    h->static_ws = false;
-    set_scratch_owner(h, false);
-    h->th_active = h->th_dirty = false;  // per-tensor values belong to the previous list
-    h->th_lr.clear();
-    h->th_wd.clear();
-    hip_check(launch_zero_state(make_ctx(h), s), "launch(zero state)");
+    const bool pairs_changed = h->th_active && h->th_dirty;
+    if (phase == 0 && (grads_changed || pairs_changed)) {
+      hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+      hip_check(hipStreamIsCapturing(s, &cs), "hipStreamIsCapturing");
+      if (cs != hipStreamCaptureStatusNone)
+        fail(LOPT_ERR_INVALID_ARGUMENT,
+             "gradient pointers or per-tensor hyperparameters changed while the stream is being captured: "
+             "step once with them before capturing");
+      upload_changes(h, ts, n, grads_changed, pairs_changed, s);
+    } else if (phase != 0 && grads_changed) {
+      fail(LOPT_ERR_STATE, "gradient pointers changed between the phases of a step");
+    }
+    hip_check(launch_shard_phase(make_ctx(h), make_params(h), phase, s), "launch(shard phase)");
+    h->shard_next = (phase + 1) % 3;
   });
 }
 
@@ -741,29 +856,7 @@ lopt_status lopt_init_state_static(lopt_handle* h, const lopt_tensor* ts, int32_
                                    ": use lopt_init_state with a workspace");
     void* scratch = nullptr;
     hip_check(scratch_address(h->device, &scratch), "hipGetSymbolAddress(scratch)");
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    drain_slots(h);  // a queued copy of the previous binding may still target its workspace
-    char* ws = static_cast<char*>(scratch);
-    const std::vector<int64_t> step0{0};
-    const std::vector<uint32_t> sync0(kSyncWords, 0u);
-    upload(ws, pl.off_desc, pl.desc, s);
-    upload(ws, pl.off_grads, pl.grads, s);
-    upload(ws, pl.off_tiles0, pl.tiles0, s);
-    upload(ws, pl.off_segs1, pl.segs1, s);
-    upload(ws, pl.off_chunks, pl.chunks, s);
-    upload(ws, pl.off_step, step0, s);
-    upload(ws, pl.off_sync, sync0, s);
-    hip_check(hipStreamSynchronize(s), "hipStreamSynchronize(plan upload)");
-    h->plan = std::move(pl);
-    h->ws = ws;
-    h->ws_bytes = kScratchBytes;
-    h->bound = true;
-    h->static_ws = true;
-    set_scratch_owner(h, true);
-    h->th_active = h->th_dirty = false;
-    h->th_lr.clear();
-    h->th_wd.clear();
-    hip_check(launch_zero_state(make_ctx(h), s), "launch(zero state)");
+    bind_plan(h, std::move(pl), static_cast<char*>(scratch), kScratchBytes, true, static_cast<hipStream_t>(stream));
   });
 }
 
@@ -774,6 +867,9 @@ lopt_status lopt_step(lopt_handle* h, const lopt_tensor* ts, int32_t n, void* st
     check_same_list(h, ts, n, &grads_changed);
     check_static_owner(h);
     check_device(h);
+    if (h->plan.sharded)
+      fail(LOPT_ERR_STATE, "a row-shard binding steps with lopt_step_shard (phases 0, 1, 2 with the exchanges "
+                           "between them)");
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool pairs_changed = h->th_active && h->th_dirty;
     if (grads_changed || pairs_changed) {
@@ -895,7 +991,7 @@ lopt_status lopt_get_tensor_stats(const lopt_handle* h, float* out, int32_t n) {
     for (int32_t i = 0; i < n; ++i) {
       const float* r = rec.data() + size_t(i) * kStatStride;
       float* o = out + size_t(i) * LOPT_STAT_FLOATS;
-      const bool matrix = h->plan.bound[size_t(i)].rows > 1;
+      const bool matrix = !h->plan.desc[size_t(i)].vec;   // a one-row shard of a matrix is a matrix
       for (int f = 0; f < kNF; ++f) {
         const int k = rho_feature(f);
         o[f] = (k < 0 || !matrix) ? r[f] : float(double(r[f]) / double(r[kNF + k]));

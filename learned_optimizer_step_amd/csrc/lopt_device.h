@@ -312,7 +312,7 @@ __device__ __forceinline__ void block_sr(const StepCtx& c, const TensorDesc& d, 
     float s = 0.f;
     for (int q = threadIdx.x; q < d.nrseg; q += kBlock) s += c.rbar_part[(d.rseg0 + q) * 4 + k];
     s = block_sum(s, red);
-    sr[k] = sqrtf(s / float(d.R));
+    sr[k] = sqrtf(s / float(d.Rg));
   }
 }
 

@@ -59,6 +59,12 @@ struct TensorDesc {
   int64_t off_colpart;       // floats: [nrb][C]       (2-D only)
   int64_t off_rq;            // floats: [R][4]  (r_1, r_2, r_3)^(-1/2), 4th unused
   int64_t off_cq;            // floats: [C][4]  (c_1, c_2, c_3)^(-1/2) (2-D only)
+  // The whole tensor this one is a row shard of (lopt_init_state_sharded;
+  // otherwise Rg = R, ng = n): the divisors of the column means, the mean of
+  // r_k and the feature normalisers.
+  int64_t Rg;                // rows (1 for a 1-D tensor)
+  int64_t ng;                // elements
+  int64_t off_sum1;          // first exported sum in StepCtx::sums1 (C of them, 1 for 1-D)
 };
 
 // Row/column sum-of-squares tile.
@@ -141,6 +147,12 @@ struct StepCtx {
   const float* mlp;                  // raw weights (handle-owned)
   int32_t n_tensors, n_tiles0, n_segs1, n_chunks;
   int32_t mlp_impl;                  // lopt_mlp_impl, AUTO resolved: 1 VALU, 2 MFMA, 3 BF16X6, 4 FP16X3, 5 BF16X9, 6 BF16X8
+  // Row shards: 1 when the list's tensors are shards of larger ones whose sums
+  // are exchanged across ranks between the step's phases (sums1: column sums
+  // of g^2, sums2: [n_tensors][32] feature sums and sums of r_k).
+  int32_t sharded;
+  float* sums1;
+  float* sums2;
 };
 
 hipError_t launch_zero_state(const StepCtx& c, hipStream_t s);
@@ -156,6 +168,10 @@ constexpr int kNumKernels = 5;
 // events: nullptr, or kNumKernels + 1 events recorded around the launches.
 hipError_t launch_step(const StepCtx& c, const StepParams& p, hipStream_t s, const hipEvent_t* events);
 hipError_t launch_apply(const StepCtx& c, const StepParams& p, hipStream_t s);
+// The step of a row-shard binding in three phases, with the exchanges between
+// them: row/column sums and the first export; moving averages, statistics
+// pass and the second export; finalize and apply.
+hipError_t launch_shard_phase(const StepCtx& c, const StepParams& p, int phase, hipStream_t s);
 
 // The one-launch step (lopt_single.hip).  Barrier words in the workspace,
 // zero at binding: [0] launch count, [1] release word, [2] fault (a barrier

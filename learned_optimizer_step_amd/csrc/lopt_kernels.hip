@@ -41,6 +41,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
 
 __global__ __launch_bounds__(kBlock) void k_finalize(StepCtx c, StepParams hp) { finalize_block(c, hp, blockIdx.x); }
 
+__global__ __launch_bounds__(kBlock) void k_shard_colsum(StepCtx c) { shard_colsum_block(c, blockIdx.x); }
+
+__global__ __launch_bounds__(kBlock) void k_shard_reduce(StepCtx c) { shard_reduce_block(c, blockIdx.x); }
+
 // ---------------------------------------------------------------------------
 // k_zero_state: zero-fills the state over the chunk list (per-element blocks
 // of each chunk; the first chunk of a tensor also clears r_k and c_k).
@@ -107,6 +111,24 @@ hipError_t launch_step(const StepCtx& c, const StepParams& p, hipStream_t s, con
   if ((e = mark(4)) != hipSuccess) return e;
   if ((e = launch_apply(c, p, s)) != hipSuccess) return e;
   if ((e = mark(5)) != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_shard_phase(const StepCtx& c, const StepParams& p, int phase, hipStream_t s) {
+  if (c.n_tensors == 0) return hipSuccess;
+  if (phase == 0) {
+    hipLaunchKernelGGL(k_rowcol_sumsq, dim3(c.n_tiles0), dim3(kBlock), 0, s, c);
+    hipLaunchKernelGGL(k_shard_colsum, dim3(c.n_segs1), dim3(kBlock), 0, s, c);
+  } else if (phase == 1) {
+    hipLaunchKernelGGL(k_moving_avg, dim3(c.n_segs1), dim3(kBlock), 0, s, c, p);
+    hipLaunchKernelGGL(k_stats, dim3(c.n_chunks), dim3(kBlock), 0, s, c, p);
+    hipLaunchKernelGGL(k_shard_reduce, dim3(c.n_tensors), dim3(kBlock), 0, s, c);
+  } else {
+    hipLaunchKernelGGL(k_finalize, dim3(c.n_tensors + 1), dim3(kBlock), 0, s, c, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_apply(c, p, s);
+  }
   return hipGetLastError();
 }
 

@@ -165,6 +165,28 @@ struct KahanSum {
   }
 };
 
+// Sum of g^2 down column j of a 2-D tensor from its row-block partials: 64
+// columns per segment, 4 thread groups per column over the partials (b =
+// group, group + 4, ...), combined in LDS in group order.  Every thread of the
+// block calls it; the result is valid in group 0 for j < end.
+__device__ __forceinline__ float column_sumsq(const StepCtx& c, const TensorDesc& d, int j, int end,
+                                              float (&part)[kColGroups][kSegCols1]) {
+  const int jl = threadIdx.x % kSegCols1, grp = threadIdx.x / kSegCols1;
+  KahanSum ks;
+  if (j < end)
+    for (int b = grp; b < d.nrb; b += kColGroups) ks.add(c.ws[d.off_colpart + size_t(b) * d.C + j]);
+  part[grp][jl] = ks.s;
+  __syncthreads();
+  return (part[0][jl] + part[1][jl]) + (part[2][jl] + part[3][jl]);
+}
+
+// Sum of g^2 over a 1-D tensor from its flat-tile partials (every thread gets it).
+__device__ __forceinline__ float vector_sumsq(const StepCtx& c, const TensorDesc& d, float* red) {
+  KahanSum ks;
+  for (int w = threadIdx.x; w < d.ncw; w += kBlock) ks.add(c.ws[d.off_rowpart + w]);
+  return block_sum(ks.s, red);
+}
+
 // Moving-average pass (k_moving_avg), one segment: r_k and c_k moving averages (written to the state), their
 // inverse square roots (workspace) and per-segment partial sums of r_k.
 __device__ __forceinline__ void moving_avg_block(const StepCtx& c, const StepParams& hp, uint32_t bid) {
@@ -201,19 +223,16 @@ __device__ __forceinline__ void moving_avg_block(const StepCtx& c, const StepPar
       if (tid == 0) c.rbar_part[sg.slot * 4 + k] = s;
     }
   } else if (sg.kind == kSegCols) {
-    // 64 columns per segment, 4 thread groups per column over the row-block
-    // partials (b = group, group + 4, ...), combined in LDS in group order.
+    // the column's sum of g^2: from this list's row-block partials, or, for a
+    // row shard (c.sharded), over every shard's rows (the exchanged sums)
     __shared__ float part[kColGroups][kSegCols1];
     const int jl = tid % kSegCols1, grp = tid / kSegCols1;
     const int j = sg.a + jl;
-    KahanSum ks;
-    if (j < sg.b)
-      for (int b = grp; b < d.nrb; b += kColGroups) ks.add(ws[d.off_colpart + size_t(b) * d.C + j]);
-    part[grp][jl] = ks.s;
-    __syncthreads();
+    float s;
+    if (c.sharded) s = (grp == 0 && j < sg.b) ? c.sums1[d.off_sum1 + j] : 0.f;
+    else s = column_sumsq(c, d, j, sg.b, part);
     if (grp == 0 && j < sg.b) {
-      const float s = (part[0][jl] + part[1][jl]) + (part[2][jl] + part[3][jl]);
-      const float mean = s / float(d.R);
+      const float mean = s / float(d.Rg);
       float q[3];
 #pragma unroll
       for (int k = 0; k < 3; ++k) {
@@ -223,12 +242,10 @@ __device__ __forceinline__ void moving_avg_block(const StepCtx& c, const StepPar
       }
       reinterpret_cast<float4*>(ws + d.off_cq)[j] = make_float4(q[0], q[1], q[2], 0.f);
     }
-  } else {  // 1-D tensor: r_k is one value per tensor
-    KahanSum ks;
-    for (int w = tid; w < d.ncw; w += kBlock) ks.add(ws[d.off_rowpart + w]);
-    const float s = block_sum(ks.s, red);
+  } else {  // 1-D tensor: r_k is one value per tensor (over every shard's elements)
+    const float s = c.sharded ? c.sums1[d.off_sum1] : vector_sumsq(c, d, red);
     if (tid == 0) {
-      const float mean = s / float(d.C);
+      const float mean = s / float(d.ng);
 #pragma unroll
       for (int k = 0; k < 3; ++k) {
         const float rk = fmaf(hp.beta_f[k], r[k], hp.omb_f[k] * (mean + hp.eps_f));
@@ -309,6 +326,27 @@ __device__ __forceinline__ void stats_block(const StepCtx& c, const StepParams& 
   }
 }
 
+// Per-tensor sums of the statistics pass's chunk partials: each thread adds
+// its chunks in order, then the wave butterfly and the 4 waves in LDS order;
+// lds[w][f] holds wave w's sum of feature f afterwards (after a barrier).
+__device__ __forceinline__ void tensor_feature_sums(const StepCtx& c, const TensorDesc& d, float (&lds)[4][kNF]) {
+  float acc[kNF];
+#pragma unroll
+  for (int f = 0; f < kNF; ++f) acc[f] = 0.f;
+  for (int q = threadIdx.x; q < d.nchunk; q += kBlock) {
+    const float* sp = c.stats_part + size_t(d.chunk0 + q) * kStatStride;
+#pragma unroll
+    for (int f = 0; f < kNF; ++f) acc[f] += sp[f];
+  }
+  const int w = threadIdx.x >> 6;
+#pragma unroll
+  for (int f = 0; f < kNF; ++f) {
+    const float s = wave_sum(acc[f]);
+    if ((threadIdx.x & 63) == 0) lds[w][f] = s;
+  }
+  __syncthreads();
+}
+
 // Packs the MLP for the apply kernel (one block): W1's feature columns, b1
 // with the step features folded in, W2, b2, W3, b3; advances the step counter.
 __device__ __forceinline__ void pack_mlp(const StepCtx& c, const StepParams& hp) {
@@ -364,35 +402,83 @@ __device__ __forceinline__ void finalize_block(const StepCtx& c, const StepParam
   const TensorDesc d = c.desc[t];
   __shared__ float lds[4][kNF];
   __shared__ float red[4];
+  // For a row shard (c.sharded) the sums of r_k over rows and of the squared
+  // features come from the exchange buffer, summed over every shard; a 1-D
+  // tensor's r_k is the same on every shard already.
+  const float* gsum = c.sharded ? c.sums2 + size_t(t) * kStatStride : nullptr;
   float sr[3];
-  block_sr(c, d, sr, red);
-  float acc[kNF];
+  if (gsum && !d.vec) {
 #pragma unroll
-  for (int f = 0; f < kNF; ++f) acc[f] = 0.f;
-  for (int q = threadIdx.x; q < d.nchunk; q += kBlock) {
-    const float* sp = c.stats_part + size_t(d.chunk0 + q) * kStatStride;
-#pragma unroll
-    for (int f = 0; f < kNF; ++f) acc[f] += sp[f];
+    for (int k = 0; k < 3; ++k) sr[k] = sqrtf(gsum[kNF + k] / float(d.Rg));
+  } else {
+    block_sr(c, d, sr, red);
   }
-  const int w = threadIdx.x >> 6;
-#pragma unroll
-  for (int f = 0; f < kNF; ++f) {
-    const float s = wave_sum(acc[f]);
-    if ((threadIdx.x & 63) == 0) lds[w][f] = s;
-  }
-  __syncthreads();
+  if (!gsum) tensor_feature_sums(c, d, lds);
   float* sc = c.scales + size_t(t) * kStatStride;
   if (threadIdx.x < kNF) {
     const int f = threadIdx.x;
     const int k = rho_feature(f);
     // a 1-D tensor's rho_k is c_k^(-1/2) itself (its r_k over their mean is 1)
     const float rb = (k < 0 || d.vec) ? 1.0f : sr[k];
-    const float S = ((lds[0][f] + lds[1][f]) + (lds[2][f] + lds[3][f])) * (rb * rb);
+    const float Sp = gsum ? gsum[f] : (lds[0][f] + lds[1][f]) + (lds[2][f] + lds[3][f]);
+    const float S = Sp * (rb * rb);
     // features the variant does not feed get scale 0 (their weights are 0 too)
-    sc[f] = f < hp.n_feat ? rb / sqrtf(S / float(d.n) + hp.eps_norm) : 0.f;
+    sc[f] = f < hp.n_feat ? rb / sqrtf(S / float(d.ng) + hp.eps_norm) : 0.f;
   } else if (threadIdx.x < kNF + 3) {
     const int k = threadIdx.x - kNF;
     sc[kNF + k] = sr[k];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Row shards (lopt_init_state_sharded): the two sums a shard exports for the
+// exchange across ranks (summed there, then read back by the passes above).
+//
+// First export, after the row/column pass, one moving-average segment: the
+// column sums of g^2 of a 2-D tensor (sums1[off_sum1 + j]) and the sum of g^2
+// of a 1-D tensor (sums1[off_sum1]); a row segment exports nothing (its rows'
+// sums are complete on the shard).
+__device__ __forceinline__ void shard_colsum_block(const StepCtx& c, uint32_t bid) {
+  const Seg1 sg = c.segs1[bid];
+  if (!uni(c.grads[sg.tensor])) return;  // no gradient this step: the tensor is skipped
+  const TensorDesc d = c.desc[sg.tensor];
+  __shared__ float red[4];
+  if (sg.kind == kSegCols) {
+    __shared__ float part[kColGroups][kSegCols1];
+    const int jl = threadIdx.x % kSegCols1, grp = threadIdx.x / kSegCols1;
+    const int j = sg.a + jl;
+    const float s = column_sumsq(c, d, j, sg.b, part);
+    if (grp == 0 && j < sg.b) c.sums1[d.off_sum1 + j] = s;
+  } else if (sg.kind == kSegVec) {
+    const float s = vector_sumsq(c, d, red);
+    if (threadIdx.x == 0) c.sums1[d.off_sum1] = s;
+  }
+}
+
+// Second export, after the statistics pass, one tensor: the sums of the
+// squared features over the shard's chunks (sums2[32 t + d], d < 28) and of
+// r_k over the shard's rows (sums2[32 t + 28 + k]; 0 for a 1-D tensor, whose
+// r_k is not summed across shards), in the finalize pass's order.
+__device__ __forceinline__ void shard_reduce_block(const StepCtx& c, uint32_t bid) {
+  const int t = int(bid);
+  if (!uni(c.grads[t])) return;  // no gradient this step: the tensor is skipped
+  const TensorDesc d = c.desc[t];
+  __shared__ float lds[4][kNF];
+  __shared__ float red[4];
+  float* out = c.sums2 + size_t(t) * kStatStride;
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    float s = 0.f;
+    for (int q = threadIdx.x; q < d.nrseg; q += kBlock) s += c.rbar_part[(d.rseg0 + q) * 4 + k];
+    s = block_sum(s, red);
+    if (threadIdx.x == 0) out[kNF + k] = d.vec ? 0.f : s;
+  }
+  tensor_feature_sums(c, d, lds);
+  if (threadIdx.x < kNF) {
+    const int f = threadIdx.x;
+    out[f] = (lds[0][f] + lds[1][f]) + (lds[2][f] + lds[3][f]);
+  } else if (threadIdx.x == kNF + 3) {
+    out[kNF + 3] = 0.f;
   }
 }
 

@@ -92,6 +92,14 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
         "lopt_init_state_static": (st, [ctypes.c_void_p, ctypes.POINTER(lopt_tensor), ctypes.c_int32, ctypes.c_void_p]),
         "lopt_step": (st, [ctypes.c_void_p, ctypes.POINTER(lopt_tensor), ctypes.c_int32, ctypes.c_void_p]),
+        "lopt_workspace_bytes_sharded": (st, [ctypes.c_void_p, ctypes.POINTER(lopt_tensor), ctypes.c_int32,
+                                              ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t)]),
+        "lopt_init_state_sharded": (st, [ctypes.c_void_p, ctypes.POINTER(lopt_tensor), ctypes.c_int32, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+        "lopt_get_shard_sums": (st, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_size_t),
+                                     ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_size_t)]),
+        "lopt_step_shard": (st, [ctypes.c_void_p, ctypes.POINTER(lopt_tensor), ctypes.c_int32, ctypes.c_int32,
+                                 ctypes.c_void_p]),
         "lopt_get_step": (st, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64)]),
         "lopt_set_step": (st, [ctypes.c_void_p, ctypes.c_int64]),
         "lopt_set_timing_events": (st, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32]),
@@ -175,6 +183,38 @@ def lopt_init_state_static(h, ts: Sequence[lopt_tensor], stream: int) -> None:
 
 def lopt_step(h, ts: Sequence[lopt_tensor], stream: int) -> None:
     _check(load_library().lopt_step(h, tensor_array(ts), len(ts), ctypes.c_void_p(stream)))
+
+
+def _dims_array(global_dims) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(global_dims, dtype=np.int64).reshape(-1))
+
+
+def lopt_workspace_bytes_sharded(h, ts: Sequence[lopt_tensor], global_dims) -> int:
+    """global_dims: (rows, cols) of the whole tensor of each shard."""
+    out = ctypes.c_size_t()
+    dims = _dims_array(global_dims)
+    _check(load_library().lopt_workspace_bytes_sharded(h, tensor_array(ts), len(ts), dims.ctypes.data_as(ctypes.c_void_p),
+                                                       ctypes.byref(out)))
+    return int(out.value)
+
+
+def lopt_init_state_sharded(h, ts: Sequence[lopt_tensor], global_dims, workspace: int, ws_bytes: int,
+                            stream: int) -> None:
+    dims = _dims_array(global_dims)
+    _check(load_library().lopt_init_state_sharded(h, tensor_array(ts), len(ts), dims.ctypes.data_as(ctypes.c_void_p),
+                                                  ctypes.c_void_p(workspace), ws_bytes, ctypes.c_void_p(stream)))
+
+
+def lopt_get_shard_sums(h):
+    """(sums1 device address, floats, sums2 device address, floats)."""
+    p1, p2 = ctypes.c_void_p(), ctypes.c_void_p()
+    n1, n2 = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(load_library().lopt_get_shard_sums(h, ctypes.byref(p1), ctypes.byref(n1), ctypes.byref(p2), ctypes.byref(n2)))
+    return int(p1.value or 0), int(n1.value), int(p2.value or 0), int(n2.value)
+
+
+def lopt_step_shard(h, ts: Sequence[lopt_tensor], phase: int, stream: int) -> None:
+    _check(load_library().lopt_step_shard(h, tensor_array(ts), len(ts), phase, ctypes.c_void_p(stream)))
 
 
 def lopt_get_step(h) -> int:
@@ -287,7 +327,10 @@ class LOpt:
     writes the gradient addresses into it.
     """
 
-    def __init__(self, params, mlp: np.ndarray, cfg: Optional[lopt_config] = None):
+    def __init__(self, params, mlp: np.ndarray, cfg: Optional[lopt_config] = None, global_dims=None):
+        """global_dims: None, or the (rows, cols) of the whole tensor that each
+        parameter is a row shard of (lopt_init_state_sharded); such an
+        optimizer steps with ``step_sharded``."""
         import torch
         self.torch = torch
         self.params = list(params)
@@ -314,15 +357,26 @@ class LOpt:
         with torch.cuda.device(dev):
             self.handle = lopt_create(self.cfg, mlp)
             ws = ctypes.c_size_t()
+            stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
             # gradients are first needed by lopt_step: NULL grad pointers here
-            _check(lib.lopt_workspace_bytes(self.handle, self._table_ptr, n, ctypes.byref(ws)))
+            self.global_dims = None if global_dims is None else _dims_array(global_dims)
+            if self.global_dims is None:
+                _check(lib.lopt_workspace_bytes(self.handle, self._table_ptr, n, ctypes.byref(ws)))
+            else:
+                if len(self.global_dims) != 2 * n:
+                    raise ValueError("global_dims needs (rows, cols) for every parameter")
+                dims = self.global_dims.ctypes.data_as(ctypes.c_void_p)
+                _check(lib.lopt_workspace_bytes_sharded(self.handle, self._table_ptr, n, dims, ctypes.byref(ws)))
             self.ws_bytes = int(ws.value)
             self.workspace = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)
-            _check(lib.lopt_init_state(self.handle, self._table_ptr, n, ctypes.c_void_p(self.workspace.data_ptr()),
-                                       self.ws_bytes, ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)))
+            wsp = ctypes.c_void_p(self.workspace.data_ptr())
+            if self.global_dims is None:
+                _check(lib.lopt_init_state(self.handle, self._table_ptr, n, wsp, self.ws_bytes, stream))
+            else:
+                _check(lib.lopt_init_state_sharded(self.handle, self._table_ptr, n, dims, wsp, self.ws_bytes, stream))
 
-    def step(self, grads) -> None:
-        """One step; grads[i] None skips parameter i (it and its state stay as they are)."""
+    def _set_grads(self, grads) -> int:
+        """Checks the gradients and writes their addresses into the table."""
         grads = list(grads)
         n = len(self.params)
         if len(grads) != n:
@@ -335,9 +389,45 @@ class LOpt:
                                  "on the parameters' device (or None)")
         if n:
             self._table["grad"][:n] = [0 if g is None else g.data_ptr() for g in grads]
+        return n
+
+    def step(self, grads) -> None:
+        """One step; grads[i] None skips parameter i (it and its state stay as they are)."""
+        n = self._set_grads(grads)
+        dev = self.device
         with self.torch.cuda.device(dev):
             _check(load_library().lopt_step(self.handle, self._table_ptr, n,
                                             ctypes.c_void_p(self.torch.cuda.current_stream(dev).cuda_stream)))
+
+    def shard_sums(self):
+        """The two exchange buffers of a row-shard binding as float32 views of
+        the workspace: (column sums of g^2, per-tensor feature sums and sums
+        of r_k)."""
+        p1, n1, p2, n2 = lopt_get_shard_sums(self.handle)
+        base = self.workspace.data_ptr()
+        f = self.workspace.view(self.torch.float32)
+        return f[(p1 - base) // 4:(p1 - base) // 4 + n1], f[(p2 - base) // 4:(p2 - base) // 4 + n2]
+
+    def step_shard_phase(self, phase: int, grads=None) -> None:
+        """Phase 0, 1 or 2 of a row-shard step (lopt_step_shard); the
+        gradients are given with phase 0."""
+        n = self._set_grads(grads) if phase == 0 else len(self.params)
+        with self.torch.cuda.device(self.device):
+            stream = ctypes.c_void_p(self.torch.cuda.current_stream(self.device).cuda_stream)
+            _check(load_library().lopt_step_shard(self.handle, self._table_ptr, n, phase, stream))
+
+    def step_sharded(self, grads, allreduce) -> None:
+        """One step of a row-shard binding: the three phases of lopt_step_shard
+        with allreduce(buf) summing each exchange buffer over the ranks in
+        place (e.g. torch.distributed.all_reduce) between them.  With one
+        rank, allreduce may do nothing."""
+        s1, s2 = self.shard_sums()
+        self.step_shard_phase(0, grads)
+        allreduce(s1)
+        self.step_shard_phase(1)
+        allreduce(s2)
+        self.step_shard_phase(2)
+
 
     @property
     def t(self) -> int:
@@ -375,6 +465,20 @@ class LOpt:
             self.close()
         except Exception:
             pass
+
+
+def allreduce_through_host(group=None):
+    """An in-place sum over the ranks of torch.distributed's default (or given)
+    process group for device buffers, through a host copy: for backends that
+    take host tensors only (gloo).  With RCCL, torch.distributed.all_reduce
+    takes the device buffer directly."""
+    import torch.distributed as dist
+
+    def allreduce(buf):
+        host = buf.cpu()
+        dist.all_reduce(host, group=group)
+        buf.copy_(host)
+    return allreduce
 
 
 def _torch_optimizer_base():

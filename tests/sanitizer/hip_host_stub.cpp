@@ -227,6 +227,30 @@ hipError_t launch_step(const StepCtx& c, const StepParams& p, hipStream_t, const
   if (p.n_feat != kNF && p.n_feat != kVeloNF) return hipErrorInvalidValue;
   return hipSuccess;
 }
+// a row-shard phase: the plan, the exchange buffers inside the workspace
+// (phase 0 writes sums1, phase 1 sums2, phase 2 reads both), then the step's
+// own workspace ranges
+hipError_t launch_shard_phase(const StepCtx& c, const StepParams& p, int phase, hipStream_t s) {
+  REQUIRE(c.sharded == 1 && phase >= 0 && phase <= 2, c.sharded, phase);
+  size_t n1 = 0;
+  for (int32_t t = 0; t < c.n_tensors; ++t) {
+    const TensorDesc& d = c.desc[t];
+    REQUIRE(d.off_sum1 == int64_t(n1), d.off_sum1, n1);
+    REQUIRE(d.Rg >= d.R && d.ng >= d.n, d.Rg, d.ng);
+    n1 += d.vec ? 1 : size_t(d.C);
+  }
+  const char* ws = reinterpret_cast<const char*>(c.ws);
+  const char* a1 = reinterpret_cast<const char*>(c.sums1);
+  const char* a2 = reinterpret_cast<const char*>(c.sums2);
+  REQUIRE(c.n_tensors == 0 || (a1 >= ws && a1 + 4 * n1 <= ws + g_stub_ws_bytes), a1 - ws, n1);
+  REQUIRE(c.n_tensors == 0 || (a2 >= ws && a2 + 4 * size_t(kStatStride) * c.n_tensors <= ws + g_stub_ws_bytes), a2 - ws,
+          c.n_tensors);
+  if (phase == 0) std::memset(c.sums1, 0, 4 * n1);
+  if (phase == 1) std::memset(c.sums2, 0, 4 * size_t(kStatStride) * c.n_tensors);
+  if (phase == 2) return launch_step(c, p, s, nullptr);
+  check_plan(c);
+  return hipSuccess;
+}
 // the one-launch step: 1024 resident blocks, as a 256-CU device at four per CU
 hipError_t single_grid_cap(int device, int impl, int* blocks) {
   if (device != 0 || impl < 1 || impl > 6) return hipErrorInvalidValue;

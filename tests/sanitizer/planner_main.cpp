@@ -122,6 +122,67 @@ void run_list(const std::vector<Shape>& shapes, const std::string& name, int n_f
   std::free(ws);
 }
 
+// A row-shard binding of `shapes`, each the shard of a whole tensor with
+// `factor` times its rows (a 1-D shard: times its length): sizing, binding,
+// two steps of three phases, the exchange buffers, the phase order and the
+// refusal of lopt_step.
+void run_sharded(const std::vector<Shape>& shapes, int64_t factor, const std::string& name) {
+  if (g_failures) return;
+  FakeSpace fs;
+  std::vector<lopt_tensor> ts = make_list(shapes, fs);
+  const int32_t n = int32_t(ts.size());
+  std::vector<int64_t> dims;
+  for (const Shape& sh : shapes) {
+    dims.push_back(sh.first == 1 ? 1 : sh.first * factor);
+    dims.push_back(sh.first == 1 ? sh.second * factor : sh.second);
+  }
+  size_t bytes = 0;
+  expect(lopt_workspace_bytes_sharded(nullptr, ts.data(), n, dims.data(), &bytes) == LOPT_OK, name + ": bytes");
+  void* ws = nullptr;
+  if (posix_memalign(&ws, 256, bytes ? bytes : 1) != 0) {
+    expect(false, name + ": host allocation");
+    return;
+  }
+  g_stub_ws_bytes = bytes;
+  lopt_config cfg;
+  lopt_default_config(&cfg);
+  std::vector<float> mlp(lopt_mlp_floats(cfg.n_feat, cfg.n_time), 0.01f);
+  lopt_handle* h = nullptr;
+  expect(lopt_create(&cfg, mlp.data(), &h) == LOPT_OK, name + ": create");
+  if (!h) {
+    std::free(ws);
+    return;
+  }
+  expect(lopt_init_state_sharded(h, ts.data(), n, dims.data(), ws, bytes, nullptr) == LOPT_OK, name + ": init");
+  float* s1 = nullptr;
+  float* s2 = nullptr;
+  size_t n1 = 0, n2 = 0;
+  expect(lopt_get_shard_sums(h, &s1, &n1, &s2, &n2) == LOPT_OK, name + ": shard sums");
+  size_t want1 = 0;
+  for (const Shape& sh : shapes) want1 += sh.first == 1 ? 1 : size_t(sh.second);
+  expect(n1 == want1 && n2 == 32 * size_t(n), name + ": exchange sizes");
+  expect(lopt_step(h, ts.data(), n, nullptr) == LOPT_ERR_STATE, name + ": lopt_step refused");
+  expect(lopt_step_shard(h, ts.data(), n, 1, nullptr) == LOPT_ERR_STATE, name + ": phase out of order");
+  for (int step = 0; step < 2; ++step)
+    for (int32_t phase = 0; phase < 3; ++phase) {
+      expect(lopt_step_shard(h, ts.data(), n, phase, nullptr) == LOPT_OK, name + ": phase " + std::to_string(phase));
+      if (phase < 2 && n1 + n2 > 0) {  // the exchange: the caller adds the other ranks' sums in place
+        for (size_t q = 0; q < n1; ++q) s1[q] *= float(factor);
+        for (size_t q = 0; q < n2; ++q) s2[q] *= float(factor);
+      }
+    }
+  if (n > 0) {
+    std::vector<lopt_tensor> moved = ts;
+    moved[0].grad = fs.take(4 * uint64_t(ts[0].rows) * uint64_t(ts[0].cols));
+    expect(lopt_step_shard(h, ts.data(), n, 0, nullptr) == LOPT_OK, name + ": phase 0 again");
+    expect(lopt_step_shard(h, moved.data(), n, 1, nullptr) == LOPT_ERR_STATE, name + ": gradients moved mid-step");
+  }
+  int64_t t = -1;
+  expect(lopt_get_step(h, &t) == LOPT_OK && t >= 0, name + ": step counter");
+  lopt_destroy(h);
+  std::free(ws);
+}
+
 // lopt_init_state_static: the same checks on the library's static array (the
 // stand-in holds LOPT_STATIC_SCRATCH_BYTES of host memory), a list too large
 // for it, and a second static binding that takes the array over.
@@ -245,6 +306,9 @@ int main(int argc, char** argv) {
   run_list({{int64_t(1) << 16, (int64_t(1) << 15) - 1}}, "2^16 x (2^15 - 1)", 28);
   run_list({{716064, 2999}, {1, 1}, {2999, 1}}, "716064 x 2999 and small ones", 28);
   run_list({}, "empty list", 28);
+  run_sharded({{16, 64}, {1, 100}, {1, 7}, {300, 5}}, 8, "row shards, one eighth");
+  run_sharded({{1, 2048}, {2, 3}}, 1, "row shards, one rank");
+  run_sharded({}, 4, "row shards, empty list");
   std::mt19937_64 rng(20261202);
   int lists = 6;
   for (int k = 0; k < 150; ++k, ++lists) run_list(random_list(rng), "random list " + std::to_string(k), k % 3 ? 28 : 19);

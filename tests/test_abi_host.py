@@ -216,3 +216,46 @@ def test_matrix_view_of_parameter_shapes():
     assert L.matrix_shape((3, 4)) == (3, 4)
     assert L.matrix_shape((8, 3, 5, 5)) == (8, 75)
     assert L.matrix_shape((2, 1, 1)) == (2, 1)
+
+
+def test_sharded_planning_and_validation_without_device(lib):
+    """Row-shard bindings: workspace size (host-only planning), the global
+    shapes the shards must fit, and the calls that need a binding."""
+    ts = fake_list([(16, 16), (1, 9), (300, 7)])
+    arr = (L.lopt_tensor * 3)(*ts)
+    out = ctypes.c_size_t()
+    assert lib.lopt_workspace_bytes(None, arr, 3, ctypes.byref(out)) == L.LOPT_OK
+    plain = out.value
+    import numpy as np
+    good = np.array([64, 16, 1, 20, 900, 7], dtype=np.int64)       # matrix rows 16 of 64, 9 of 20 elements, ...
+    assert lib.lopt_workspace_bytes_sharded(None, arr, 3, good.ctypes.data_as(ctypes.c_void_p),
+                                            ctypes.byref(out)) == L.LOPT_OK
+    # the exchange buffers: 16 + 1 + 7 column sums, 32 floats per tensor (each 256-byte aligned)
+    assert out.value >= plain + 4 * (16 + 1 + 7) + 4 * 32 * 3
+    bad = [np.array([64, 17, 1, 20, 900, 7], dtype=np.int64),    # other column count
+           np.array([8, 16, 1, 20, 900, 7], dtype=np.int64),     # fewer rows than the shard
+           np.array([64, 16, 1, 5, 900, 7], dtype=np.int64),     # shorter than the 1-D shard
+           np.array([64, 16, 2, 9, 900, 7], dtype=np.int64),     # a 1 x 9 shard of a matrix with 9 columns? rows 2
+           np.array([0, 16, 1, 20, 900, 7], dtype=np.int64)]
+    expect = [L.LOPT_ERR_INVALID_ARGUMENT] * 3 + [L.LOPT_OK, L.LOPT_ERR_INVALID_ARGUMENT]
+    for dims, want in zip(bad, expect):
+        got = lib.lopt_workspace_bytes_sharded(None, arr, 3, dims.ctypes.data_as(ctypes.c_void_p), ctypes.byref(out))
+        assert got == want, (dims, got, L.lopt_last_error())
+    assert lib.lopt_workspace_bytes_sharded(None, arr, 3, None, ctypes.byref(out)) == L.LOPT_ERR_INVALID_ARGUMENT
+    p1, p2 = ctypes.c_void_p(), ctypes.c_void_p()
+    n1, n2 = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.lopt_get_shard_sums(None, ctypes.byref(p1), ctypes.byref(n1), ctypes.byref(p2),
+                                   ctypes.byref(n2)) == L.LOPT_ERR_INVALID_ARGUMENT
+    assert lib.lopt_step_shard(None, arr, 3, 0, None) == L.LOPT_ERR_INVALID_ARGUMENT
+    assert lib.lopt_init_state_sharded(None, arr, 3, good.ctypes.data_as(ctypes.c_void_p), None, 0,
+                                       None) == L.LOPT_ERR_INVALID_ARGUMENT
+
+
+def test_binding_classes_have_their_methods():
+    """The GPU tests use these; a CPU run checks that they exist."""
+    for m in ("step", "t", "set_tensor_hyper", "tensor_stats", "state_views", "close", "shard_sums",
+              "step_shard_phase", "step_sharded"):
+        assert hasattr(L.LOpt, m), m
+    for m in ("step", "state_dict", "load_state_dict", "zero_grad"):
+        assert hasattr(L.LearnedOptimizer, m), m
+    assert callable(L.allreduce_through_host)
