@@ -179,6 +179,10 @@ def main():
                          "under 10 M parameters, where launch latency dominates)")
     ap.add_argument("--peaks", action="store_true",
                     help="also run the machine-figure microbenchmark and include it as measured_peaks")
+    ap.add_argument("--shard-of", type=int, default=1,
+                    help="time rank 0's share of a row-sharded step over this many ranks: its rows of every "
+                         "matrix and its elements of every 1-D tensor, the three phases of lopt_step_shard "
+                         "(the exchanges between them need other GPUs and are not made)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, run one plain 1 GiB device copy (reference for HBM counters)")
     args = ap.parse_args()
@@ -202,13 +206,36 @@ def main():
     w = W.get_workload(args.workload)
     log(f"[bench] {w.key}: {len(w.tensors)} tensors, {w.n_params} params; generating inputs")
     dev = torch.device("cuda:0")
+    ranks = max(1, args.shard_of)
+
+    def shard(x, t):
+        """Rank 0's rows (matrix) or elements (1-D tensor) of t's values."""
+        x = x.reshape(t.rows, t.cols)
+        if t.rows > 1:
+            return np.ascontiguousarray(x[:max(1, t.rows // ranks)])
+        return np.ascontiguousarray(x[:, :max(1, t.cols // ranks)])
+
     params, grads = [], []
     for i, t in enumerate(w.tensors):
-        params.append(torch.from_numpy(W.param_init(w, i).reshape(t.shape)).to(dev))
-        grads.append(torch.from_numpy(W.grad_at(w, i, 1).reshape(t.shape)).to(dev))
+        if ranks > 1:
+            params.append(torch.from_numpy(shard(W.param_init(w, i), t)).to(dev))
+            grads.append(torch.from_numpy(shard(W.grad_at(w, i, 1), t)).to(dev))
+        else:
+            params.append(torch.from_numpy(W.param_init(w, i).reshape(t.shape)).to(dev))
+            grads.append(torch.from_numpy(W.grad_at(w, i, 1).reshape(t.shape)).to(dev))
     mlp = W.mlp_weights(n_feat=args.n_feat)
     opt = L.LOpt(params, mlp, L.config_from(mlp_impl=impl_of[args.impl], n_feat=args.n_feat,
-                                            launch=launch_of[args.launch]))
+                                            launch=launch_of[args.launch]),
+                 global_dims=[(t.rows, t.cols) for t in w.tensors] if ranks > 1 else None)
+    if ranks > 1 and w.prewarm_std is not None:
+        raise SystemExit("--shard-of takes workloads with zero initial state")
+    exchange_floats = [int(b.numel()) for b in opt.shard_sums()] if ranks > 1 else None
+
+    def one_step():
+        if ranks > 1:
+            opt.step_sharded(grads, lambda buf: None)   # one GPU: no other ranks to exchange with
+        else:
+            opt.step(grads)
     if w.prewarm_std is not None:
         for i in range(len(w.tensors)):
             st = W.state_init(w, i)
@@ -216,7 +243,7 @@ def main():
             for k in ("m", "v", "r", "c"):
                 v[k].copy_(torch.from_numpy(st[k]))
     head = name_of[L.lopt_get_mlp_impl(opt.handle)]   # "auto" resolved
-    launch = launch_name[L.lopt_get_launch(opt.handle)]
+    launch = launch_name[L.lopt_get_launch(opt.handle)] if ranks == 1 else "row shard"
     # the initial state, restored before each path is timed
     p0 = [p.clone() for p in params]
     s0 = [s.clone() for s in opt.states]
@@ -228,7 +255,7 @@ def main():
         for s, q in zip(opt.states, s0):
             s.copy_(q)
         L.lopt_set_config(opt.handle, L.config_from(mlp_impl=impl_of[path], n_feat=args.n_feat,
-                                                    launch=launch_of[mode]))
+                                                    launch=launch_of.get(mode, L.LOPT_LAUNCH_AUTO)))
         opt.t = 0    # waits for the device, then resets the step counter
 
     nk = L.LOPT_N_KERNELS
@@ -240,7 +267,7 @@ def main():
         its whole time counts as k_apply's."""
         restore(path, mode)
         for _ in range(warmup):
-            opt.step(grads)
+            one_step()
         events = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(steps)]
         for evs in events:          # torch creates the HIP event on first record
             for e in evs:
@@ -249,7 +276,7 @@ def main():
         t0 = time.perf_counter()
         for k in range(steps):
             L.lopt_set_timing_events(opt.handle, [e.cuda_event for e in events[k]])
-            opt.step(grads)
+            one_step()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         L.lopt_set_timing_events(opt.handle, [])
@@ -283,7 +310,7 @@ def main():
                 "steps": args.steps, "launches_per_step": 1 if mode == "single" else nk}
 
     graph, launches = None, None
-    if args.graph or w.n_params < 10_000_000:
+    if ranks == 1 and (args.graph or w.n_params < 10_000_000):
         log("[bench] graph replay")
         graph = time_graph(launch)
         # the other launch mode, eager and replayed, on the same inputs and initial state
@@ -296,8 +323,8 @@ def main():
                             "launches_per_step": 1 if other == "single" else nk, "graph_replay": time_graph(other)}}
 
     fpe = flop_per_elem(args.n_feat)
-    n = w.n_params
-    n_vec = sum(t.n for t in w.tensors if t.rows == 1)
+    n = sum(int(p.numel()) for p in params)                 # the whole list, or rank 0's share of it
+    n_vec = sum(int(p.numel()) for p, t in zip(params, w.tensors) if t.rows == 1)
 
     side_paths = {}
     if not args.no_fp32_compare:
@@ -343,10 +370,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": (round(value / PAGE_VIT_GPARAMS_PER_S, 3)
-                        if w.key == "vit_b16" and args.n_feat == 28 else None),
+                        if w.key == "vit_b16" and args.n_feat == 28 and ranks == 1 else None),
         "dtype": "f32" if head in ("bf16x8", "bf16x9", "mfma", "valu") else head,
         "data": "synthetic",
-        "config": {"workload": f"{w.key}: {w.description}", "n_params": n, "n_tensors": len(w.tensors),
+        "config": {"workload": f"{w.key}: {w.description}" + (f"; rank 0 of {ranks} row shards" if ranks > 1 else ""),
+                   "n_params": n, "n_tensors": len(w.tensors),
                    "mlp_impl": head, "mlp_arithmetic": PATHS[head][4], "launch": launch,
                    "state": "zero-init, gradients fixed" if w.prewarm_std is None else "pre-warmed, gradients fixed",
                    "variant": "small_fc_lopt" if args.n_feat == 28 else "VeLO-shaped (19 features, 30 inputs)"},
@@ -364,6 +392,11 @@ def main():
     if graph is not None:
         out["graph_replay"] = graph
         out["launch_modes"] = launches
+    if ranks > 1:
+        out["row_shards"] = {"ranks": ranks, "rank": 0, "whole_list_params": w.n_params,
+                             "exchange_floats": exchange_floats,
+                             "exchange_note": "the two in-place sums over the ranks between the phases are not "
+                                              "made on one GPU; the events around the finalize include the gap"}
     out["other_paths"] = side_paths
     for j, name in enumerate(L.KERNEL_NAMES):
         if name in stream_bytes and launch == "split":

@@ -407,7 +407,11 @@ lopt_status lopt_get_tensor_stats(const lopt_handle* h, float* out, int32_t n);
  * stream just before kernel k and events[LOPT_N_KERNELS] after the last one
  * (a one-launch step records events[0..LOPT_N_KERNELS-1] before its kernel
  * and events[LOPT_N_KERNELS] after it, so the whole step counts as the apply
- * kernel's time); n == 0 switches recording off.  The array is copied; the events must stay
+ * kernel's time; a row-shard step records events[0] in phase 0, events[1],
+ * [2], [3] in phase 1 before the moving averages, the statistics pass and the
+ * second export, events[4], [5] around the apply pass in phase 2, so the
+ * exchanges count with the row/column sums and the finalize); n == 0
+ * switches recording off.  The array is copied; the events must stay
  * valid while steps that record them are queued.  Errors: NULL handle, NULL
  * events with n > 0, other n -> INVALID_ARGUMENT. */
 lopt_status lopt_set_timing_events(lopt_handle* h, void* const* events, int32_t n);

@@ -840,7 +840,8 @@ lopt_status lopt_step_shard(lopt_handle* h, const lopt_tensor* ts, int32_t n, in
     } else if (phase != 0 && grads_changed) {
       fail(LOPT_ERR_STATE, "gradient pointers changed between the phases of a step");
     }
-    hip_check(launch_shard_phase(make_ctx(h), make_params(h), phase, s), "launch(shard phase)");
+    hip_check(launch_shard_phase(make_ctx(h), make_params(h), phase, s, h->events.empty() ? nullptr : h->events.data()),
+              "launch(shard phase)");
     h->shard_next = (phase + 1) % 3;
   });
 }

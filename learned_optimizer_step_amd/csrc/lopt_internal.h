@@ -170,8 +170,10 @@ hipError_t launch_step(const StepCtx& c, const StepParams& p, hipStream_t s, con
 hipError_t launch_apply(const StepCtx& c, const StepParams& p, hipStream_t s);
 // The step of a row-shard binding in three phases, with the exchanges between
 // them: row/column sums and the first export; moving averages, statistics
-// pass and the second export; finalize and apply.
-hipError_t launch_shard_phase(const StepCtx& c, const StepParams& p, int phase, hipStream_t s);
+// pass and the second export; finalize and apply.  events as launch_step's:
+// [0] before phase 0, [1] [2] [3] before the moving averages, the statistics
+// pass and the second export, [4] [5] around the apply pass.
+hipError_t launch_shard_phase(const StepCtx& c, const StepParams& p, int phase, hipStream_t s, const hipEvent_t* events);
 
 // The one-launch step (lopt_single.hip).  Barrier words in the workspace,
 // zero at binding: [0] launch count, [1] release word, [2] fault (a barrier

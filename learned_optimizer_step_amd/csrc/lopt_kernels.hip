@@ -114,20 +114,27 @@ hipError_t launch_step(const StepCtx& c, const StepParams& p, hipStream_t s, con
   return hipGetLastError();
 }
 
-hipError_t launch_shard_phase(const StepCtx& c, const StepParams& p, int phase, hipStream_t s) {
+hipError_t launch_shard_phase(const StepCtx& c, const StepParams& p, int phase, hipStream_t s, const hipEvent_t* ev) {
   if (c.n_tensors == 0) return hipSuccess;
+  auto mark = [&](int k) -> hipError_t { return ev ? hipEventRecord(ev[k], s) : hipSuccess; };
+  hipError_t e;
   if (phase == 0) {
+    if ((e = mark(0)) != hipSuccess) return e;
     hipLaunchKernelGGL(k_rowcol_sumsq, dim3(c.n_tiles0), dim3(kBlock), 0, s, c);
     hipLaunchKernelGGL(k_shard_colsum, dim3(c.n_segs1), dim3(kBlock), 0, s, c);
   } else if (phase == 1) {
+    if ((e = mark(1)) != hipSuccess) return e;
     hipLaunchKernelGGL(k_moving_avg, dim3(c.n_segs1), dim3(kBlock), 0, s, c, p);
+    if ((e = mark(2)) != hipSuccess) return e;
     hipLaunchKernelGGL(k_stats, dim3(c.n_chunks), dim3(kBlock), 0, s, c, p);
+    if ((e = mark(3)) != hipSuccess) return e;
     hipLaunchKernelGGL(k_shard_reduce, dim3(c.n_tensors), dim3(kBlock), 0, s, c);
   } else {
     hipLaunchKernelGGL(k_finalize, dim3(c.n_tensors + 1), dim3(kBlock), 0, s, c, p);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return launch_apply(c, p, s);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = mark(4)) != hipSuccess) return e;
+    if ((e = launch_apply(c, p, s)) != hipSuccess) return e;
+    if ((e = mark(5)) != hipSuccess) return e;
   }
   return hipGetLastError();
 }

@@ -230,7 +230,7 @@ hipError_t launch_step(const StepCtx& c, const StepParams& p, hipStream_t, const
 // a row-shard phase: the plan, the exchange buffers inside the workspace
 // (phase 0 writes sums1, phase 1 sums2, phase 2 reads both), then the step's
 // own workspace ranges
-hipError_t launch_shard_phase(const StepCtx& c, const StepParams& p, int phase, hipStream_t s) {
+hipError_t launch_shard_phase(const StepCtx& c, const StepParams& p, int phase, hipStream_t s, const hipEvent_t*) {
   REQUIRE(c.sharded == 1 && phase >= 0 && phase <= 2, c.sharded, phase);
   size_t n1 = 0;
   for (int32_t t = 0; t < c.n_tensors; ++t) {
