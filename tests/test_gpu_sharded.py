@@ -42,8 +42,9 @@ class Shards:
             self.params.append(ps)
             self.opts.append(L.LOpt(ps, mlp, cfg, global_dims=dims))
 
-    def step(self, t):
-        grads = [[torch.from_numpy(take(W.grad_at(self.w, i, t), tt, *self.cut[k][i])).cuda()
+    def step(self, t, skip=()):
+        """Step t; the tensors in skip have no gradient in it (on every shard)."""
+        grads = [[None if i in skip else torch.from_numpy(take(W.grad_at(self.w, i, t), tt, *self.cut[k][i])).cuda()
                   for i, tt in enumerate(self.w.tensors)] for k in range(self.ranks)]
         sums = [o.shard_sums() for o in self.opts]
         for phase in range(3):
@@ -101,6 +102,42 @@ def test_shards_equal_the_oracle_on_the_whole_tensors(ranks, impl, n_feat):
         for k, o in enumerate(sh.opts):   # every shard normalised with the whole tensor's statistics
             errs += compare_stats(o.tensor_stats()[i], want[i], n_feat, f"{label} shard {k}")
     assert all(o.t == steps for o in sh.opts)
+    sh.close()
+    assert not errs, "\n".join(errs[:20])
+
+
+def test_shards_with_per_tensor_values_and_skipped_gradients():
+    """Per-tensor learning rates and weight decays (the same on every shard),
+    and a tensor without a gradient in one step, against the oracle with the
+    same values and the same skip."""
+    steps = 4
+    w = W.custom_workload("sharded", SHAPES, grad_std=1e-2, steps=steps, wid=180)
+    cfg = L.config_from()
+    mlp = W.mlp_weights(11, bias_std=0.1)
+    th = [(0.5 + 0.1 * i, 0.01 * (i % 3)) for i in range(len(SHAPES))]
+    sh = Shards(w, 2, cfg, mlp)
+    for o in sh.opts:
+        o.set_tensor_hyper([a for a, _ in th], [b for _, b in th])
+    skip_step, skipped = 3, 4
+    for t in range(1, steps + 1):
+        sh.step(t, skip=(skipped,) if t == skip_step else ())
+    torch.cuda.synchronize()
+    # the oracle: tensor `skipped` takes steps 1, 2 and 4 (t still counts 1, 2, 4), the others all four
+    want = oracle_run(w, mlp, hyper_from_cfg(cfg), steps, tensor_hyper=th)
+    errs = []
+    for i, t in enumerate(w.tensors):
+        if i == skipped:
+            continue
+        errs += compare(sh.gather(i), want[i], f"per-tensor[{i}]")
+    import dataclasses
+    import oracle
+    hp = dataclasses.replace(hyper_from_cfg(cfg).as_f32(), lr=float(np.float32(th[skipped][0])),
+                             weight_decay=float(np.float32(th[skipped][1])))
+    m = oracle.unpack_mlp(mlp, hp.n_time, hp.n_feat)
+    p, st = W.param_init(w, skipped), W.state_init(w, skipped)
+    for t in (1, 2, 4):
+        p, st, _ = oracle.step_tensor(p, W.grad_at(w, skipped, t), st, t, m, hp)
+    errs += compare(sh.gather(skipped), dict(p=p, **st), f"skipped[{skipped}]")
     sh.close()
     assert not errs, "\n".join(errs[:20])
 
