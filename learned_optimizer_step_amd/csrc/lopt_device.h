@@ -303,18 +303,4 @@ __device__ __forceinline__ void store_param(const Streams& s, uint32_t e, float 
   stb(s.p, (e - s.e0) * 4u, p_new);
 }
 
-// sqrt(mean_i r_k[i]) from the per-segment partial sums of r_k, summed by the
-// whole block in a fixed order (every caller gets bitwise the same value).
-// All threads must call it (it contains barriers); a 1-D tensor gets sqrt(r_k).
-__device__ __forceinline__ void block_sr(const StepCtx& c, const TensorDesc& d, float sr[3], float* red) {
-#pragma unroll
-  for (int k = 0; k < 3; ++k) {
-    float s = 0.f;
-    for (int q = threadIdx.x; q < d.nrseg; q += kBlock) s += c.rbar_part[(d.rseg0 + q) * 4 + k];
-    s = block_sum(s, red);
-    sr[k] = sqrtf(s / float(d.Rg));
-  }
-}
-
-
 }  // namespace lopt

@@ -326,11 +326,26 @@ __device__ __forceinline__ void stats_block(const StepCtx& c, const StepParams& 
   }
 }
 
-// Per-tensor sums of the statistics pass's chunk partials: each thread adds
-// its chunks in order, then the wave butterfly and the 4 waves in LDS order;
-// lds[w][f] holds wave w's sum of feature f afterwards (after a barrier).
-__device__ __forceinline__ void tensor_feature_sums(const StepCtx& c, const TensorDesc& d, float (&lds)[4][kNF]) {
-  float acc[kNF];
+// sqrt(mean_i r_k[i]) from the per-segment partial sums of r_k, summed by the
+// whole block in a fixed order (every caller gets bitwise the same value).
+// All threads must call it (it contains barriers); a 1-D tensor gets sqrt(r_k).
+__device__ __forceinline__ void block_sr(const StepCtx& c, const TensorDesc& d, float sr[3], float* red) {
+  // every thread's loads first (one round trip), then the three block sums
+  float s[3] = {0.f, 0.f, 0.f};
+  for (int q = threadIdx.x; q < d.nrseg; q += kBlock) {
+#pragma unroll
+    for (int k = 0; k < 3; ++k) s[k] += c.rbar_part[(d.rseg0 + q) * 4 + k];
+  }
+#pragma unroll
+  for (int k = 0; k < 3; ++k) sr[k] = sqrtf(block_sum(s[k], red) / float(d.Rg));
+}
+
+// Per-tensor sums of the statistics pass's chunk partials, in two parts so
+// that a caller can issue other loads between them: each thread adds its
+// chunks in order (chunk_partials), then the wave butterfly and the 4 waves
+// in LDS order (feature_wave_sums: lds[w][f] holds wave w's sum of feature f
+// after its barrier).
+__device__ __forceinline__ void chunk_partials(const StepCtx& c, const TensorDesc& d, float (&acc)[kNF]) {
 #pragma unroll
   for (int f = 0; f < kNF; ++f) acc[f] = 0.f;
   for (int q = threadIdx.x; q < d.nchunk; q += kBlock) {
@@ -338,6 +353,9 @@ __device__ __forceinline__ void tensor_feature_sums(const StepCtx& c, const Tens
 #pragma unroll
     for (int f = 0; f < kNF; ++f) acc[f] += sp[f];
   }
+}
+
+__device__ __forceinline__ void feature_wave_sums(const float (&acc)[kNF], float (&lds)[4][kNF]) {
   const int w = threadIdx.x >> 6;
 #pragma unroll
   for (int f = 0; f < kNF; ++f) {
@@ -364,14 +382,18 @@ __device__ __forceinline__ void pack_mlp(const StepCtx& c, const StepParams& hp)
   const float* W3 = b2 + kH;
   const float* b3 = W3 + 2 * kH;
   float* pk = c.packed;
+  // the step features tanh(t / tau_s), one per thread, shared through LDS
+  __shared__ float tfeat[kMaxTime];
+  if (threadIdx.x < hp.n_time) tfeat[threadIdx.x] = tanhf(tf / hp.timescales[threadIdx.x]);
   for (int q = threadIdx.x; q < kH * kNF; q += kBlock) {
     const int o = q / kNF, f = q - o * kNF;
     pk[kPkW1 + q] = f < nf ? W1[o * din + f] : 0.f;
   }
+  __syncthreads();
   if (threadIdx.x < kH) {
     const int o = threadIdx.x;
     float b = b1[o];
-    for (int s = 0; s < hp.n_time; ++s) b = fmaf(W1[o * din + nf + s], tanhf(tf / hp.timescales[s]), b);
+    for (int s = 0; s < hp.n_time; ++s) b = fmaf(W1[o * din + nf + s], tfeat[s], b);
     pk[kPkB1 + o] = b;
     pk[kPkB2 + o] = b2[o];
     pk[kPkW3 + o] = W3[o];
@@ -407,13 +429,15 @@ __device__ __forceinline__ void finalize_block(const StepCtx& c, const StepParam
   // tensor's r_k is the same on every shard already.
   const float* gsum = c.sharded ? c.sums2 + size_t(t) * kStatStride : nullptr;
   float sr[3];
+  float acc[kNF];
+  if (!gsum) chunk_partials(c, d, acc);   // its loads go out with block_sr's
   if (gsum && !d.vec) {
 #pragma unroll
     for (int k = 0; k < 3; ++k) sr[k] = sqrtf(gsum[kNF + k] / float(d.Rg));
   } else {
     block_sr(c, d, sr, red);
   }
-  if (!gsum) tensor_feature_sums(c, d, lds);
+  if (!gsum) feature_wave_sums(acc, lds);
   float* sc = c.scales + size_t(t) * kStatStride;
   if (threadIdx.x < kNF) {
     const int f = threadIdx.x;
@@ -466,14 +490,19 @@ __device__ __forceinline__ void shard_reduce_block(const StepCtx& c, uint32_t bi
   __shared__ float lds[4][kNF];
   __shared__ float red[4];
   float* out = c.sums2 + size_t(t) * kStatStride;
+  float acc[kNF];
+  chunk_partials(c, d, acc);
+  float s[3] = {0.f, 0.f, 0.f};   // block_sr's sums, without the root
+  for (int q = threadIdx.x; q < d.nrseg; q += kBlock) {
+#pragma unroll
+    for (int k = 0; k < 3; ++k) s[k] += c.rbar_part[(d.rseg0 + q) * 4 + k];
+  }
 #pragma unroll
   for (int k = 0; k < 3; ++k) {
-    float s = 0.f;
-    for (int q = threadIdx.x; q < d.nrseg; q += kBlock) s += c.rbar_part[(d.rseg0 + q) * 4 + k];
-    s = block_sum(s, red);
-    if (threadIdx.x == 0) out[kNF + k] = d.vec ? 0.f : s;
+    const float v = block_sum(s[k], red);
+    if (threadIdx.x == 0) out[kNF + k] = d.vec ? 0.f : v;
   }
-  tensor_feature_sums(c, d, lds);
+  feature_wave_sums(acc, lds);
   if (threadIdx.x < kNF) {
     const int f = threadIdx.x;
     out[f] = (lds[0][f] + lds[1][f]) + (lds[2][f] + lds[3][f]);
