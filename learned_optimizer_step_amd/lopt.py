@@ -12,7 +12,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from typing import List, Optional, Sequence
+from typing import Optional, Sequence
 
 import numpy as np
 
@@ -427,7 +427,6 @@ class LOpt:
         self.step_shard_phase(1)
         allreduce(s2)
         self.step_shard_phase(2)
-
 
     @property
     def t(self) -> int:

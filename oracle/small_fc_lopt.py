@@ -68,8 +68,8 @@ computes in fp64 and rounds the returned state and parameters to fp32 once.
 """
 from __future__ import annotations
 
-from dataclasses import dataclass, field, replace
-from typing import List, Optional, Sequence, Tuple
+from dataclasses import dataclass, replace
+from typing import Optional, Sequence, Tuple
 
 import numpy as np
 

@@ -1,7 +1,7 @@
 """Helpers shared by the oracle tests (test-side only)."""
 import numpy as np
 
-from oracle import Hyper, pack_mlp, unpack_mlp, Mlp, mlp_size
+from oracle import pack_mlp, unpack_mlp, Mlp
 
 
 def rng(seed):

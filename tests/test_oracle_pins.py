@@ -9,7 +9,7 @@ import math
 import numpy as np
 import pytest
 
-from oracle import (Hyper, Mlp, accumulate, cross_index, pack_mlp, step, step_tensor, unpack_mlp,
+from oracle import (Hyper, Mlp, accumulate, cross_index, pack_mlp, step, step_tensor,
                     zero_state)
 from oracle_helpers import magnitude_selector_mlp, random_case, random_mlp, rng, selector_mlp
 

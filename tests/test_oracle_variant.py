@@ -4,13 +4,11 @@ plus 11 step features: the d_feat of about 30 that the PyLO page gives VeLO in
 closed forms on a constant rank-1 gradient through selector networks, the
 unit-mean-square invariant, an independent MLP implementation and the
 scalar-loop twin."""
-import math
-import types
 
 import numpy as np
 import pytest
 
-from oracle import Hyper, Mlp, VELO_FEATURES, mlp_size, pack_mlp, step, step_tensor, unpack_mlp, zero_state
+from oracle import Hyper, Mlp, VELO_FEATURES, mlp_size, pack_mlp, step, step_tensor, unpack_mlp
 from oracle.scalar_twin import twin_step, unpack as twin_unpack
 from oracle_helpers import random_case, rng
 from test_oracle_pins import F64, f64_state, rank1, rank1_expected_inputs

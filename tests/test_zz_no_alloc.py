@@ -11,7 +11,6 @@ Then: the first handle's binding was replaced by the second's, so its step is
 refused with LOPT_ERR_STATE until it binds again, and a list whose workspace
 exceeds LOPT_STATIC_SCRATCH_BYTES is refused with LOPT_ERR_WORKSPACE.
 """
-import ctypes
 
 import numpy as np
 import pytest
