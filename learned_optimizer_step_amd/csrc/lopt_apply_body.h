@@ -342,12 +342,29 @@ __device__ __forceinline__ void split3_x8(const float (&x)[8], u32x4 (&bt)[3]) {
   for (int j = 0; j < 4; ++j) {
     const Pieces u0 = split3(x[2 * j]), u1 = split3(x[2 * j + 1]);
 #pragma unroll
-    for (int p = 0; p < 3; ++p) bt[p][j] = pack2(piece(u0, p), piece(u1, p));
+    for (int p = 0; p < 3; ++p)   // a zero low value: the high value's upper half, the split's own mask
+      bt[p][j] = (__builtin_constant_p(x[2 * j]) && x[2 * j] == 0.f) ? __float_as_uint(piece(u1, p)) & 0xffff0000u
+                                                                     : pack2(piece(u0, p), piece(u1, p));
   }
 }
 
-// Layer-1 entries: feature of entry q (q < 30), -1 = zero.
+// Layer-1 entries: feature of entry q (q < 30), -1 = zero.  Entry q sits at
+// K-step (q/2)/8, position (q/2)%8, lane half q%2, so a lane's bf16 pair j
+// holds entries 4j + h (low) and 4j + 2 + h (high) for lane half h.  The
+// features fill the entries in order, except that a last group of one or two
+// features moves up by two entries, into the high halves of its pairs: a pair
+// whose low entry is zero packs its value's pieces with the masks the split
+// already takes (split3_x8).
 __device__ constexpr int x6_feature(int q, int nf, bool ru) {
+  const int n = ru ? nf - 3 : nf;   // entries that carry a feature
+  const int g = n & ~3, r = n & 3;
+  if (r == 1 || r == 2) {
+    if (q >= g && q < g + 2) return -1;
+    if (q >= g + 2 && q < g + 2 + r)
+      q -= 2;
+    else if (q >= g + 2 + r)
+      return -1;
+  }
   for (int f = 0; f < nf; ++f) {
     if (ru && f >= 13 && f < 16) continue;
     if (q == 0) return f;
@@ -355,9 +372,14 @@ __device__ constexpr int x6_feature(int q, int nf, bool ru) {
   }
   return -1;
 }
-// entry q sits at K-step (q/2)/8, position (q/2)%8, lane half q%2
-static_assert(x6_feature(24, kNF, true) == 27 && x6_feature(25, kNF, true) == -1 && x6_feature(27, kNF, false) == 27 &&
-                  x6_feature(13, kNF, true) == 16 && x6_feature(16, kVeloNF, true) == -1,
+static_assert(x6_feature(23, kNF, true) == 26 && x6_feature(24, kNF, true) == -1 && x6_feature(25, kNF, true) == -1 &&
+                  x6_feature(26, kNF, true) == 27 && x6_feature(27, kNF, true) == -1 &&
+                  x6_feature(29, kNF, true) == -1 && x6_feature(27, kNF, false) == 27 &&
+                  x6_feature(13, kNF, true) == 16 && x6_feature(16, kVeloNF, true) == -1 &&
+                  x6_feature(18, kVeloNF, false) == 18 &&
+                  // K-step 1, position 6 (entries 28, 29) is zero on every variant (apply_x6_body's kc1)
+                  x6_feature(28, kNF, true) == -1 && x6_feature(29, kNF, false) == -1 &&
+                  x6_feature(28, kVeloNF, true) == -1 && x6_feature(29, kVeloNF, false) == -1,
               "bf16x6 layer-1 entries");
 
 // (A piece, B piece) of product t of NP (9, 8 or 6), smallest terms first:
@@ -382,7 +404,7 @@ struct X6Lds {
   float4 tab[3][2][4];  // {b2, W3 dir, W3 mag} x half x 16 floats
 };
 
-template <int NP, bool VEC, bool NORMAL, int NF, bool RU>
+template <int NP, bool VEC, bool NORMAL, int NF, bool RU, bool KREG>
 __device__ __forceinline__ void apply_x6_body(const StepCtx& c, const StepParams& hp, const Chunk& ch,
                                               const TensorDesc& d, const float* g, X6Lds& L) {
   const int lane = threadIdx.x & 63;
@@ -451,6 +473,14 @@ __device__ __forceinline__ void apply_x6_body(const StepCtx& c, const StepParams
   update_constants(c, hp, ch, decay, lr_step);
   uint32_t base = ch.e0 + wave * 64;
   if (base >= ch.e1) return;
+  // K-step 1's last pair (positions 6 and 7) is always (0, 1): pieces
+  // (1.0's upper half in the high half, 0, 0).  KREG holds it in a register
+  // the compiler cannot see through: as a constant, each B operand holding it
+  // was built by copying a four-register constant and overwriting three of
+  // them (10 vector instructions per 64 elements).  The one-launch kernel,
+  // whose other passes share the register budget, keeps the constant.
+  uint32_t kc1[3] = {0x3f800000u, 0u, 0u};
+  if constexpr (KREG) asm volatile("" : "+v"(kc1[0]));
   for (; base < ch.e1; base += kBlock) {
     const uint32_t e = base + lane;
     const bool valid = e < ch.e1;
@@ -512,6 +542,10 @@ __device__ __forceinline__ void apply_x6_body(const StepCtx& c, const StepParams
       for (int b = 0; b < 2; ++b) {
         u32x4 bt[3];
         split3_x8(v[b][k], bt);
+        if (k == 1) {
+#pragma unroll
+          for (int p = 0; p < 3; ++p) bt[p][3] = kc1[p];
+        }
 #pragma unroll
         for (int t = 0; t < NP; ++t)
           acc1s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a[xp_a(NP, t)]), as_bf16x8(bt[xp_b(NP, t)]),
@@ -567,7 +601,7 @@ __device__ __forceinline__ void apply_x6_body(const StepCtx& c, const StepParams
   }
 }
 
-template <int NP>
+template <int NP, bool KREG>
 __device__ __forceinline__ void apply_bf16_block(const StepCtx& c, const StepParams& hp, uint32_t bid) {
   Chunk ch;
   TensorDesc d;
@@ -577,7 +611,7 @@ __device__ __forceinline__ void apply_bf16_block(const StepCtx& c, const StepPar
   __shared__ X6Lds lds;
   dispatch_variant<true>(d, hp, [&](auto v) {
     using V = decltype(v);
-    apply_x6_body<NP, V::vec, V::normal, V::nf, V::rowuni>(c, hp, ch, d, g, lds);
+    apply_x6_body<NP, V::vec, V::normal, V::nf, V::rowuni, KREG>(c, hp, ch, d, g, lds);
   });
 }
 
@@ -864,14 +898,15 @@ __device__ __forceinline__ void apply_fp16x3_block(const StepCtx& c, const StepP
 // ---------------------------------------------------------------------------
 // One chunk of the apply pass on MLP path IMPL (lopt_mlp_impl numbering:
 // 1 VALU, 2 fp32 matrix cores, 3 bf16x6, 4 fp16x3, 5 bf16x9, 6 bf16x8).
-template <int IMPL>
+// KREG: see apply_x6_body (false in the one-launch kernel).
+template <int IMPL, bool KREG = true>
 __device__ __forceinline__ void apply_block(const StepCtx& c, const StepParams& hp, uint32_t bid) {
   if constexpr (IMPL == 1) apply_valu_block(c, hp, bid);
   else if constexpr (IMPL == 2) apply_mfma_block(c, hp, bid);
-  else if constexpr (IMPL == 3) apply_bf16_block<6>(c, hp, bid);
+  else if constexpr (IMPL == 3) apply_bf16_block<6, KREG>(c, hp, bid);
   else if constexpr (IMPL == 4) apply_fp16x3_block(c, hp, bid);
-  else if constexpr (IMPL == 5) apply_bf16_block<9>(c, hp, bid);
-  else apply_bf16_block<8>(c, hp, bid);
+  else if constexpr (IMPL == 5) apply_bf16_block<9, KREG>(c, hp, bid);
+  else apply_bf16_block<8, KREG>(c, hp, bid);
 }
 
 }  // namespace lopt

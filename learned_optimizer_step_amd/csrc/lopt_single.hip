@@ -114,7 +114,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
   grid_sync(sync, id0 + 3u, G);
   if (blockIdx.x == 0 && threadIdx.x == 0) __hip_atomic_store(sync, epoch + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   for (uint32_t b = blockIdx.x; b < uint32_t(c.n_chunks); b += G) {
-    apply_block<IMPL>(c, hp, b);
+    apply_block<IMPL, false>(c, hp, b);
     __syncthreads();
   }
 }
