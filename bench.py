@@ -187,8 +187,8 @@ def main():
                     help="after the timed steps, run one plain 1 GiB device copy (reference for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the library has no "
-              f"multi-GPU path", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); for one rank's share of a "
+              f"row-sharded step across W GPUs use --shard-of W", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
