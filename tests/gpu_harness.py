@@ -41,7 +41,7 @@ def to_matrix_state(st: dict) -> dict:
     return {k: np.asarray(v, dtype=np.float32) for k, v in st.items()}
 
 
-class GpuRun:
+class DeviceRun:
     """A workload on the GPU through LOpt; inputs from the seeded generator."""
 
     def __init__(self, w: W.Workload, mlp: np.ndarray, cfg, torch):
@@ -152,7 +152,7 @@ def parity(w: W.Workload, mlp: np.ndarray, cfg, torch, steps: Optional[int] = No
     steps = w.steps if steps is None else steps
     say(f"[parity] {w.key}: {len(w.tensors)} tensors, {w.n_params} params, {steps} steps, impl={cfg.mlp_impl}"
         + (", per-tensor lr/wd" if tensor_hyper is not None else ""))
-    run = GpuRun(w, mlp, cfg, torch)
+    run = DeviceRun(w, mlp, cfg, torch)
     if tensor_hyper is not None:
         run.opt.set_tensor_hyper([a for a, _ in tensor_hyper], [b for _, b in tensor_hyper])
     for t in range(1, steps + 1):
@@ -176,7 +176,7 @@ def parity_one_step_rows(w: W.Workload, mlp: np.ndarray, cfg, torch, picks) -> L
     per-tensor sums always cover the whole tensor, the update is compared on
     the listed rows."""
     say(f"[parity-rows] {w.key}: {len(w.tensors)} tensors, {w.n_params} params, 1 step, impl={cfg.mlp_impl}")
-    run = GpuRun(w, mlp, cfg, torch)
+    run = DeviceRun(w, mlp, cfg, torch)
     run.step(1)
     got = {i: run.fetch(i) for i in picks}
     run.close()

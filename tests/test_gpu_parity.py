@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_harness import IMPLS, GpuRun, compare, hyper_from_cfg, oracle_run, parity, parity_one_step_rows, say
+from gpu_harness import IMPLS, DeviceRun, compare, hyper_from_cfg, oracle_run, parity, parity_one_step_rows, say
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -111,7 +111,7 @@ def test_update_accuracy_of_each_mlp_path():
             off += r.size
         got = {}
         for impl in IMPLS:
-            run = GpuRun(w, weights, L.config_from(mlp_impl=impl), torch)
+            run = DeviceRun(w, weights, L.config_from(mlp_impl=impl), torch)
             run.step(1)
             got[impl] = np.concatenate([np.asarray(run.fetch(i)["p"], np.float64).ravel()
                                         for i in range(len(shapes))])
@@ -148,7 +148,7 @@ def test_auto_runs_bf16x8():
     for mlp in (weights, big):
         out = {}
         for impl in (L.LOPT_MLP_AUTO, L.LOPT_MLP_BF16X8):
-            run = GpuRun(w, mlp, L.config_from(mlp_impl=impl), torch)
+            run = DeviceRun(w, mlp, L.config_from(mlp_impl=impl), torch)
             assert L.lopt_get_mlp_impl(run.opt.handle) == L.LOPT_MLP_BF16X8
             for t in (1, 2):
                 run.step(t)
@@ -226,7 +226,7 @@ def sample_rows(R, k, seed):
 
 
 def _run_states(w, cfg, steps, m):
-    run = GpuRun(w, m, cfg, torch)
+    run = DeviceRun(w, m, cfg, torch)
     for t in range(1, steps + 1):
         run.step(t)
     out = [run.fetch(i) for i in range(len(w.tensors))]
@@ -267,12 +267,12 @@ def test_resume_equals_uninterrupted_and_grad_pointers_may_change():
     m = mlp(bias_std=0.1)
     w = W.custom_workload("res", shapes, steps=10, wid=106)
     full = _run_states(w, L.config_from(), 10, m)
-    run = GpuRun(w, m, L.config_from(), torch)
+    run = DeviceRun(w, m, L.config_from(), torch)
     for t in range(1, 6):
         run.step(t)          # fresh gradient tensors each step: pointers change
     saved = [run.fetch(i) for i in range(len(shapes))]
     run.close()
-    run2 = GpuRun(w, m, L.config_from(), torch)
+    run2 = DeviceRun(w, m, L.config_from(), torch)
     for i in range(len(shapes)):
         run2.params[i].copy_(torch.from_numpy(saved[i]["p"].reshape(w.tensors[i].shape)))
         v = run2.opt.state_views(i)
@@ -386,8 +386,8 @@ def test_per_tensor_values_equal_to_the_config_are_bitwise_the_config():
     w = W.custom_workload("th_eq", shapes, grad_std=1e-2, steps=3, wid=171)
     m = mlp(bias_std=0.1)
     cfg = L.config_from(lr=0.7, weight_decay=0.05)
-    a = GpuRun(w, m, cfg, torch)
-    b = GpuRun(w, m, cfg, torch)
+    a = DeviceRun(w, m, cfg, torch)
+    b = DeviceRun(w, m, cfg, torch)
     b.opt.set_tensor_hyper([0.7] * 3, [0.05] * 3)
     for t in (1, 2):
         a.step(t)
@@ -615,7 +615,7 @@ def test_non_finite_gradient_stays_in_its_tensor(impl, bad):
     w = W.custom_workload("nonfinite", shapes, grad_std=1e-2, steps=1, wid=130)
     cfg = L.config_from(mlp_impl=impl)
     weights = mlp(bias_std=0.1)
-    run = GpuRun(w, weights, cfg, torch)
+    run = DeviceRun(w, weights, cfg, torch)
     grads = [torch.from_numpy(W.grad_at(w, i, 1).reshape(t.shape)).cuda() for i, t in enumerate(w.tensors)]
     grads[0][5, 17] = bad
     run.opt.step(grads)
