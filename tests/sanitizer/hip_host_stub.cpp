@@ -20,8 +20,8 @@
 
 #include "../../learned_optimizer_step_amd/csrc/lopt_internal.h"
 
-// Size of the workspace the driver handed to lopt_init_state (set by the
-// driver; check_plan keeps every offset below it).
+// Size of the workspace the test program handed to lopt_init_state (set by
+// planner_main.cpp; check_plan keeps every offset below it).
 size_t g_stub_ws_bytes = 0;
 long g_stub_plan_checks = 0;
 
