@@ -381,6 +381,21 @@ static_assert(x6_feature(23, kNF, true) == 26 && x6_feature(24, kNF, true) == -1
                   x6_feature(28, kNF, true) == -1 && x6_feature(29, kNF, false) == -1 &&
                   x6_feature(28, kVeloNF, true) == -1 && x6_feature(29, kVeloNF, false) == -1,
               "bf16x6 layer-1 entries");
+// Every fed feature (all n_feat but the folded row features 13..15 with RU) in
+// exactly one of the entries 0..29 (30 and 31 hold the constant term).
+__device__ constexpr bool x6_layout_ok(int nf, bool ru) {
+  for (int f = 0; f < nf; ++f) {
+    int hits = 0;
+    for (int q = 0; q < 30; ++q) hits += x6_feature(q, nf, ru) == f;
+    if (hits != ((ru && f >= 13 && f < 16) ? 0 : 1)) return false;
+  }
+  for (int q = 0; q < 30; ++q)
+    if (x6_feature(q, nf, ru) >= nf) return false;
+  return true;
+}
+static_assert(x6_layout_ok(kNF, false) && x6_layout_ok(kNF, true) && x6_layout_ok(kVeloNF, false) &&
+                  x6_layout_ok(kVeloNF, true),
+              "bf16x6 layer-1 entries: each fed feature once");
 
 // (A piece, B piece) of product t of NP (9, 8 or 6), smallest terms first:
 // bf16x9: ll, then bf16x8's lm, ml, then bf16x6's hl, lh, mm, hm, mh, hh.
