@@ -275,9 +275,10 @@ lopt_status lopt_get_shard_sums(const lopt_handle* h, float** sums1, size_t* n1,
  * Phases run in the order 0, 1, 2, 0, ...; ts as for lopt_step, gradient
  * pointers read at phase 0 (a change in a later phase is refused).  With one
  * rank (no exchange) the three phases give lopt_step's result for the whole
- * tensors, bit for bit.  Errors: no row-shard binding, a phase out of order,
- * or a different list -> STATE; as lopt_step otherwise.  On error nothing is
- * queued and the expected phase does not change. */
+ * tensors, bit for bit.  The phases always run as separate kernels
+ * (lopt_config.launch does not apply).  Errors: no row-shard binding, a phase
+ * out of order, or a different list -> STATE; as lopt_step otherwise.  On
+ * error nothing is queued and the expected phase does not change. */
 lopt_status lopt_step_shard(lopt_handle* h, const lopt_tensor* ts, int32_t n, int32_t phase, void* stream);
 
 /* Bytes of the device array behind lopt_init_state_static, per GPU. */
