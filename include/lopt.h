@@ -125,7 +125,9 @@ typedef struct lopt_config {
   float beta_m[3];    /* momentum decays, default 0.1, 0.5, 0.9 */
   float beta_v;       /* second-moment decay, default 0.999 */
   float beta_f[3];    /* row/column second-moment decays, default 0.9, 0.99, 0.999 */
-  float eps_v;        /* inside 1/sqrt(v + eps_v), default 1e-8 */
+  float eps_v;        /* inside 1/sqrt(v + eps_v), default 1e-8; with 0, an element whose v is
+                         exactly 0 (a zero gradient from zero state) has infinite features and
+                         makes its tensor's update unspecified for that step */
   float eps_f;        /* added to the row/column means of g^2, default 1e-20 */
   float eps_norm;     /* inside the feature normaliser's root, default 1e-30 */
   float exp_mult;     /* default 1e-3 */
